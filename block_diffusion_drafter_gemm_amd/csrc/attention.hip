@@ -1,0 +1,302 @@
+// Block attention of the drafter: the B block queries of every query head
+// attend, without a mask, to the sequence's paged context keys plus the
+// block's own B keys (in-block attention is non-causal).
+//
+// Work items are (sequence, context chunk, KV head): the G = nq/nkv query heads
+// of one KV head share every K/V byte, so an item streams its chunk of K/V once
+// for G*B query rows.  Items write an unnormalised partial (O, running max,
+// running sum); a merge kernel combines the chunks of a (sequence, KV head) in
+// chunk order.
+//
+// Inside an item, 64-key sub-blocks of K and V are staged in LDS (V
+// transposed).  Scores are formed as S^T = K Q^T on the matrix cores, so a
+// lane holds 4 keys of one query row; the exponentiated scores of two 16-key
+// tiles are then exactly that lane's fragment of P^T, and O^T = V^T P^T keeps
+// the query row in the same lane, which makes the online-softmax rescale
+// lane-local.
+#include "dflash_device.h"
+#include "dflash_internal.h"
+
+namespace dflash {
+
+constexpr int kSub = 64;        // keys per LDS sub-block
+constexpr float kLog2e = 1.4426950408889634f;
+
+int attn_chunk(int batch, int max_ctx, int block_size, int nkv) {
+  // aim for a few items per compute unit; chunk in [64, 1024] keys, multiple of 64
+  const long keys = (long)batch * (max_ctx + block_size) * nkv;
+  long c = keys / 1024;
+  c = (c + kSub - 1) / kSub * kSub;
+  if (c < kSub) c = kSub;
+  if (c > 1024) c = 1024;
+  return (int)c;
+}
+
+int attn_max_items(int batch, int max_ctx, int block_size, int nkv, int chunk) {
+  return batch * ((max_ctx + block_size + chunk - 1) / chunk) * nkv;
+}
+
+// Locate flat chunk index f among the sequences (chunks per sequence =
+// ceil((ctx_len + B) / chunk)).  Executed by one wave; returns seq (-1 when f
+// is beyond the total) and the sequence's first flat chunk index.
+__device__ void find_seq(const int *ctx_len, int batch, int B, int chunk, int f, int *seq_out, int *first_out) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int s0 = 0; s0 < batch; s0 += 64) {
+    const int s = s0 + lane;
+    const int n = s < batch ? (ctx_len[s] + B + chunk - 1) / chunk : 0;
+    int inc = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(inc, o);
+      if (lane >= o) inc += t;
+    }
+    const int excl = base + inc - n;
+    const bool hit = s < batch && f >= excl && f < excl + n;
+    const unsigned long long m = __ballot(hit);
+    if (m) {
+      const int src = __ffsll((long long)m) - 1;
+      *seq_out = __shfl(s, src);
+      *first_out = __shfl(excl, src);
+      return;
+    }
+    base += __shfl(inc, 63);
+  }
+  *seq_out = -1;
+  *first_out = 0;
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
+  constexpr int EPV = 16 / (int)sizeof(T);      // elements per 16-byte vector
+  constexpr int VPK = HD / EPV;                 // vectors per key row
+  constexpr int KSTR = HD + EPV;                // LDS row stride of K (elements)
+  constexpr int VSTR = kSub + EPV;              // LDS row stride of V^T (elements)
+  constexpr int NU = HD / 32;                   // k-chunks over head_dim
+  constexpr int ND = HD / 16;                   // d tiles
+  __shared__ __align__(16) T k_lds[kSub * KSTR];
+  __shared__ __align__(16) T vt_lds[HD * VSTR];
+  __shared__ int s_seq, s_first;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, ln = lane & 15;
+  const int item = blockIdx.x;
+  const int f = item / a.nkv, g = item % a.nkv;
+  if (wave == 0) {
+    int sq, first;
+    find_seq(a.ctx_len, a.batch, a.block_size, a.chunk, f, &sq, &first);
+    if (lane == 0) { s_seq = sq; s_first = first; }
+  }
+  __syncthreads();
+  const int s = s_seq;
+  if (s < 0) return;
+  const int c = f - s_first;
+  const int B = a.block_size, G = a.nq / a.nkv, GB = G * B;
+  const int ctx = a.ctx_len[s];
+  const int kbeg = c * a.chunk;
+  const int kend = min(kbeg + a.chunk, ctx + B);
+  const int MTQ = (GB + 15) / 16;
+  const T *Q = (const T *)a.q;
+  const T *Kc = (const T *)a.kc, *Vc = (const T *)a.vc, *Kb = (const T *)a.kb, *Vb = (const T *)a.vb;
+  const float scale = kLog2e / sqrtf((float)HD);
+
+  // query fragments of this wave's tiles (B operand: column = query row)
+  Frag<T> qf[2][NU];
+  bool tile_on[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int qt = wave + 4 * t;
+    tile_on[t] = qt < MTQ;
+    const int r = qt * 16 + ln;
+    const bool ok = tile_on[t] && r < GB;
+    const int hh = ok ? r / B : 0, j = ok ? r % B : 0;
+    const T *qp = Q + ((size_t)(s * B + j) * a.nq + g * G + hh) * HD + 8 * g4;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      if (ok) qf[t][u].load(qp + 32 * u); else qf[t][u].zero();
+    }
+  }
+  f32x4 o[2][ND];
+  float m_run[2], l_run[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    m_run[t] = -1e30f;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) o[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int sub = kbeg; sub < kend; sub += kSub) {
+    __syncthreads();
+    for (int i = tid; i < kSub * VPK; i += 256) {
+      const int kk = i / VPK, vv = i - kk * VPK;
+      const int t = sub + kk;
+      uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+      if (t < kend) {
+        size_t off;
+        const T *kp, *vp;
+        if (t < ctx) {
+          const int page = a.block_table[(size_t)s * a.max_pages + t / a.page_size];
+          off = (((size_t)page * a.page_size + t % a.page_size) * a.nkv + g) * HD;
+          kp = Kc; vp = Vc;
+        } else {
+          off = ((size_t)(s * B + (t - ctx)) * a.nkv + g) * HD;
+          kp = Kb; vp = Vb;
+        }
+        kx = *reinterpret_cast<const uint4 *>(kp + off + vv * EPV);
+        vx = *reinterpret_cast<const uint4 *>(vp + off + vv * EPV);
+      }
+      *reinterpret_cast<uint4 *>(k_lds + kk * KSTR + vv * EPV) = kx;
+      const T *ve = reinterpret_cast<const T *>(&vx);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) vt_lds[(vv * EPV + e) * VSTR + kk] = ve[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kb2 = 0; kb2 < kSub; kb2 += 32) {
+      if (sub + kb2 >= kend) break;
+      // V^T fragments for all d tiles (A operand: row = d, k = keys)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (!tile_on[t]) continue;
+        f32x4 st[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const T *kr = k_lds + (kb2 + kt * 16 + ln) * KSTR + 8 * g4;
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            Frag<T> kf;
+            kf.load(kr + 32 * u);
+            st[kt] = mma(st[kt], kf, qf[t][u]);
+          }
+        }
+        float p[8];
+        float bmax = -1e30f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = sub + kb2 + kt * 16 + 4 * g4 + i;
+            const float sc = key < kend ? f4get(st[kt], i) * scale : -1e30f;
+            p[kt * 4 + i] = sc;
+            bmax = fmaxf(bmax, sc);
+          }
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+        const float m_new = fmaxf(m_run[t], bmax);
+        const float alpha = exp2f(m_run[t] - m_new);
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = exp2f(p[e] - m_new);
+          psum += Storage<T>::round(p[e]);   // the weights the P*V product uses
+        }
+        l_run[t] = l_run[t] * alpha + psum;
+        m_run[t] = m_new;
+        Frag<T> pf;
+        pf.set(p);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          o[t][d] *= alpha;
+          Frag<T> vf;
+          const T *vr = vt_lds + (d * 16 + ln) * VSTR + kb2 + 4 * g4;
+          if constexpr (sizeof(T) == 2) {
+            const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
+            reinterpret_cast<Frag<bf16_t> &>(vf).v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          } else {
+            reinterpret_cast<Frag<float> &>(vf).lo = *reinterpret_cast<const float4 *>(vr);
+            reinterpret_cast<Frag<float> &>(vf).hi = *reinterpret_cast<const float4 *>(vr + 16);
+          }
+          o[t][d] = mma(o[t][d], vf, pf);
+        }
+      }
+    }
+  }
+
+  // partial results: O^T (lane: query row ln, d rows 4*g4..), max, sum
+  const int GBP = MTQ * 16;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (!tile_on[t]) continue;
+    float l = l_run[t];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int r = (wave + 4 * t) * 16 + ln;
+    if (r >= GB) continue;
+    float *po = a.partial + ((size_t)item * GBP + r) * HD;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) po[d * 16 + 4 * g4 + i] = f4get(o[t][d], i);
+    if (g4 == 0) {
+      a.stats[((size_t)item * GBP + r) * 2 + 0] = m_run[t];
+      a.stats[((size_t)item * GBP + r) * 2 + 1] = l;
+    }
+  }
+}
+
+// One wave per (sequence, KV head, query row): combine the chunk partials.
+template <typename T, int HD>
+__global__ __launch_bounds__(64) void attn_merge_kernel(const AttnArgs a) {
+  const int lane = threadIdx.x;
+  const int B = a.block_size, G = a.nq / a.nkv, GB = G * B;
+  const int MTQ = (GB + 15) / 16, GBP = MTQ * 16;
+  const int r = blockIdx.x % GB;
+  const int sg = blockIdx.x / GB;
+  const int s = sg / a.nkv, g = sg % a.nkv;
+  // first flat chunk of sequence s (prefix over the ragged chunk counts)
+  int base = 0;
+  for (int s0 = 0; s0 < s; s0 += 64) {
+    const int q = s0 + lane;
+    int n = q < s ? (a.ctx_len[q] + B + a.chunk - 1) / a.chunk : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+    base += n;
+  }
+  int nch = (a.ctx_len[s] + B + a.chunk - 1) / a.chunk;
+  // chunks past the launched item range were never computed (ctx_len above the
+  // declared maximum); never read beyond the partial buffers
+  if ((base + nch) * a.nkv > a.max_items) nch = max(0, a.max_items / a.nkv - base);
+  float M = -1e30f;
+  for (int c = 0; c < nch; ++c) {
+    const size_t item = (size_t)(base + c) * a.nkv + g;
+    M = fmaxf(M, a.stats[(item * GBP + r) * 2]);
+  }
+  constexpr int PER = HD / 64;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float lsum = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const size_t item = (size_t)(base + c) * a.nkv + g;
+    const float w = exp2f(a.stats[(item * GBP + r) * 2] - M);
+    lsum += w * a.stats[(item * GBP + r) * 2 + 1];
+    const float *po = a.partial + (item * GBP + r) * HD;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += w * po[lane + 64 * e];
+  }
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  const int hh = r / B, j = r % B;
+  T *O = (T *)a.o;
+  const size_t ob = ((size_t)(s * B + j) * a.nq + g * G + hh) * HD;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) Storage<T>::store(O, ob + lane + 64 * e, acc[e] * inv);
+}
+
+template <typename T, int HD>
+static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL((attn_partial_kernel<T, HD>), dim3(a.max_items), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int GB = (a.nq / a.nkv) * a.block_size;
+  hipLaunchKernelGGL((attn_merge_kernel<T, HD>), dim3(a.batch * a.nkv * GB), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(bool is_bf16, const AttnArgs &a, hipStream_t st) {
+  if (is_bf16) return a.hd == 128 ? launch_attn_t<bf16_t, 128>(a, st) : launch_attn_t<bf16_t, 64>(a, st);
+  return a.hd == 128 ? launch_attn_t<float, 128>(a, st) : launch_attn_t<float, 64>(a, st);
+}
+
+}  // namespace dflash

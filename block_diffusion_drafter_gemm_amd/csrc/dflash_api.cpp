@@ -1,0 +1,453 @@
+// C ABI of libdflash: argument validation, workspace layout and the launch
+// sequence of each entry point.  All compute happens in the HIP kernels; this
+// file only plans and enqueues.
+#include <math.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/dflash.h"
+#include "dflash_internal.h"
+
+using namespace dflash;
+
+struct dflash_handle_s {
+  dflash_config cfg;
+  const void *embed, *lm_head, *w_fc, *final_norm;
+  const void *attn_norm[kMaxLayers], *w_qkv[kMaxLayers], *w_o[kMaxLayers];
+  const void *mlp_norm[kMaxLayers], *w_gate_up[kMaxLayers], *w_down[kMaxLayers];
+  bool bf16;
+  size_t esz;  // bytes per stored element
+};
+
+namespace {
+
+constexpr size_t kCounterBytes = 256 * 1024;  // completion counters at the front of every workspace
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Carve {
+  size_t off = kCounterBytes;
+  size_t take(size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+// ---- draft_block layout --------------------------------------------------
+struct DraftLayout {
+  size_t X, Y, Q, Kb, Vb, O, Hs, part, attn_part, attn_stats, total;
+  int chunk, max_items;
+};
+
+size_t gemm_partial_floats(const dflash_handle_s *h, int M, int N_groups, int K, int z) {
+  int ks, kps;
+  return gemm_plan(M, N_groups, K, z, h->bf16, &ks, &kps);
+}
+
+int groups_of(int N) { return (N + kColGroup - 1) / kColGroup; }
+
+DraftLayout draft_layout(const dflash_handle_s *h, int batch, int max_ctx) {
+  const dflash_config &c = h->cfg;
+  const int B = c.block_size, R = batch * B;
+  const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+  DraftLayout L;
+  Carve cv;
+  L.X = cv.take((size_t)R * c.hidden * 4);
+  L.Y = cv.take((size_t)R * c.hidden * h->esz);
+  L.Q = cv.take((size_t)R * qd * h->esz);
+  L.Kb = cv.take((size_t)R * kvd * h->esz);
+  L.Vb = cv.take((size_t)R * kvd * h->esz);
+  L.O = cv.take((size_t)R * qd * h->esz);
+  L.Hs = cv.take((size_t)R * c.ffn * h->esz);
+  size_t pf = 0, t;
+  t = gemm_partial_floats(h, R, groups_of(qd + 2 * kvd), c.hidden, 1); pf = t > pf ? t : pf;
+  t = gemm_partial_floats(h, R, groups_of(c.hidden), qd, 1); pf = t > pf ? t : pf;
+  t = gemm_partial_floats(h, R, c.ffn / 64, c.hidden, 1); pf = t > pf ? t : pf;
+  t = gemm_partial_floats(h, R, groups_of(c.hidden), c.ffn, 1); pf = t > pf ? t : pf;
+  L.part = cv.take(pf * 4);
+  L.chunk = attn_chunk(batch, max_ctx, B, c.n_kv_heads);
+  L.max_items = attn_max_items(batch, max_ctx, B, c.n_kv_heads, L.chunk);
+  const int GB = (c.n_q_heads / c.n_kv_heads) * B, GBP = (GB + 15) / 16 * 16;
+  L.attn_part = cv.take((size_t)L.max_items * GBP * c.head_dim * 4);
+  L.attn_stats = cv.take((size_t)L.max_items * GBP * 2 * 4);
+  L.total = cv.off;
+  return L;
+}
+
+struct LmLayout {
+  size_t part, val, idx, total;
+};
+
+LmLayout lm_layout(const dflash_handle_s *h, int rows) {
+  const dflash_config &c = h->cfg;
+  LmLayout L;
+  Carve cv;
+  const int ng = groups_of(c.vocab);
+  L.part = cv.take(gemm_partial_floats(h, rows, ng, c.hidden, 1) * 4);
+  L.val = cv.take((size_t)rows * ng * 4);
+  L.idx = cv.take((size_t)rows * ng * 4);
+  L.total = cv.off;
+  return L;
+}
+
+struct InjectLayout {
+  size_t c, part, total;
+};
+
+InjectLayout inject_layout(const dflash_handle_s *h, int n_new) {
+  const dflash_config &c = h->cfg;
+  InjectLayout L;
+  Carve cv;
+  L.c = cv.take((size_t)n_new * c.hidden * h->esz);
+  size_t pf = gemm_partial_floats(h, n_new, groups_of(c.hidden), c.n_feat_layers * c.hidden, 1);
+  size_t t = gemm_partial_floats(h, n_new, groups_of(2 * c.n_kv_heads * c.head_dim), c.hidden, c.n_layers);
+  L.part = cv.take((pf > t ? pf : t) * 4);
+  L.total = cv.off;
+  return L;
+}
+
+int counters_needed(int M, int n_groups, int z) {
+  const int MP = gemm_rows_per_group(M);
+  return ((M + MP - 1) / MP) * z * n_groups;
+}
+
+bool counters_fit(int M, int n_groups, int z) {
+  return (size_t)counters_needed(M, n_groups, z) * sizeof(int) <= kCounterBytes;
+}
+
+// Fill the GEMM plan fields of ``a`` (row groups, split-K, scratch) and launch.
+int launch(const dflash_handle_s *h, Epilogue epi, GemmArgs &a, int z, char *ws, size_t part_off, hipStream_t st) {
+  const int MP = gemm_rows_per_group(a.M);
+  a.m_groups = (a.M + MP - 1) / MP;
+  gemm_plan(a.M, a.n_groups, a.K, z, h->bf16, &a.k_split, &a.k_per_split);
+  a.partial = reinterpret_cast<float *>(ws + part_off);
+  a.counters = reinterpret_cast<int *>(ws);
+  if (!counters_fit(a.M, a.n_groups, z)) return DFLASH_ERR_SHAPE;
+  return launch_gemm(h->bf16, epi, a, z, st) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+int validate_config(const dflash_config *c) {
+  if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return DFLASH_ERR_DTYPE;
+  if (c->hidden <= 0 || c->hidden % 64) return DFLASH_ERR_SHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return DFLASH_ERR_SHAPE;
+  if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->n_q_heads % c->n_kv_heads) return DFLASH_ERR_SHAPE;
+  if ((c->n_q_heads * c->head_dim) % 64) return DFLASH_ERR_SHAPE;
+  if (c->ffn <= 0 || c->ffn % 64) return DFLASH_ERR_SHAPE;
+  if (c->vocab <= 0 || c->vocab % 16) return DFLASH_ERR_SHAPE;
+  if (c->n_layers < 1 || c->n_layers > kMaxLayers) return DFLASH_ERR_SHAPE;
+  if (c->n_feat_layers < 1) return DFLASH_ERR_SHAPE;
+  if (c->block_size < 2 || c->block_size > 64) return DFLASH_ERR_SHAPE;
+  if ((c->n_q_heads / c->n_kv_heads) * c->block_size > 128) return DFLASH_ERR_SHAPE;
+  if (c->page_size != 16) return DFLASH_ERR_SHAPE;
+  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return DFLASH_ERR_RANGE;
+  if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return DFLASH_ERR_RANGE;
+  return DFLASH_OK;
+}
+
+int validate_kv(const dflash_handle_s *h, const dflash_kv *kv) {
+  if (!kv) return DFLASH_ERR_NULL;
+  if (!kv->k || !kv->v || !kv->block_table || !kv->ctx_len) return DFLASH_ERR_NULL;
+  if (kv->batch < 1 || kv->max_pages < 1 || kv->n_pages < 1 || kv->max_ctx < 0) return DFLASH_ERR_SHAPE;
+  (void)h;
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dflash_status_str(int status) {
+  switch (status) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_ERR_NULL: return "null pointer argument";
+    case DFLASH_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case DFLASH_ERR_DTYPE: return "unknown storage type";
+    case DFLASH_ERR_RANGE: return "value out of range";
+    case DFLASH_ERR_WORKSPACE: return "workspace too small";
+    case DFLASH_ERR_UNSUPPORTED: return "unsupported combination";
+    case DFLASH_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int dflash_create(const dflash_config *cfg, const dflash_weights *w, dflash_handle *out) {
+  if (!cfg || !w || !out) return DFLASH_ERR_NULL;
+  *out = nullptr;
+  int st = validate_config(cfg);
+  if (st != DFLASH_OK) return st;
+  if (!w->embed || !w->lm_head || !w->w_fc || !w->final_norm || !w->attn_norm || !w->w_qkv || !w->w_o ||
+      !w->mlp_norm || !w->w_gate_up || !w->w_down)
+    return DFLASH_ERR_NULL;
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if (!w->attn_norm[l] || !w->w_qkv[l] || !w->w_o[l] || !w->mlp_norm[l] || !w->w_gate_up[l] || !w->w_down[l])
+      return DFLASH_ERR_NULL;
+  dflash_handle_s *h = new (std::nothrow) dflash_handle_s();
+  if (!h) return DFLASH_ERR_RANGE;
+  h->cfg = *cfg;
+  h->embed = w->embed;
+  h->lm_head = w->lm_head;
+  h->w_fc = w->w_fc;
+  h->final_norm = w->final_norm;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    h->attn_norm[l] = w->attn_norm[l];
+    h->w_qkv[l] = w->w_qkv[l];
+    h->w_o[l] = w->w_o[l];
+    h->mlp_norm[l] = w->mlp_norm[l];
+    h->w_gate_up[l] = w->w_gate_up[l];
+    h->w_down[l] = w->w_down[l];
+  }
+  h->bf16 = cfg->dtype == DFLASH_BF16;
+  h->esz = h->bf16 ? 2 : 4;
+  *out = h;
+  return DFLASH_OK;
+}
+
+int dflash_destroy(dflash_handle h) {
+  if (!h) return DFLASH_ERR_NULL;
+  delete h;
+  return DFLASH_OK;
+}
+
+int dflash_workspace_size(dflash_handle h, int32_t max_batch, int32_t max_ctx, int32_t max_new, size_t *bytes) {
+  if (!h || !bytes) return DFLASH_ERR_NULL;
+  if (max_batch < 1 || max_ctx < 0 || max_new < 0) return DFLASH_ERR_SHAPE;
+  size_t need = draft_layout(h, max_batch, max_ctx).total;
+  const size_t lm = lm_layout(h, max_batch * (h->cfg.block_size - 1)).total;
+  const size_t inj = inject_layout(h, max_new).total;
+  need = need > lm ? need : lm;
+  need = need > inj ? need : inj;
+  *bytes = need;
+  return DFLASH_OK;
+}
+
+int dflash_workspace_init(dflash_handle h, void *ws, size_t ws_bytes, void *stream) {
+  if (!h || !ws) return DFLASH_ERR_NULL;
+  if (ws_bytes < kCounterBytes) return DFLASH_ERR_WORKSPACE;
+  return launch_zero(ws, kCounterBytes, (hipStream_t)stream) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq, const int32_t *pos, int32_t n_new,
+                          const dflash_kv *kv, void *ws, size_t ws_bytes, void *stream) {
+  if (!h) return DFLASH_ERR_NULL;
+  if (n_new < 0) return DFLASH_ERR_SHAPE;
+  int st = validate_kv(h, kv);
+  if (st != DFLASH_OK) return st;
+  if (n_new == 0) return DFLASH_OK;
+  if (!feats || !seq || !pos || !ws) return DFLASH_ERR_NULL;
+  const dflash_config &c = h->cfg;
+  const InjectLayout L = inject_layout(h, n_new);
+  if (ws_bytes < L.total) return DFLASH_ERR_WORKSPACE;
+  char *w = static_cast<char *>(ws);
+  hipStream_t s = (hipStream_t)stream;
+  const int kvd = c.n_kv_heads * c.head_dim, qd = c.n_q_heads * c.head_dim;
+
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.A = feats;
+  a.lda = c.n_feat_layers * c.hidden;
+  a.W[0] = h->w_fc;
+  a.ldw = c.n_feat_layers * c.hidden;
+  a.M = n_new;
+  a.N = c.hidden;
+  a.K = c.n_feat_layers * c.hidden;
+  a.n_groups = groups_of(c.hidden);
+  a.out = w + L.c;
+  a.ldo = c.hidden;
+  if (!counters_fit(n_new, a.n_groups, 1)) return DFLASH_ERR_SHAPE;
+  if ((st = launch(h, EPI_STORE, a, 1, w, L.part, s)) != DFLASH_OK) return st;
+
+  GemmArgs b;
+  memset(&b, 0, sizeof(b));
+  b.A = w + L.c;
+  b.lda = c.hidden;
+  for (int l = 0; l < c.n_layers; ++l)
+    b.W[l] = static_cast<const char *>(h->w_qkv[l]) + (size_t)qd * c.hidden * h->esz;
+  b.ldw = c.hidden;
+  b.M = n_new;
+  b.N = 2 * kvd;
+  b.K = c.hidden;
+  b.n_groups = groups_of(2 * kvd);
+  b.k_out = kv->k;
+  b.v_out = kv->v;
+  b.nq = c.n_q_heads;
+  b.nkv = c.n_kv_heads;
+  b.hd = c.head_dim;
+  b.log2_theta = log2((double)c.rope_theta);
+  b.seq = seq;
+  b.pos = pos;
+  b.block_table = kv->block_table;
+  b.max_pages = kv->max_pages;
+  b.page_size = c.page_size;
+  b.cache_layer_stride = (size_t)kv->n_pages * c.page_size * kvd;
+  return launch(h, EPI_INJECT, b, c.n_layers, w, L.part, s);
+}
+
+int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_kv *kv, void *hidden_out, void *ws,
+                       size_t ws_bytes, void *stream) {
+  if (!h) return DFLASH_ERR_NULL;
+  int st = validate_kv(h, kv);
+  if (st != DFLASH_OK) return st;
+  if (!anchor_ids || !hidden_out || !ws) return DFLASH_ERR_NULL;
+  const dflash_config &c = h->cfg;
+  const int B = c.block_size, batch = kv->batch, R = batch * B;
+  const DraftLayout L = draft_layout(h, batch, kv->max_ctx);
+  if (ws_bytes < L.total) return DFLASH_ERR_WORKSPACE;
+  char *w = static_cast<char *>(ws);
+  hipStream_t s = (hipStream_t)stream;
+  const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+  float *X = reinterpret_cast<float *>(w + L.X);
+  const size_t cache_layer = (size_t)kv->n_pages * c.page_size * kvd * h->esz;
+
+  if (launch_embed(h->bf16, h->embed, anchor_ids, c.mask_token_id, batch, B, c.hidden, X, s) != hipSuccess)
+    return DFLASH_ERR_HIP;
+  for (int l = 0; l < c.n_layers; ++l) {
+    if (launch_rmsnorm(h->bf16, X, h->attn_norm[l], c.rms_eps, R, c.hidden, B, false, w + L.Y, s) != hipSuccess)
+      return DFLASH_ERR_HIP;
+    GemmArgs q;
+    memset(&q, 0, sizeof(q));
+    q.A = w + L.Y;
+    q.lda = c.hidden;
+    q.W[0] = h->w_qkv[l];
+    q.ldw = c.hidden;
+    q.M = R;
+    q.N = qd + 2 * kvd;
+    q.K = c.hidden;
+    q.n_groups = groups_of(q.N);
+    q.q_out = w + L.Q;
+    q.k_out = w + L.Kb;
+    q.v_out = w + L.Vb;
+    q.ctx_len = kv->ctx_len;
+    q.block_size = B;
+    q.nq = c.n_q_heads;
+    q.nkv = c.n_kv_heads;
+    q.hd = c.head_dim;
+    q.log2_theta = log2((double)c.rope_theta);
+    if ((st = launch(h, EPI_QKV, q, 1, w, L.part, s)) != DFLASH_OK) return st;
+
+    AttnArgs at;
+    memset(&at, 0, sizeof(at));
+    at.q = w + L.Q;
+    at.kb = w + L.Kb;
+    at.vb = w + L.Vb;
+    at.kc = static_cast<const char *>(kv->k) + l * cache_layer;
+    at.vc = static_cast<const char *>(kv->v) + l * cache_layer;
+    at.block_table = kv->block_table;
+    at.ctx_len = kv->ctx_len;
+    at.o = w + L.O;
+    at.partial = reinterpret_cast<float *>(w + L.attn_part);
+    at.stats = reinterpret_cast<float *>(w + L.attn_stats);
+    at.batch = batch;
+    at.block_size = B;
+    at.nq = c.n_q_heads;
+    at.nkv = c.n_kv_heads;
+    at.hd = c.head_dim;
+    at.max_pages = kv->max_pages;
+    at.page_size = c.page_size;
+    at.chunk = L.chunk;
+    at.max_items = L.max_items;
+    if (launch_attention(h->bf16, at, s) != hipSuccess) return DFLASH_ERR_HIP;
+
+    GemmArgs o;
+    memset(&o, 0, sizeof(o));
+    o.A = w + L.O;
+    o.lda = qd;
+    o.W[0] = h->w_o[l];
+    o.ldw = qd;
+    o.M = R;
+    o.N = c.hidden;
+    o.K = qd;
+    o.n_groups = groups_of(c.hidden);
+    o.X = X;
+    o.ldx = c.hidden;
+    if ((st = launch(h, EPI_RESID, o, 1, w, L.part, s)) != DFLASH_OK) return st;
+
+    if (launch_rmsnorm(h->bf16, X, h->mlp_norm[l], c.rms_eps, R, c.hidden, B, false, w + L.Y, s) != hipSuccess)
+      return DFLASH_ERR_HIP;
+    GemmArgs gu;
+    memset(&gu, 0, sizeof(gu));
+    gu.A = w + L.Y;
+    gu.lda = c.hidden;
+    gu.W[0] = h->w_gate_up[l];
+    gu.ldw = c.hidden;
+    gu.M = R;
+    gu.N = 2 * c.ffn;
+    gu.K = c.hidden;
+    gu.n_groups = c.ffn / 64;
+    gu.ffn = c.ffn;
+    gu.out = w + L.Hs;
+    gu.ldo = c.ffn;
+    if ((st = launch(h, EPI_SWIGLU, gu, 1, w, L.part, s)) != DFLASH_OK) return st;
+
+    GemmArgs dn;
+    memset(&dn, 0, sizeof(dn));
+    dn.A = w + L.Hs;
+    dn.lda = c.ffn;
+    dn.W[0] = h->w_down[l];
+    dn.ldw = c.ffn;
+    dn.M = R;
+    dn.N = c.hidden;
+    dn.K = c.ffn;
+    dn.n_groups = groups_of(c.hidden);
+    dn.X = X;
+    dn.ldx = c.hidden;
+    if ((st = launch(h, EPI_RESID, dn, 1, w, L.part, s)) != DFLASH_OK) return st;
+  }
+  if (launch_rmsnorm(h->bf16, X, h->final_norm, c.rms_eps, batch * (B - 1), c.hidden, B, true, hidden_out, s) !=
+      hipSuccess)
+    return DFLASH_ERR_HIP;
+  return DFLASH_OK;
+}
+
+int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int32_t *ids_out, float *max_logit_out,
+                         float *logits_out, void *ws, size_t ws_bytes, void *stream) {
+  if (!h) return DFLASH_ERR_NULL;
+  if (rows < 0) return DFLASH_ERR_SHAPE;
+  if (rows == 0) return DFLASH_OK;
+  if (!hidden || !ids_out || !ws) return DFLASH_ERR_NULL;
+  const dflash_config &c = h->cfg;
+  const LmLayout L = lm_layout(h, rows);
+  if (ws_bytes < L.total) return DFLASH_ERR_WORKSPACE;
+  char *w = static_cast<char *>(ws);
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.A = hidden;
+  a.lda = c.hidden;
+  a.W[0] = h->lm_head;
+  a.ldw = c.hidden;
+  a.M = rows;
+  a.N = c.vocab;
+  a.K = c.hidden;
+  a.n_groups = groups_of(c.vocab);
+  a.amax_val = reinterpret_cast<float *>(w + L.val);
+  a.amax_idx = reinterpret_cast<int *>(w + L.idx);
+  int st = launch(h, EPI_ARGMAX, a, 1, w, L.part, s);
+  if (st != DFLASH_OK) return st;
+  if (launch_argmax_reduce(a.amax_val, a.amax_idx, rows, a.n_groups, ids_out, max_logit_out, s) != hipSuccess)
+    return DFLASH_ERR_HIP;
+  if (logits_out) {
+    GemmArgs b = a;
+    b.out = logits_out;
+    b.ldo = c.vocab;
+    if ((st = launch(h, EPI_STORE_F32, b, 1, w, L.part, s)) != DFLASH_OK) return st;
+  }
+  return DFLASH_OK;
+}
+
+int dflash_accept_len(const int32_t *draft_ids, const int32_t *target_ids, int32_t batch, int32_t block_size,
+                      int32_t *accept_len_out, int32_t *bonus_out, void *stream) {
+  if (batch < 0) return DFLASH_ERR_SHAPE;
+  if (block_size < 2 || block_size > 64) return DFLASH_ERR_SHAPE;
+  if (batch == 0) return DFLASH_OK;
+  if (!draft_ids || !target_ids || !accept_len_out || !bonus_out) return DFLASH_ERR_NULL;
+  return launch_accept(draft_ids, target_ids, batch, block_size, accept_len_out, bonus_out, (hipStream_t)stream) ==
+                 hipSuccess
+             ? DFLASH_OK
+             : DFLASH_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+// Device-side building blocks shared by the libdflash kernels (gfx950 only).
+//
+// Matrix-core fragments.  Every dense contraction in this library is cut into
+// 16 x 16 output tiles and 32-wide k-chunks.  A fragment is the 8 consecutive
+// k-elements one lane contributes to one k-chunk: lane l serves row (or column)
+// l % 16 and k-elements 8*(l/16) .. 8*(l/16)+7 of the chunk.  Both operands of
+// a product use the same lane -> k assignment, so the contraction is exact for
+// any order in which the hardware walks k inside a chunk.
+//   bf16: one v_mfma_f32_16x16x32_bf16 per chunk (fragment = 16 bytes).
+//   fp32: eight v_mfma_f32_16x16x4_f32 per chunk; product j takes element j of
+//         every lane's fragment (fragment = 32 bytes).
+// The accumulator of a 16 x 16 tile holds, in lane l, column l % 16 and rows
+// 4*(l/16) .. 4*(l/16)+3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dflash {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// scalar conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Storage;
+template <> struct Storage<float> {
+  __device__ __forceinline__ static float load(const float *p, size_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float *p, size_t i, float v) { p[i] = v; }
+  // value after rounding to the storage type
+  __device__ __forceinline__ static float round(float v) { return v; }
+};
+template <> struct Storage<bf16_t> {
+  __device__ __forceinline__ static float load(const bf16_t *p, size_t i) { return bf16_to_f32(p[i].bits); }
+  __device__ __forceinline__ static void store(bf16_t *p, size_t i, float v) { p[i].bits = f32_to_bf16(v); }
+  __device__ __forceinline__ static float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+};
+
+// ---------------------------------------------------------------------------
+// fragments
+// ---------------------------------------------------------------------------
+template <typename T> struct Frag;
+
+template <> struct Frag<bf16_t> {
+  uint4 v;  // 8 bf16
+  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void load(const bf16_t *p) { v = *reinterpret_cast<const uint4 *>(p); }
+  __device__ __forceinline__ void store(bf16_t *p) const { *reinterpret_cast<uint4 *>(p) = v; }
+  // element e as float (e in 0..7)
+  __device__ __forceinline__ float get(int e) const {
+    uint32_t w = (e < 2) ? v.x : (e < 4) ? v.y : (e < 6) ? v.z : v.w;
+    return bf16_to_f32(static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xffffu)));
+  }
+  // pack 8 floats (rounded to bf16)
+  __device__ __forceinline__ void set(const float *f) {
+    v.x = f32_to_bf16(f[0]) | (static_cast<uint32_t>(f32_to_bf16(f[1])) << 16);
+    v.y = f32_to_bf16(f[2]) | (static_cast<uint32_t>(f32_to_bf16(f[3])) << 16);
+    v.z = f32_to_bf16(f[4]) | (static_cast<uint32_t>(f32_to_bf16(f[5])) << 16);
+    v.w = f32_to_bf16(f[6]) | (static_cast<uint32_t>(f32_to_bf16(f[7])) << 16);
+  }
+};
+
+template <> struct Frag<float> {
+  float4 lo, hi;  // 8 fp32
+  __device__ __forceinline__ void zero() {
+    lo = make_float4(0.f, 0.f, 0.f, 0.f);
+    hi = lo;
+  }
+  __device__ __forceinline__ void load(const float *p) {
+    lo = *reinterpret_cast<const float4 *>(p);
+    hi = *reinterpret_cast<const float4 *>(p + 4);
+  }
+  __device__ __forceinline__ void store(float *p) const {
+    *reinterpret_cast<float4 *>(p) = lo;
+    *reinterpret_cast<float4 *>(p + 4) = hi;
+  }
+  __device__ __forceinline__ float get(int e) const {
+    switch (e) {
+      case 0: return lo.x; case 1: return lo.y; case 2: return lo.z; case 3: return lo.w;
+      case 4: return hi.x; case 5: return hi.y; case 6: return hi.z; default: return hi.w;
+    }
+  }
+  __device__ __forceinline__ void set(const float *f) {
+    lo = make_float4(f[0], f[1], f[2], f[3]);
+    hi = make_float4(f[4], f[5], f[6], f[7]);
+  }
+};
+
+// acc += A_chunk * B_chunk for one 16 x 16 tile and one 32-wide k-chunk.
+__device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<bf16_t> &a, const Frag<bf16_t> &b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v), __builtin_bit_cast(bf16x8, b.v),
+                                                 acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<float> &a, const Frag<float> &b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ float f4get(const f32x4 &v, int i) {
+  return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+
+// ---------------------------------------------------------------------------
+// cross-workgroup completion counters (agent scope)
+// ---------------------------------------------------------------------------
+// Called by all threads of a workgroup after its partial results are stored.
+// Returns true in every thread of the workgroup that arrives last; that
+// workgroup then sees every other workgroup's stores and resets the counter.
+__device__ __forceinline__ bool arrive_last(int *counter, int expected, int *lds_flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    int last = (prev == expected - 1);
+    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *lds_flag = last;
+  }
+  __syncthreads();
+  bool last = *lds_flag != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+// RoPE angle pos * theta^(-2i/d), evaluated in double, returned as (cos, sin).
+__device__ __forceinline__ void rope_cs(int pos, int i, int d, double log2_theta, float *c, float *s) {
+  double inv = exp2(-2.0 * static_cast<double>(i) / static_cast<double>(d) * log2_theta);
+  double a = static_cast<double>(pos) * inv;
+  double sn, cs;
+  sincos(a, &sn, &cs);
+  *c = static_cast<float>(cs);
+  *s = static_cast<float>(sn);
+}
+
+}  // namespace dflash

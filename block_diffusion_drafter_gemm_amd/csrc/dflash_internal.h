@@ -1,0 +1,90 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dflash {
+
+constexpr int kMaxLayers = 16;
+constexpr int kColGroup = 128;   // output columns per GEMM workgroup
+
+enum Epilogue {
+  EPI_STORE = 0,      // out[row, col] = acc (storage type)
+  EPI_STORE_F32 = 1,  // out[row, col] = acc (fp32)
+  EPI_RESID = 2,      // X[row, col] += acc (fp32 residual)
+  EPI_SWIGLU = 3,     // out[row, j] = silu(gate_j) * up_j (storage type)
+  EPI_QKV = 4,        // RoPE(q), RoPE(k), v -> block q/k/v buffers
+  EPI_INJECT = 5,     // RoPE(k), v -> paged context cache
+  EPI_ARGMAX = 6,     // per-row (max, lowest argmax) over the column group
+};
+
+struct GemmArgs {
+  // operands
+  const void *A;          // [M, K] storage type, row stride lda
+  int lda;
+  const void *W[kMaxLayers];  // per z-slice weights [N_phys, K], row stride ldw
+  int ldw;
+  int M, N, K;            // N: logical output columns
+  int n_groups;           // ceil(N / 128) (SwiGLU: ffn / 64)
+  int m_groups;           // ceil(M / MP)
+  int k_split, k_per_split;
+  float *partial;         // [z][n_groups][k_split][MP][128]
+  int *counters;          // [z][n_groups]
+  // EPI_STORE / EPI_STORE_F32 / EPI_SWIGLU
+  void *out;
+  int ldo;
+  // EPI_RESID
+  float *X;
+  int ldx;
+  // EPI_QKV / EPI_INJECT
+  void *q_out, *k_out, *v_out;
+  const int *ctx_len;
+  int block_size, nq, nkv, hd;
+  double log2_theta;
+  const int *seq, *pos, *block_table;
+  int max_pages, page_size;
+  size_t cache_layer_stride;  // elements per layer of the paged cache
+  // EPI_SWIGLU
+  int ffn;
+  // EPI_ARGMAX
+  float *amax_val;
+  int *amax_idx;
+};
+
+// Launch a skinny GEMM; ``z_slices`` = number of weight slices (layers) in the
+// launch.  ``is_bf16`` selects the storage type.
+hipError_t launch_gemm(bool is_bf16, Epilogue epi, const GemmArgs &a, int z_slices, hipStream_t st);
+
+// Rows per GEMM workgroup for M rows (16, 32 or 64).
+int gemm_rows_per_group(int M);
+
+// Pick k_split / k_per_split for a GEMM; returns partial floats needed.
+size_t gemm_plan(int M, int N_groups, int K, int z_slices, bool is_bf16, int *k_split, int *k_per_split);
+
+struct AttnArgs {
+  const void *q;          // [R, nq*hd]
+  const void *kb, *vb;    // [R, nkv*hd] block keys / values
+  const void *kc, *vc;    // layer base of the paged cache
+  const int *block_table, *ctx_len;
+  void *o;                // [R, nq*hd]
+  float *partial;         // [items][GB_pad][hd] + stats
+  float *stats;           // [items][GB_pad][2]
+  int batch, block_size, nq, nkv, hd, max_pages, page_size, chunk, max_items;
+};
+hipError_t launch_attention(bool is_bf16, const AttnArgs &a, hipStream_t st);
+int attn_chunk(int batch, int max_ctx, int block_size, int nkv);
+int attn_max_items(int batch, int max_ctx, int block_size, int nkv, int chunk);
+
+hipError_t launch_embed(bool is_bf16, const void *embed, const int *anchor, int mask_id, int batch, int block_size,
+                        int hidden, float *X, hipStream_t st);
+hipError_t launch_rmsnorm(bool is_bf16, const float *X, const void *gain, float eps, int rows, int hidden,
+                          int block_size, bool skip_anchor, void *Y, hipStream_t st);
+hipError_t launch_argmax_reduce(const float *val, const int *idx, int rows, int n_groups, int *ids_out,
+                                float *max_out, hipStream_t st);
+hipError_t launch_accept(const int *draft, const int *target, int batch, int block_size, int *tau, int *bonus,
+                         hipStream_t st);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
+
+}  // namespace dflash

@@ -1,0 +1,141 @@
+// Row-wise kernels of the draft step: block embedding, RMSNorm, the second
+// level of the vocabulary argmax, greedy accept length and a zero fill.
+#include "dflash_device.h"
+#include "dflash_internal.h"
+
+namespace dflash {
+
+// X[s*B + j, :] = E[j == 0 ? anchor[s] : mask] as fp32 (the residual stream).
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const T *E, const int *anchor, int mask_id, int B, int H,
+                                                    float *X) {
+  const int row = blockIdx.x;
+  const int s = row / B, j = row % B;
+  const int id = j == 0 ? anchor[s] : mask_id;
+  const T *e = E + (size_t)id * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) X[(size_t)row * H + i] = Storage<T>::load(e, i);
+}
+
+__device__ __forceinline__ float block_sum(float v, float *red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+  return t;
+}
+
+// Y[r] = X[src(r)] / sqrt(mean(X^2) + eps) * gain, rounded to the storage type.
+// skip_anchor: output row r reads input row s*B + 1 + (r % (B-1)) with
+// s = r / (B-1) (the mask rows of every block).
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *X, const T *gain, float eps, int H, int B,
+                                                      int skip_anchor, T *Y) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const int src = skip_anchor ? (r / (B - 1)) * B + 1 + r % (B - 1) : r;
+  const float *x = X + (size_t)src * H;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) ss += x[i] * x[i];
+  ss = block_sum(ss, red);
+  const float rs = 1.0f / sqrtf(ss / (float)H + eps);
+  for (int i = threadIdx.x; i < H; i += blockDim.x)
+    Storage<T>::store(Y, (size_t)r * H + i, x[i] * rs * Storage<T>::load(gain, i));
+}
+
+// Second level of the vocabulary argmax: one workgroup per row scans the
+// per-column-group maxima; the lowest id wins ties.
+__global__ __launch_bounds__(256) void argmax_reduce_kernel(const float *val, const int *idx, int n_groups,
+                                                            int *ids_out, float *max_out) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int r = blockIdx.x;
+  float best = -INFINITY;
+  int bidx = 0x7fffffff;
+  for (int i = threadIdx.x; i < n_groups; i += blockDim.x) {
+    const float v = val[(size_t)r * n_groups + i];
+    const int id = idx[(size_t)r * n_groups + i];
+    if (v > best || (v == best && id < bidx)) { best = v; bidx = id; }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o);
+    const int oi = __shfl_xor(bidx, o);
+    if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) { sv[wave] = best; si[wave] = bidx; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w)
+      if (sv[w] > best || (sv[w] == best && si[w] < bidx)) { best = sv[w]; bidx = si[w]; }
+    ids_out[r] = bidx;
+    if (max_out) max_out[r] = best;
+  }
+}
+
+// One wave per sequence: tau = 1 + (leading matches of draft vs target), bonus = target[tau-1].
+__global__ __launch_bounds__(64) void accept_kernel(const int *draft, const int *target, int B, int *tau,
+                                                    int *bonus) {
+  const int s = blockIdx.x, lane = threadIdx.x;
+  const bool miss = lane < B - 1 && draft[(size_t)s * (B - 1) + lane] != target[(size_t)s * B + lane];
+  const unsigned long long m = __ballot(miss);
+  const int k = m ? __ffsll((long long)m) - 1 : B - 1;
+  if (lane == 0) {
+    tau[s] = k + 1;
+    bonus[s] = target[(size_t)s * B + k];
+  }
+}
+
+__global__ void zero_kernel(uint4 *p, size_t n16) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_embed(bool is_bf16, const void *embed, const int *anchor, int mask_id, int batch, int B, int H,
+                        float *X, hipStream_t st) {
+  if (is_bf16)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(batch * B), dim3(256), 0, st, (const bf16_t *)embed, anchor,
+                       mask_id, B, H, X);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(batch * B), dim3(256), 0, st, (const float *)embed, anchor,
+                       mask_id, B, H, X);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(bool is_bf16, const float *X, const void *gain, float eps, int rows, int H, int B,
+                          bool skip_anchor, void *Y, hipStream_t st) {
+  if (is_bf16)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, X, (const bf16_t *)gain, eps, H, B,
+                       (int)skip_anchor, (bf16_t *)Y);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, st, X, (const float *)gain, eps, H, B,
+                       (int)skip_anchor, (float *)Y);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_reduce(const float *val, const int *idx, int rows, int n_groups, int *ids_out,
+                                float *max_out, hipStream_t st) {
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(rows), dim3(256), 0, st, val, idx, n_groups, ids_out, max_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(const int *draft, const int *target, int batch, int B, int *tau, int *bonus,
+                         hipStream_t st) {
+  hipLaunchKernelGGL(accept_kernel, dim3(batch), dim3(64), 0, st, draft, target, B, tau, bonus);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (uint4 *)p, n16);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -1,0 +1,121 @@
+"""Device-resident drafter state around the C ABI: weights, paged context cache
+and workspace as torch tensors (torch only supplies memory and streams).
+
+``Drafter`` takes any configuration object exposing the drafter shape fields
+(hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, n_layers, n_feat_layers,
+block_size, mask_token_id, dtype, rope_theta, rms_eps) and host weight arrays
+(bf16 as uint16 bit patterns, or float32).
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+_LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """Host array -> device tensor with the same bytes (bf16 bits travel as int16)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def to_host_storage(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> host array (int16-held bf16 back to uint16 bit patterns)."""
+    a = t.detach().cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+def storage_dtype(cfg) -> torch.dtype:
+    return torch.int16 if cfg.dtype == "bf16" else torch.float32
+
+
+class PagedKV:
+    """Paged context cache [n_layers][n_pages][16][nkv][d] plus page table and lengths."""
+
+    def __init__(self, cfg, block_table: np.ndarray, ctx_len: np.ndarray, n_pages: int,
+                 k: Optional[np.ndarray] = None, v: Optional[np.ndarray] = None, device="cuda",
+                 max_ctx: Optional[int] = None):
+        self.cfg = cfg
+        shape = (cfg.n_layers, n_pages, cfg.page_size, cfg.n_kv_heads, cfg.head_dim)
+        dt = storage_dtype(cfg)
+        self.k = to_device(k, device) if k is not None else torch.zeros(shape, dtype=dt, device=device)
+        self.v = to_device(v, device) if v is not None else torch.zeros(shape, dtype=dt, device=device)
+        assert tuple(self.k.shape) == shape and tuple(self.v.shape) == shape
+        self.block_table = torch.from_numpy(np.ascontiguousarray(block_table, dtype=np.int32)).to(device)
+        self.ctx_len = torch.from_numpy(np.ascontiguousarray(ctx_len, dtype=np.int32)).to(device)
+        self.batch, self.max_pages = int(block_table.shape[0]), int(block_table.shape[1])
+        self.n_pages = int(n_pages)
+        self.max_ctx = int(max_ctx if max_ctx is not None else int(np.max(ctx_len)))
+
+    def set_ctx_len(self, ctx_len: np.ndarray, max_ctx: Optional[int] = None) -> None:
+        self.ctx_len.copy_(torch.from_numpy(np.ascontiguousarray(ctx_len, dtype=np.int32)))
+        self.max_ctx = int(max_ctx if max_ctx is not None else int(np.max(ctx_len)))
+
+    def struct(self) -> L.DflashKV:
+        return L.make_kv(self.k, self.v, self.block_table, self.ctx_len, self.batch, self.max_pages,
+                         self.n_pages, self.max_ctx)
+
+
+class Drafter:
+    """One drafter handle with its device weights and a workspace."""
+
+    def __init__(self, cfg, weights: dict, max_batch: int, max_ctx: int, max_new: int, device="cuda"):
+        L.load()
+        self.cfg = cfg
+        self.device = device
+        self.w = {k: ([to_device(x, device) for x in v] if isinstance(v, list) else to_device(v, device))
+                  for k, v in weights.items()}
+        c = L.make_config(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn, cfg.vocab,
+                          cfg.n_layers, cfg.n_feat_layers, cfg.block_size, cfg.mask_token_id, cfg.dtype,
+                          cfg.rope_theta, cfg.rms_eps, cfg.page_size)
+        ws, self._keep = L.make_weights(self.w["embed"], self.w["lm_head"], self.w["w_fc"], self.w["final_norm"],
+                                        *[self.w[k] for k in _LAYER_KEYS])
+        self.handle = L.dflash_create(c, ws)
+        self.ws_bytes = L.dflash_workspace_size(self.handle, max_batch, max_ctx, max_new)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=device)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            L.dflash_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- the four hot calls ------------------------------------------------
+    def inject_context(self, feats: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor, kv: PagedKV) -> None:
+        L.dflash_inject_context(self.handle, feats, seq, pos, int(feats.shape[0]), kv.struct(), self.ws)
+
+    def draft_block(self, anchor_ids: torch.Tensor, kv: PagedKV, hidden_out: Optional[torch.Tensor] = None):
+        B = self.cfg.block_size
+        if hidden_out is None:
+            hidden_out = torch.empty((kv.batch * (B - 1), self.cfg.hidden), dtype=storage_dtype(self.cfg),
+                                     device=self.device)
+        L.dflash_draft_block(self.handle, anchor_ids, kv.struct(), hidden_out, self.ws)
+        return hidden_out
+
+    def lmhead_argmax(self, hidden: torch.Tensor, want_max: bool = True, want_logits: bool = False):
+        rows = int(hidden.shape[0])
+        ids = torch.empty(rows, dtype=torch.int32, device=self.device)
+        mx = torch.empty(rows, dtype=torch.float32, device=self.device) if want_max else None
+        lg = torch.empty((rows, self.cfg.vocab), dtype=torch.float32, device=self.device) if want_logits else None
+        L.dflash_lmhead_argmax(self.handle, hidden, rows, ids, mx, lg, self.ws)
+        return ids, mx, lg
+
+    @staticmethod
+    def accept_len(draft_ids: torch.Tensor, target_ids: torch.Tensor, block_size: int):
+        b = int(draft_ids.shape[0])
+        tau = torch.empty(b, dtype=torch.int32, device=draft_ids.device)
+        bonus = torch.empty(b, dtype=torch.int32, device=draft_ids.device)
+        L.dflash_accept_len(draft_ids, target_ids, b, block_size, tau, bonus)
+        return tau, bonus

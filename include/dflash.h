@@ -1,0 +1,183 @@
+/*
+ * dflash.h - C ABI of libdflash, the DFlash block-diffusion drafter step for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *  [FN]  "DFlash — 블록 확산 드래프터로 6배 빨라지는 투기적 디코딩" (LLM field
+ *        notes appendix), sections 1, 2, 3.1, 6, 7.
+ *  [INS] "한 번에 초안을 생성하는 DFlash …" (molayo insight article), paragraph on
+ *        multi-layer feature fusion and Key/Value injection.
+ *  [SUM] "기술 요약: DFlash – 플래시 추측적 디코딩을 위한 블록 확산" (gist.science
+ *        summary of arXiv 2602.06036), sections 2.2 and 2.3.
+ *  [PKR] "DFlash 소개" (discuss.pytorch.kr), ``spec_generate`` example.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer unless stated otherwise; the
+ *    library never allocates, frees or retains caller memory beyond the
+ *    lifetime stated below, and the compute entry points allocate nothing.
+ *  - Matrices are row-major [out, in].  The storage type of weights,
+ *    features, caches and hidden states is the handle's dtype (fp32 or bf16;
+ *    bf16 = raw 16-bit patterns).  Token ids are int32; logits are fp32.
+ *  - ``stream`` is a hipStream_t (NULL = the default stream).  All work is
+ *    enqueued on it asynchronously; nothing synchronises.
+ *  - Every call returns a dflash_status.  Validation happens on the host
+ *    before anything is enqueued; a failed validation enqueues nothing.
+ *    Device faults surface as HIP errors at the caller's next synchronisation.
+ *    Out-of-range device data (ids >= vocab, page ids >= n_pages) is the
+ *    caller's responsibility and is not checked on the device.
+ *  - A handle is not thread-safe; concurrent streams need separate
+ *    workspaces.  Two calls that share a workspace must be ordered on one
+ *    stream.
+ *  - A workspace must be zero-filled before its first use (a zero-filled
+ *    allocation, or dflash_workspace_init).  The counters in it are left at
+ *    zero by every call, so it can be reused without clearing.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dflash_handle_s *dflash_handle;
+
+typedef enum {
+    DFLASH_OK = 0,
+    DFLASH_ERR_NULL = -1,        /* a required pointer is NULL */
+    DFLASH_ERR_SHAPE = -2,       /* a size is out of the supported range */
+    DFLASH_ERR_DTYPE = -3,       /* unknown storage type */
+    DFLASH_ERR_RANGE = -4,       /* a host-side value is out of range */
+    DFLASH_ERR_WORKSPACE = -5,   /* workspace too small */
+    DFLASH_ERR_UNSUPPORTED = -6, /* combination not implemented */
+    DFLASH_ERR_HIP = -7          /* a HIP runtime call failed */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Drafter shape.  Supported: head_dim in {64, 128}; n_q_heads a multiple of
+ * n_kv_heads; (n_q_heads / n_kv_heads) * block_size <= 128; 2 <= block_size
+ * <= 64; hidden, n_q_heads*head_dim and ffn multiples of 64; vocab a multiple
+ * of 16; page_size 16; 1 <= n_layers <= 16.  The mask token is a row of the
+ * shared embedding (mask_token_id < vocab). */
+typedef struct {
+    int32_t hidden;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t ffn;
+    int32_t vocab;
+    int32_t n_layers;
+    int32_t n_feat_layers;   /* L: the context feature is [L * hidden] wide */
+    int32_t block_size;      /* B: anchor + (B-1) masked positions */
+    int32_t mask_token_id;
+    int32_t page_size;       /* positions per KV page; must be 16 */
+    int32_t dtype;           /* dflash_dtype */
+    float rope_theta;
+    float rms_eps;
+} dflash_config;
+
+/* Device pointers to the drafter's weights (borrowed for the handle's
+ * lifetime; the pointer arrays are copied at creation).  The embedding and the
+ * LM head are the target's, shared and frozen ([FN] §3.1; [SUM] §2.3). */
+typedef struct {
+    const void *embed;              /* [vocab, hidden] */
+    const void *lm_head;            /* [vocab, hidden] */
+    const void *w_fc;               /* [hidden, n_feat_layers*hidden] fusion projection */
+    const void *final_norm;         /* [hidden] */
+    const void *const *attn_norm;   /* n_layers host-array entries, each [hidden] */
+    const void *const *w_qkv;       /* [(nq + 2*nkv)*head_dim, hidden]: q rows, k rows, v rows */
+    const void *const *w_o;         /* [hidden, nq*head_dim] */
+    const void *const *mlp_norm;    /* [hidden] */
+    const void *const *w_gate_up;   /* [2*ffn, hidden]: gate rows first, then up rows */
+    const void *const *w_down;      /* [hidden, ffn] */
+} dflash_weights;
+
+/* Paged drafter context cache (injected K/V, [FN] §2 "KV injection").
+ * Position t of sequence s lives in physical page block_table[s*max_pages +
+ * t/page_size], slot t % page_size.  The anchor of sequence s sits at position
+ * ctx_len[s]; positions 0..ctx_len[s]-1 are the context. */
+typedef struct {
+    void *k;                        /* [n_layers][n_pages][page_size][n_kv_heads][head_dim] */
+    void *v;                        /* same layout as k */
+    const int32_t *block_table;     /* device [batch][max_pages] */
+    const int32_t *ctx_len;         /* device [batch] */
+    int32_t batch;
+    int32_t max_pages;
+    int32_t n_pages;
+    int32_t max_ctx;                /* HOST value: upper bound of every ctx_len[s];
+                                       sizes launch grids and workspace */
+} dflash_kv;
+
+/* Creates a handle for one drafter.  ``cfg`` and ``w`` are host structs read
+ * during the call; the weight memory they point to is borrowed until
+ * dflash_destroy.  Validates shapes only; launches nothing. */
+int dflash_create(const dflash_config *cfg, const dflash_weights *w, dflash_handle *out);
+
+/* Releases the handle (host memory only). */
+int dflash_destroy(dflash_handle h);
+
+/* Workspace bytes needed for calls with at most ``max_batch`` sequences, an
+ * upper bound ``max_ctx`` on context lengths, and at most ``max_new`` positions
+ * per dflash_inject_context call.  ``bytes`` is a host pointer. */
+int dflash_workspace_size(dflash_handle h, int32_t max_batch, int32_t max_ctx, int32_t max_new,
+                          size_t *bytes);
+
+/* Zero-fills the counter region of a workspace (enqueued on ``stream``). */
+int dflash_workspace_init(dflash_handle h, void *ws, size_t ws_bytes, void *stream);
+
+/* A1 + A2: feature fusion and KV injection ([INS]; [SUM] §2.2; [FN] §2).
+ * For each of the ``n_new`` rows: c = W_fc * feats[row] (rounded to the
+ * storage type), then for every drafter layer l the layer's own K and V
+ * projections of c are written to the cache at (seq[row], pos[row]); K gets
+ * RoPE at pos[row].
+ *   feats  [n_new, n_feat_layers*hidden] storage type
+ *   seq    [n_new] int32 sequence index (< kv->batch)
+ *   pos    [n_new] int32 position (< kv->max_pages * page_size)
+ * Rows must not write the same (seq, pos) twice in one call.  ctx_len is not
+ * read or written; the caller advances it. */
+int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq, const int32_t *pos,
+                          int32_t n_new, const dflash_kv *kv, void *ws, size_t ws_bytes, void *stream);
+
+/* A3..A8: one drafter forward pass over each sequence's block
+ * [anchor, mask x (B-1)] at positions ctx_len[s] .. ctx_len[s]+B-1 ([FN] §2
+ * cycle and §7; [SUM] §2.2).  Attention covers the context K/V and the block's
+ * own K/V without a mask ([FN] §6).  The block K/V stay in the workspace: the
+ * context cache is only read.
+ *   anchor_ids [kv->batch] int32
+ *   hidden_out [kv->batch * (B-1), hidden] storage type: final-norm hidden
+ *              states of mask rows 1..B-1 of every sequence (sequence-major). */
+int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_kv *kv, void *hidden_out,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* A9: shared LM head and greedy argmax ([FN] §3.1; [SUM] §2.3).
+ * logits = hidden * lm_head^T in fp32; ids_out[r] = the lowest id among the
+ * maxima of row r.
+ *   hidden        [rows, hidden] storage type
+ *   ids_out       [rows] int32
+ *   max_logit_out [rows] fp32, may be NULL
+ *   logits_out    [rows, vocab] fp32, may be NULL (materialises the logits; testing aid) */
+int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int32_t *ids_out,
+                         float *max_logit_out, float *logits_out, void *ws, size_t ws_bytes, void *stream);
+
+/* A10: greedy verify ([FN] §1 and §2 box, point (b)).  For each sequence,
+ * k = the number of leading positions where draft_ids equals target_ids
+ * (at most B-1), accept_len_out = k + 1 and bonus_out = target_ids[k].
+ *   draft_ids  [batch, B-1] int32: d_1..d_{B-1}
+ *   target_ids [batch, B]   int32: the target's greedy token y_1..y_B for the
+ *              positions after anchor, d_1, .., d_{B-1}
+ * Needs no handle; 2 <= block_size <= 64. */
+int dflash_accept_len(const int32_t *draft_ids, const int32_t *target_ids, int32_t batch, int32_t block_size,
+                      int32_t *accept_len_out, int32_t *bonus_out, void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *dflash_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

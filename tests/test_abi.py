@@ -1,0 +1,136 @@
+"""C ABI of libdflash on the CPU: the library loads, exports every entry point
+``include/dflash.h`` declares, and rejects bad arguments on the host (no GPU
+call is made on any path exercised here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diffusion_drafter_gemm_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(dflash_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libdflash.so is not built (run __graft_entry__.build())")
+    return L.load()
+
+
+def test_header_declares_the_hot_calls():
+    syms = declared_symbols()
+    for s in ("dflash_inject_context", "dflash_draft_block", "dflash_lmhead_argmax", "dflash_accept_len"):
+        assert s in syms
+    assert set(syms) == set(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+    out = os.popen(f"nm -D --defined-only {L.LIB_PATH}").read()
+    for s in declared_symbols():
+        assert re.search(rf"\bT {s}\b", out), s
+
+
+def test_status_strings(lib):
+    assert L.status_str(0) == "ok"
+    assert "workspace" in L.status_str(-5)
+    assert L.status_str(12345) == "unknown status"
+
+
+FAKE = 0x10000  # never dereferenced: validation fails or the call stops before any launch
+
+
+def good_config(**kw):
+    c = dict(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, ffn=512, vocab=1024, n_layers=2,
+             n_feat_layers=3, block_size=4, mask_token_id=1023, dtype="bf16", rope_theta=1e6, rms_eps=1e-6)
+    c.update(kw)
+    return L.make_config(**c)
+
+
+def fake_weights(n_layers=2):
+    arr = (ctypes.c_void_p * n_layers)(*([FAKE] * n_layers))
+    pp = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    return L.DflashWeights(FAKE, FAKE, FAKE, FAKE, pp, pp, pp, pp, pp, pp), arr
+
+
+def create(cfg):
+    w, keep = fake_weights(cfg.n_layers)
+    h = ctypes.c_void_p()
+    st = L.load().dflash_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h))
+    return st, h.value
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(head_dim=96), -2), (dict(n_q_heads=5), -2), (dict(hidden=100), -2), (dict(ffn=100), -2),
+    (dict(vocab=1000 + 3), -2), (dict(block_size=1), -2), (dict(block_size=65), -2), (dict(n_layers=0), -2),
+    (dict(n_layers=17), -2), (dict(mask_token_id=1024), -4), (dict(dtype="bf16", rope_theta=0.0), -4),
+    (dict(n_q_heads=32, n_kv_heads=1, block_size=16), -2),
+])
+def test_create_rejects_bad_config(lib, bad, code):
+    st, h = create(good_config(**bad))
+    assert st == code and not h
+
+
+def test_create_rejects_bad_dtype(lib):
+    cfg = good_config()
+    cfg.dtype = 7
+    assert create(cfg)[0] == -3
+
+
+def test_create_rejects_null(lib):
+    h = ctypes.c_void_p()
+    assert lib.dflash_create(None, None, ctypes.byref(h)) == -1
+    cfg = good_config()
+    w, keep = fake_weights()
+    w.w_fc = None
+    assert lib.dflash_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)) == -1
+
+
+def test_workspace_size_and_host_validation(lib):
+    st, h = create(good_config())
+    assert st == 0 and h
+    try:
+        n1 = L.dflash_workspace_size(h, 1, 64, 16)
+        n2 = L.dflash_workspace_size(h, 8, 4096, 256)
+        assert 0 < n1 < n2
+        with pytest.raises(L.DflashError) as e:
+            L.dflash_workspace_size(h, 0, 64, 16)
+        assert e.value.status == -2
+        kv = L.DflashKV(FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 64)
+        # null anchor / workspace: rejected before any launch
+        assert lib.dflash_draft_block(h, None, ctypes.byref(kv), FAKE, FAKE, n1, None) == -1
+        assert lib.dflash_draft_block(h, FAKE, None, FAKE, FAKE, n1, None) == -1
+        # workspace too small
+        assert lib.dflash_draft_block(h, FAKE, ctypes.byref(kv), FAKE, FAKE, 1024, None) == -5
+        assert lib.dflash_lmhead_argmax(h, FAKE, 3, FAKE, None, None, FAKE, 1024, None) == -5
+        assert lib.dflash_inject_context(h, FAKE, FAKE, FAKE, 16, ctypes.byref(kv), FAKE, 1024, None) == -5
+        # empty work is a no-op
+        assert lib.dflash_lmhead_argmax(h, None, 0, None, None, None, None, 0, None) == 0
+        assert lib.dflash_inject_context(h, None, None, None, 0, ctypes.byref(kv), None, 0, None) == 0
+        # bad cache descriptors
+        bad = L.DflashKV(FAKE, FAKE, FAKE, FAKE, 0, 8, 8, 64)
+        assert lib.dflash_draft_block(h, FAKE, ctypes.byref(bad), FAKE, FAKE, n1, None) == -2
+        nul = L.DflashKV(FAKE, None, FAKE, FAKE, 1, 8, 8, 64)
+        assert lib.dflash_draft_block(h, FAKE, ctypes.byref(nul), FAKE, FAKE, n1, None) == -1
+        assert lib.dflash_lmhead_argmax(h, FAKE, -1, FAKE, None, None, FAKE, n1, None) == -2
+        assert lib.dflash_workspace_init(h, FAKE, 16, None) == -5
+    finally:
+        assert lib.dflash_destroy(h) == 0
+    assert lib.dflash_destroy(None) == -1
+
+
+def test_accept_len_host_validation(lib):
+    assert lib.dflash_accept_len(FAKE, FAKE, 4, 1, FAKE, FAKE, None) == -2
+    assert lib.dflash_accept_len(FAKE, FAKE, 4, 65, FAKE, FAKE, None) == -2
+    assert lib.dflash_accept_len(None, FAKE, 4, 16, FAKE, FAKE, None) == -1
+    assert lib.dflash_accept_len(FAKE, FAKE, -1, 16, FAKE, FAKE, None) == -2
+    assert lib.dflash_accept_len(None, None, 0, 16, None, None, None) == 0

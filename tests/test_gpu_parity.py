@@ -1,0 +1,243 @@
+"""GPU parity of every libdflash entry point against the CPU oracle, on small
+shapes with ragged tails (several tiles, partial column groups, contexts that
+are not page multiples, padded query tiles, fp32 and bf16 storage).
+
+Token ids and accept lengths must match exactly (ids may differ only on an
+oracle near-tie); hidden states, cache entries and logits must be within
+1e-4 (fp32) or 2e-2 (bf16) of the oracle, scaled by max(1, |oracle|).
+"""
+import numpy as np
+import pytest
+
+import dflash_synth as S
+from oracle import drafter as D
+from oracle.numerics import bf16_bits, from_storage, round_storage
+
+from gpu_cases import MINI, assert_close, check_ids, gather_ctx, log, oracle_draft, tol_of
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_diffusion_drafter_gemm_amd import _lib
+    _lib.load()
+
+
+def runtime():
+    from block_diffusion_drafter_gemm_amd import runtime as R
+    return R
+
+
+def storage_of(cfg, x):
+    """float64 values already representable in the storage type -> storage array."""
+    return bf16_bits(x) if cfg.dtype == "bf16" else np.asarray(x, dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------
+# A10 accept length
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("B", [2, 4, 10, 16, 64])
+def test_accept_len(B):
+    log(f"accept_len B={B}")
+    cfg = S.get_config("llama31_8b", block_size=B)
+    n = 3000
+    d = S.draft_ids_random(cfg, n, seed=B)
+    y = S.target_ids_for(cfg, d, seed=B)
+    y[0, :-1] = d[0]                       # all drafts accepted
+    y[1, 0] = (d[1, 0] + 1) % cfg.vocab    # first draft rejected
+    tau_o, bonus_o = D.accept_len_batch(d, y)
+    dt, yt = torch.from_numpy(d).cuda(), torch.from_numpy(y).cuda()
+    tau, bonus = runtime().Drafter.accept_len(dt, yt, B)
+    torch.cuda.synchronize()
+    assert np.array_equal(tau.cpu().numpy(), tau_o)
+    assert np.array_equal(bonus.cpu().numpy(), bonus_o)
+    assert tau_o[0] == B and tau_o[1] == 1
+
+
+# ----------------------------------------------------------------------------
+# A9 LM head + argmax
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "mini_bf16", "mini_f32", "mini_b10"])
+@pytest.mark.parametrize("rows", [1, 15, 33, 70])
+def test_lmhead_argmax(name, rows):
+    cfg = MINI[name]
+    log(f"lmhead_argmax {name} rows={rows}")
+    R = runtime()
+    w = S.drafter_weights(cfg, seed=1)
+    # duplicate a vocabulary row at a higher id: exact ties must go to the lower id
+    w["lm_head"][cfg.vocab - 3] = w["lm_head"][5]
+    dr = R.Drafter(cfg, w, max_batch=(rows + cfg.block_size - 2) // (cfg.block_size - 1), max_ctx=16, max_new=1)
+    z = S.normal_matrix(cfg, 77, (rows, cfg.hidden), 1.0, seed=rows)
+    # row 0 points at vocabulary row 5, so ids 5 and vocab-3 tie exactly at the top
+    z[0] = storage_of(cfg, round_storage(from_storage(w["lm_head"][5]) * 50.0, cfg.dtype))
+    z_dev = R.to_device(z)
+    ids, mx, lg = dr.lmhead_argmax(z_dev, want_max=True, want_logits=True)
+    torch.cuda.synchronize()
+    ids_o, best_o, logits_o = D.lm_argmax(w["lm_head"], z)
+    assert_close(lg.cpu().numpy(), logits_o, 1e-4, f"{name} logits")
+    assert_close(mx.cpu().numpy(), best_o, 1e-4, f"{name} max logit")
+    check_ids(ids.cpu().numpy(), ids_o, logits_o, tol_of(cfg), f"{name} ids")
+    # rows whose best is the duplicated row: the GPU must return the lower id 5
+    g = ids.cpu().numpy()
+    assert g[0] == 5 and ids_o[0] == 5
+    assert not np.any(g == cfg.vocab - 3)
+    dr.close()
+
+
+# ----------------------------------------------------------------------------
+# A1 + A2 inject
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "mini_bf16", "mini_d64", "mini_f32"])
+@pytest.mark.parametrize("n_new", [1, 16, 90])
+def test_inject_context(name, n_new):
+    cfg = MINI[name]
+    log(f"inject {name} n_new={n_new}")
+    R = runtime()
+    w = S.drafter_weights(cfg, seed=2)
+    batch = 3
+    lens = np.array([n_new, n_new + 7, 3], dtype=np.int32)
+    lay = S.paged_layout(cfg, lens, headroom=cfg.block_size, seed=2)
+    rng = np.random.default_rng(n_new)
+    # n_new distinct (seq, pos) slots, scattered over the sequences
+    slots = [(s, p) for s in range(batch) for p in range(int(lens[s]) + cfg.block_size)]
+    pick = rng.choice(len(slots), size=n_new, replace=False)
+    seq = np.array([slots[i][0] for i in pick], dtype=np.int32)
+    pos = np.array([slots[i][1] for i in pick], dtype=np.int32)
+    feats = S.features(cfg, n_new, seed=3)
+    dr = R.Drafter(cfg, w, max_batch=batch, max_ctx=int(lens.max()), max_new=n_new)
+    kv = R.PagedKV(cfg, lay.block_table, lens, lay.n_pages)
+    dr.inject_context(R.to_device(feats), torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), kv)
+    torch.cuda.synchronize()
+    K_o, V_o = D.inject(w, cfg, feats, pos)
+    Kg, Vg = R.to_host_storage(kv.k), R.to_host_storage(kv.v)
+    pages = lay.block_table[seq, pos // cfg.page_size]
+    sl = pos % cfg.page_size
+    tol = tol_of(cfg)
+    assert_close(from_storage(Kg[:, pages, sl]), K_o, tol, f"{name} injected K")
+    assert_close(from_storage(Vg[:, pages, sl]), V_o, tol, f"{name} injected V")
+    # nothing else was written
+    mask = np.ones(Kg.shape[:3], dtype=bool)
+    mask[:, pages, sl] = False
+    assert not from_storage(Kg[mask]).any() and not from_storage(Vg[mask]).any()
+    dr.close()
+
+
+# ----------------------------------------------------------------------------
+# A3..A8 draft block (+ A9 on its output)
+# ----------------------------------------------------------------------------
+def run_draft_case(cfg, seed=0, lens=None, check_seqs=None):
+    R = runtime()
+    w = S.drafter_weights(cfg, seed=seed, random_gain=True)
+    lens = S.ctx_lens(cfg, seed=seed) if lens is None else np.asarray(lens, dtype=np.int32)
+    batch = len(lens)
+    lay = S.paged_layout(cfg, lens, headroom=cfg.block_size, seed=seed)
+    Kp, Vp = S.ctx_kv_cache(cfg, lay, seed=seed)
+    anchors = S.anchor_ids(cfg, seed=seed, batch=batch)
+    dr = R.Drafter(cfg, w, max_batch=batch, max_ctx=int(lens.max()), max_new=1)
+    kv = R.PagedKV(cfg, lay.block_table, lens, lay.n_pages, k=Kp, v=Vp)
+    k0, v0 = kv.k.clone(), kv.v.clone()
+    hid = dr.draft_block(torch.from_numpy(anchors).cuda(), kv)
+    ids, mx, _ = dr.lmhead_argmax(hid)
+    hid2 = dr.draft_block(torch.from_numpy(anchors).cuda(), kv)     # determinism
+    torch.cuda.synchronize()
+    assert torch.equal(hid, hid2), "draft_block is not deterministic"
+    assert torch.equal(kv.k, k0) and torch.equal(kv.v, v0), "draft_block wrote the context cache"
+    hid_h = from_storage(R.to_host_storage(hid)).reshape(batch, cfg.block_size - 1, cfg.hidden)
+    ids_h = ids.cpu().numpy().reshape(batch, cfg.block_size - 1)
+    tol = tol_of(cfg)
+    seqs = range(batch) if check_seqs is None else check_seqs
+    for s in seqs:
+        Z = oracle_draft(cfg, w, anchors[s], Kp, Vp, lay.block_table, s, int(lens[s]))
+        assert_close(hid_h[s], Z, tol, f"{cfg.name} seq {s} (ctx {lens[s]}) hidden")
+        ids_o, _, logits_o = D.lm_argmax(w["lm_head"], Z)
+        check_ids(ids_h[s], ids_o, logits_o, tol, f"{cfg.name} seq {s} draft ids")
+    dr.close()
+    return hid_h, ids_h
+
+
+@pytest.mark.parametrize("name", ["tiny", "mini_bf16", "mini_b10", "mini_d64", "mini_f32"])
+def test_draft_block(name):
+    log(f"draft_block {name}")
+    run_draft_case(MINI[name], seed=0)
+
+
+def test_draft_block_empty_and_short_context():
+    cfg = MINI["mini_bf16"]
+    log("draft_block ctx 0/1/16")
+    run_draft_case(cfg, seed=5, lens=[0, 1, 16])
+
+
+def test_draft_independent_of_anchor_for_cache():
+    """Context K/V written by inject depend on the features only."""
+    cfg = MINI["mini_bf16"]
+    R = runtime()
+    log("inject/draft cache independence")
+    w = S.drafter_weights(cfg, seed=4)
+    lens = np.array([40], dtype=np.int32)
+    lay = S.paged_layout(cfg, lens, headroom=cfg.block_size, seed=4)
+    feats = R.to_device(S.features(cfg, 40, seed=4))
+    seq = torch.zeros(40, dtype=torch.int32, device="cuda")
+    pos = torch.arange(40, dtype=torch.int32, device="cuda")
+    dr = R.Drafter(cfg, w, max_batch=1, max_ctx=40, max_new=40)
+    kv = R.PagedKV(cfg, lay.block_table, lens, lay.n_pages)
+    dr.inject_context(feats, seq, pos, kv)
+    k0 = kv.k.clone()
+    for a in (3, 77, cfg.vocab - 1):
+        dr.draft_block(torch.tensor([a], dtype=torch.int32, device="cuda"), kv)
+    kv2 = R.PagedKV(cfg, lay.block_table, lens, lay.n_pages)
+    dr.inject_context(feats, seq, pos, kv2)
+    torch.cuda.synchronize()
+    assert torch.equal(kv.k, k0) and torch.equal(kv2.k, k0) and torch.equal(kv2.v, kv.v)
+    dr.close()
+
+
+# ----------------------------------------------------------------------------
+# end to end: greedy speculative decoding with the GPU drafter is lossless
+# ----------------------------------------------------------------------------
+class GpuDrafter:
+    """Speculative-loop adapter: the GPU drafter behind the C ABI."""
+
+    def __init__(self, cfg, w, max_positions):
+        R = runtime()
+        self.R, self.cfg = R, cfg
+        self.d = R.Drafter(cfg, w, max_batch=1, max_ctx=max_positions, max_new=max_positions)
+        lay = S.paged_layout(cfg, np.array([max_positions]), headroom=0, seed=9)
+        self.kv = R.PagedKV(cfg, lay.block_table, np.array([0]), lay.n_pages)
+        self.ctx = 0
+
+    def inject(self, feats, pos):
+        R = self.R
+        f = R.to_device(storage_of(self.cfg, feats))
+        seq = torch.zeros(len(pos), dtype=torch.int32, device="cuda")
+        p = torch.from_numpy(np.asarray(pos, dtype=np.int32)).cuda()
+        self.d.inject_context(f, seq, p, self.kv)
+        self.ctx += len(pos)
+        self.kv.set_ctx_len(np.array([self.ctx]))
+
+    def draft(self, anchor):
+        hid = self.d.draft_block(torch.tensor([anchor], dtype=torch.int32, device="cuda"), self.kv)
+        ids, _, _ = self.d.lmhead_argmax(hid, want_max=False)
+        return ids.cpu().numpy()
+
+
+@pytest.mark.parametrize("seed,layer_std", [(0, 0.02), (1, 0.1), (2, 0.05)])
+def test_lossless_speculative_decoding_with_gpu_drafter(seed, layer_std):
+    from oracle import target as T
+    cfg = MINI["tiny"]
+    log(f"lossless e2e seed={seed} layer_std={layer_std}")
+    tgt = T.TinyTarget(S.target_weights(cfg, seed, layer_std=layer_std), cfg)
+    prompt = S.prompt_ids(cfg, seed)
+    g = T.greedy_decode(tgt, prompt, cfg.new_tokens)
+    gd = GpuDrafter(cfg, S.drafter_weights(cfg, seed), cfg.prompt_len + cfg.new_tokens + 2 * cfg.block_size)
+    s, taus = T.spec_decode(tgt, gd, prompt, cfg.new_tokens, cfg.dtype)
+    assert np.array_equal(g, s)
+    # the oracle drafter, run on the same inputs, drafts the same blocks
+    s2, taus2 = T.spec_decode(tgt, D.OracleDrafter(S.drafter_weights(cfg, seed), cfg), prompt, cfg.new_tokens,
+                              cfg.dtype)
+    assert np.array_equal(s2, g)
+    log(f"  taus gpu {taus} oracle {taus2}")
+    gd.d.close()
