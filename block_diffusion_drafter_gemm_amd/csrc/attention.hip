@@ -13,7 +13,8 @@
 // lane holds 4 keys of one query row; the exponentiated scores of two 16-key
 // tiles are then exactly that lane's fragment of P^T, and O^T = V^T P^T keeps
 // the query row in the same lane, which makes the online-softmax rescale
-// lane-local.
+// lane-local.  With bf16 storage the softmax weights enter the P*V product as
+// two bf16 terms (P_hi + P_lo), so P keeps about 16 mantissa bits.
 #include "dflash_device.h"
 #include "dflash_internal.h"
 
@@ -189,12 +190,20 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           p[e] = exp2f(p[e] - m_new);
-          psum += Storage<T>::round(p[e]);   // the weights the P*V product uses
+          psum += p[e];
         }
         l_run[t] = l_run[t] * alpha + psum;
         m_run[t] = m_new;
-        Frag<T> pf;
+        // bf16: P = P_hi + P_lo, two bf16 terms, so the product keeps ~16
+        // mantissa bits of the softmax weights instead of 8
+        Frag<T> pf, pf_lo;
         pf.set(p);
+        if constexpr (sizeof(T) == 2) {
+          float lo[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lo[e] = p[e] - pf.get(e);
+          pf_lo.set(lo);
+        }
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
           o[t][d] *= alpha;
@@ -209,6 +218,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
             reinterpret_cast<Frag<float> &>(vf).hi = *reinterpret_cast<const float4 *>(vr + 16);
           }
           o[t][d] = mma(o[t][d], vf, pf);
+          if constexpr (sizeof(T) == 2) o[t][d] = mma(o[t][d], vf, pf_lo);
         }
       }
     }

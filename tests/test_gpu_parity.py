@@ -153,8 +153,10 @@ def run_draft_case(cfg, seed=0, lens=None, check_seqs=None):
     for s in seqs:
         Z = oracle_draft(cfg, w, anchors[s], Kp, Vp, lay.block_table, s, int(lens[s]))
         assert_close(hid_h[s], Z, tol, f"{cfg.name} seq {s} (ctx {lens[s]}) hidden")
-        ids_o, _, logits_o = D.lm_argmax(w["lm_head"], Z)
+        ids_o, best_o, logits_o = D.lm_argmax(w["lm_head"], Z)
         check_ids(ids_h[s], ids_o, logits_o, tol, f"{cfg.name} seq {s} draft ids")
+        mx_h = mx.cpu().numpy().reshape(batch, cfg.block_size - 1)
+        assert_close(mx_h[s], best_o, tol, f"{cfg.name} seq {s} max logit")
     dr.close()
     return hid_h, ids_h
 
