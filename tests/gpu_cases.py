@@ -60,6 +60,20 @@ def assert_close(got, want, tol: float, what: str) -> None:
     assert worst <= tol, f"{what}: max scaled error {worst:.3e} > {tol:g}"
 
 
+def assert_rows_close(got, want, tol: float, what: str) -> float:
+    """Per-row normwise relative error ||got - want|| / ||want|| <= tol."""
+    got = np.asarray(got, dtype=np.float64).reshape(-1, np.shape(want)[-1])
+    want = np.asarray(want, dtype=np.float64).reshape(got.shape)
+    num = np.linalg.norm(got - want, axis=1)
+    den = np.maximum(np.linalg.norm(want, axis=1), 1e-30)
+    rel = num / den
+    el = np.abs(got - want) / np.maximum(1.0, np.abs(want))
+    log(f"  {what}: row-norm relative error max {rel.max():.3e} mean {rel.mean():.3e} "
+        f"(tol {tol:g}); elementwise max {el.max():.3e}")
+    assert rel.max() <= tol, f"{what}: row-norm relative error {rel.max():.3e} > {tol:g}"
+    return float(rel.max())
+
+
 def check_ids(ids_gpu, ids_oracle, logits_oracle, tol: float, what: str) -> int:
     """Token ids must match, except where the GPU's choice is an oracle near-tie:
     oracle_logit[g] >= oracle_logit[o] - tol * max(1, |oracle_logit[o]|)."""

@@ -3,7 +3,22 @@ benchmark times: Qwen3-8B shape (batch 1, context 2048, B=16), LLaMA-3.1-8B
 shape (batch 1, context 4096, B=10), Qwen3-8B shape at batch 32 with ragged
 contexts 512..8192, and the Qwen3-Coder-30B-A3B shape (8 layers, batch 4,
 context 16384).  The oracle recomputes sampled sequences one by one.
+
+Each workload runs in three variants:
+* bf16 storage, all layers.  Bar: per-row relative error of the hidden states
+  and of the logit vectors <= 5e-2.  An fp32-accumulation evaluation of the
+  same bf16 rounding contract already sits 2.2% (row norm) from the float64
+  oracle at the Qwen3-8B shape, because rounding flips cascade through the
+  layers; the bar is that floor with a factor ~2 margin.
+* fp32 storage of the same shapes, all layers: per-row relative error <= 1e-4
+  (measured floor 1.6e-5).  Same kernels and indexing as bf16, tight bar.
+* bf16 storage, one layer: elementwise <= 2e-2 * max(1, |oracle|)
+  (measured floor 7.8e-3).
+Token ids must match except on oracle near-ties (2e-2 bf16 / 1e-4 fp32 of
+max(1, |logit|)); accept lengths must match exactly whenever the ids do.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -11,7 +26,7 @@ import dflash_synth as S
 from oracle import drafter as D
 from oracle.numerics import from_storage
 
-from gpu_cases import assert_close, check_ids, log, oracle_draft, tol_of
+from gpu_cases import assert_close, assert_rows_close, check_ids, log, oracle_draft, tol_of
 
 torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
@@ -29,38 +44,53 @@ def _gpu():
     _STATE.clear()
 
 
-def state(name):
-    """Weights, drafter and synthetic paged cache of a configuration (built once)."""
+def variant_cfg(name, dtype, layers):
+    cfg = S.get_config(name)
+    over = {}
+    if dtype != cfg.dtype:
+        over["dtype"] = dtype
+    if layers is not None:
+        over["n_layers"] = layers
+    return dataclasses.replace(cfg, **over) if over else cfg
+
+
+def state(name, dtype, layers):
+    """Weights, drafter and synthetic paged cache of a variant (one resident at a time)."""
     from block_diffusion_drafter_gemm_amd import runtime as R
-    if name in _STATE:
-        return _STATE[name]
-    for other in list(_STATE):            # keep one configuration resident at a time
+    key = (name, dtype, layers)
+    if key in _STATE:
+        return _STATE[key]
+    for other in list(_STATE):
         _STATE.pop(other)["dr"].close()
     torch.cuda.empty_cache()
-    cfg = S.get_config(name)
-    log(f"[{name}] generating weights")
+    cfg = variant_cfg(name, dtype, layers)
+    log(f"[{key}] generating weights")
     w = S.drafter_weights(cfg, seed=0)
     lens = S.ctx_lens(cfg, seed=0)
     lay = S.paged_layout(cfg, lens, headroom=cfg.block_size, seed=0)
-    log(f"[{name}] generating context cache ({lay.n_pages} pages)")
+    log(f"[{key}] generating context cache ({lay.n_pages} pages)")
     Kp, Vp = S.ctx_kv_cache(cfg, lay, seed=0)
     dr = R.Drafter(cfg, w, max_batch=cfg.batch, max_ctx=int(lens.max()), max_new=256)
     kv = R.PagedKV(cfg, lay.block_table, lens, lay.n_pages, k=Kp, v=Vp)
-    _STATE[name] = dict(cfg=cfg, w=w, lens=lens, lay=lay, Kp=Kp, Vp=Vp, dr=dr, kv=kv, R=R)
-    return _STATE[name]
+    _STATE[key] = dict(cfg=cfg, w=w, lens=lens, lay=lay, Kp=Kp, Vp=Vp, dr=dr, kv=kv, R=R)
+    return _STATE[key]
 
 
 SAMPLED = {"qwen3_8b": None, "llama31_8b": None, "qwen3_8b_b32": "minmax", "qwen3_coder_30b": [2]}
+VARIANTS = [("qwen3_8b", "bf16", None), ("qwen3_8b", "f32", None), ("qwen3_8b", "bf16", 1),
+            ("llama31_8b", "bf16", None), ("llama31_8b", "f32", None),
+            ("qwen3_8b_b32", "bf16", None), ("qwen3_8b_b32", "f32", None),
+            ("qwen3_coder_30b", "bf16", None), ("qwen3_coder_30b", "f32", None), ("qwen3_coder_30b", "bf16", 1)]
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["qwen3_8b", "llama31_8b", "qwen3_8b_b32", "qwen3_coder_30b"])
-def test_full_draft_step(name):
-    st = state(name)
+@pytest.mark.parametrize("name,dtype,layers", VARIANTS)
+def test_full_draft_step(name, dtype, layers):
+    st = state(name, dtype, layers)
     cfg, w, lens, lay, dr, kv = st["cfg"], st["w"], st["lens"], st["lay"], st["dr"], st["kv"]
     b, B = cfg.batch, cfg.block_size
     anchors = S.anchor_ids(cfg, seed=0)
-    log(f"[{name}] GPU draft step")
+    log(f"[{name} {dtype} layers={cfg.n_layers}] GPU draft step")
     k0 = kv.k[:, :4].clone()
     hid = dr.draft_block(torch.from_numpy(anchors).cuda(), kv)
     ids, mx, _ = dr.lmhead_argmax(hid)
@@ -73,36 +103,41 @@ def test_full_draft_step(name):
     tau, bonus = tau.cpu().numpy(), bonus.cpu().numpy()
     hid_h = from_storage(st["R"].to_host_storage(hid)).reshape(b, B - 1, cfg.hidden)
     pick = SAMPLED[name]
-    if pick is None:
-        seqs = list(range(b))
-    elif pick == "minmax":
-        seqs = [int(np.argmin(lens)), int(np.argmax(lens))]
-    else:
-        seqs = pick
+    seqs = (list(range(b)) if pick is None else
+            [int(np.argmin(lens)), int(np.argmax(lens))] if pick == "minmax" else pick)
     tol = tol_of(cfg)
     d_mixed = d_gpu.copy()
     for s in seqs:
-        log(f"[{name}] oracle for sequence {s} (context {lens[s]})")
+        log(f"  oracle for sequence {s} (context {lens[s]})")
         Z = oracle_draft(cfg, w, anchors[s], st["Kp"], st["Vp"], lay.block_table, s, int(lens[s]))
-        assert_close(hid_h[s], Z, tol, f"{name} seq {s} hidden")
         ids_o, best_o, logits_o = D.lm_argmax(w["lm_head"], Z)
-        excused = check_ids(d_gpu[s], ids_o, logits_o, tol, f"{name} seq {s} ids")
-        assert_close(mx.cpu().numpy().reshape(b, B - 1)[s], best_o, tol, f"{name} seq {s} max logit")
+        if cfg.dtype == "f32":
+            assert_rows_close(hid_h[s], Z, 1e-4, f"seq {s} hidden")
+            assert_close(mx.cpu().numpy().reshape(b, B - 1)[s], best_o, 1e-4, f"seq {s} max logit")
+        elif cfg.n_layers == 1:
+            assert_close(hid_h[s], Z, 2e-2, f"seq {s} hidden")
+            assert_close(mx.cpu().numpy().reshape(b, B - 1)[s], best_o, 2e-2, f"seq {s} max logit")
+        else:
+            assert_rows_close(hid_h[s], Z, 5e-2, f"seq {s} hidden")
+            logits_g = D.lm_logits(w["lm_head"], hid_h[s])   # oracle LM head on the GPU's hidden states
+            assert_rows_close(logits_o, D.lm_logits(w["lm_head"], Z), 1e-12, f"seq {s} oracle logits")
+            assert_rows_close(logits_g, logits_o, 5e-2, f"seq {s} logits")
+        excused = check_ids(d_gpu[s], ids_o, logits_o, tol, f"seq {s} ids")
         d_mixed[s] = ids_o
         if not excused:
             y_o = S.target_ids_for(cfg, d_mixed, seed=0)[s]
             t_o, b_o = D.accept_len(ids_o, y_o)
             assert (tau[s], bonus[s]) == (t_o, b_o)
-    # every sequence's accept length follows the prefix rule on its own inputs
     assert np.all((tau >= 1) & (tau <= B))
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,n_new", [("qwen3_8b", 16), ("qwen3_8b", 200), ("qwen3_coder_30b", 16),
-                                        ("llama31_8b", 10)])
-def test_full_inject(name, n_new):
+@pytest.mark.parametrize("name,dtype,n_new", [("qwen3_8b", "bf16", 16), ("qwen3_8b", "bf16", 200),
+                                              ("qwen3_8b", "f32", 16), ("qwen3_coder_30b", "bf16", 16),
+                                              ("llama31_8b", "bf16", 10)])
+def test_full_inject(name, dtype, n_new):
     from block_diffusion_drafter_gemm_amd import runtime as R
-    st = state(name)
+    st = state(name, dtype, None)
     cfg, w, dr = st["cfg"], st["w"], st["dr"]
     lens = np.full(cfg.batch, 0, dtype=np.int32)
     lay = S.paged_layout(cfg, np.array([n_new] * cfg.batch), headroom=0, seed=1)
@@ -110,21 +145,20 @@ def test_full_inject(name, n_new):
     pos = np.arange(n_new, dtype=np.int32)
     seq = np.full(n_new, cfg.batch - 1, dtype=np.int32)
     feats = S.features(cfg, n_new, seed=5)
-    log(f"[{name}] GPU inject n_new={n_new}")
+    log(f"[{name} {dtype}] GPU inject n_new={n_new}")
     dr.inject_context(R.to_device(feats), torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), kv)
     torch.cuda.synchronize()
-    log(f"[{name}] oracle inject")
     K_o, V_o = D.inject(w, cfg, feats, pos)
     pages = lay.block_table[seq, pos // 16]
     Kg = from_storage(R.to_host_storage(kv.k)[:, pages, pos % 16])
     Vg = from_storage(R.to_host_storage(kv.v)[:, pages, pos % 16])
-    assert_close(Kg, K_o, tol_of(cfg), f"{name} K")
-    assert_close(Vg, V_o, tol_of(cfg), f"{name} V")
+    assert_close(Kg, K_o, tol_of(cfg), "K")
+    assert_close(Vg, V_o, tol_of(cfg), "V")
 
 
 @pytest.mark.timeout(600)
 def test_full_lmhead_identical_input():
-    st = state("qwen3_8b")
+    st = state("qwen3_8b", "bf16", None)
     cfg, w, dr = st["cfg"], st["w"], st["dr"]
     z = S.normal_matrix(cfg, 88, (15, cfg.hidden), 1.0, seed=0)
     log("[qwen3_8b] GPU LM head on fixed hidden states")
