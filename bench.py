@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the DFlash drafter step on one MI355X.
+
+One step = dflash_draft_block + dflash_lmhead_argmax + dflash_accept_len over
+one batch of synthetic input (the Qwen3-8B-shaped drafter at batch 1, context
+2048, B = 16 by default), with weights, context cache and ids resident in HBM
+before the timed region.  Prints one JSON line: drafted tokens/s as ``value``,
+the step latency, the HBM fraction of the step, the roofline of the dominant
+kernel (the LM-head GEMM with its argmax), and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
+METRIC = "draft-block latency (µs) + drafted tokens/s, Qwen3-8B-shape B=16; % HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="qwen3_8b")
+    ap.add_argument("--no-graph", action="store_true", help="report eager launches only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--inject", action="store_true", help="also time steady-state inject (B positions)")
+    return ap.parse_args()
+
+
+def step_bytes(cfg, lens):
+    """Algorithmic HBM bytes of one draft step: every weight matrix once, the
+    valid context K/V once, the embedding rows read; activations excluded."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    H, F, nq, nkv, d = cfg.hidden, cfg.ffn, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    layer = (cfg.qkv_rows * H + H * nq * d + 2 * F * H + H * F + 2 * H) * e
+    lm = cfg.vocab * H * e
+    kv = cfg.n_layers * int(sum(lens)) * nkv * d * 2 * e
+    emb = 2 * H * e + H * e
+    return cfg.n_layers * layer, lm, kv, emb
+
+
+def step_flops(cfg, lens):
+    H, F, nq, nkv, d, B = cfg.hidden, cfg.ffn, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_size
+    R = cfg.batch * B
+    gemm = 2 * R * (cfg.qkv_rows * H + H * nq * d + 2 * F * H + H * F) * cfg.n_layers
+    lm = 2 * cfg.batch * (B - 1) * cfg.vocab * H
+    attn = sum(4 * B * nq * d * (int(p) + B) for p in lens) * cfg.n_layers
+    return gemm, lm, attn
+
+
+def cpu_baseline(cfg, w, Kp, Vp, lay, lens, anchors, y):
+    """The float64 oracle on the host cores: one full draft step of sequence 0."""
+    import numpy as np
+    from oracle import drafter as D
+    from oracle.numerics import from_storage
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t = np.arange(int(lens[0]))
+    pages, slots = lay.block_table[0, t // cfg.page_size], t % cfg.page_size
+    Kc, Vc = from_storage(Kp[:, pages, slots]), from_storage(Vp[:, pages, slots])
+    t0 = time.perf_counter()
+    Z = D.draft_block(w, cfg, int(anchors[0]), Kc, Vc)
+    ids, _, _ = D.lm_argmax(w["lm_head"], Z)
+    D.accept_len(ids, y[0])
+    dt = time.perf_counter() - t0
+    return {"value": round((cfg.block_size - 1) / dt, 3), "unit": "drafted tokens/s", "cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"one draft step of sequence 0 ({cfg.block_size - 1} drafted tokens, context {int(lens[0])})"
+                      " in float64 numpy"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the drafter step is measured per GPU",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import dflash_synth as S
+    from block_diffusion_drafter_gemm_amd import _lib as L
+    from block_diffusion_drafter_gemm_amd import runtime as R
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = S.get_config(args.config)
+    b, B = cfg.batch, cfg.block_size
+    w = S.drafter_weights(cfg, seed=0)
+    lens = S.ctx_lens(cfg, seed=0)
+    lay = S.paged_layout(cfg, lens, headroom=B, seed=0)
+    Kp, Vp = S.ctx_kv_cache(cfg, lay, seed=0)
+    anchors = S.anchor_ids(cfg, seed=0)
+    dr = R.Drafter(cfg, w, max_batch=b, max_ctx=int(lens.max()), max_new=B)
+    kv = R.PagedKV(cfg, lay.block_table, lens, lay.n_pages, k=Kp, v=Vp)
+    kvs = kv.struct()
+    st = torch.cuda.current_stream().cuda_stream
+    anc = torch.from_numpy(anchors).cuda()
+    hid = torch.empty((b * (B - 1), cfg.hidden), dtype=R.storage_dtype(cfg), device="cuda")
+    ids = torch.empty(b * (B - 1), dtype=torch.int32, device="cuda")
+    tau = torch.empty(b, dtype=torch.int32, device="cuda")
+    bonus = torch.empty(b, dtype=torch.int32, device="cuda")
+    lib, ws, wsb, h = L.load(), dr.ws, dr.ws_bytes, dr.handle
+    rows = b * (B - 1)
+
+    def draft():
+        assert lib.dflash_draft_block(h, anc.data_ptr(), kvs, hid.data_ptr(), ws.data_ptr(), wsb, st) == 0
+
+    def lmhead():
+        assert lib.dflash_lmhead_argmax(h, hid.data_ptr(), rows, ids.data_ptr(), None, None, ws.data_ptr(), wsb,
+                                        st) == 0
+
+    def accept():
+        assert lib.dflash_accept_len(ids.data_ptr(), y_dev.data_ptr(), b, B, tau.data_ptr(), bonus.data_ptr(),
+                                     st) == 0
+
+    # synthetic target ids (70% agreement) from the first step's drafts
+    draft()
+    lmhead()
+    torch.cuda.synchronize()
+    d0 = ids.cpu().numpy().reshape(b, B - 1)
+    y = S.target_ids_for(cfg, d0, seed=0)
+    y_dev = torch.from_numpy(y).cuda()
+
+    def step():
+        draft()
+        lmhead()
+        accept()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # eager timed region: events on the launch stream bracket the draft pass and the LM head
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(K):
+        ev[i][0].record()
+        draft()
+        ev[i][1].record()
+        lmhead()
+        ev[i][2].record()
+        accept()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / K
+    draft_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
+    lm_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    assert np.array_equal(ids.cpu().numpy().reshape(b, B - 1), d0), "drafts changed between steps"
+
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            step()
+        torch.cuda.current_stream().wait_stream(s2)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            st_cap = torch.cuda.current_stream().cuda_stream
+            st_saved, st = st, st_cap
+            step()
+            st = st_saved
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ids.zero_()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(K):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / K
+        assert np.array_equal(ids.cpu().numpy().reshape(b, B - 1), d0), "graph replay drafts differ from eager"
+
+    ms = graph_ms if graph_ms is not None else eager_ms
+    layers_b, lm_b, kv_b, emb_b = step_bytes(cfg, lens)
+    total_b = layers_b + lm_b + kv_b + emb_b
+    gemm_f, lm_f, attn_f = step_flops(cfg, lens)
+    lm_s = float(np.mean(lm_ms)) / 1e3
+    achieved = lm_b / lm_s / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(b * (B - 1) / (ms / 1e3), 1),
+        "unit": "drafted tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "latency_us": round(ms * 1e3, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,sigma) context K/V, uniform anchor ids)",
+        "config": {"workload": f"{cfg.name} drafter step: batch {b}, context {int(lens.max())}, B={B}, "
+                               f"{cfg.n_layers} layers, hidden {cfg.hidden}, vocab {cfg.vocab}",
+                   "batch": b, "block_size": B, "ctx_len": int(lens.max()),
+                   "launch": "hipgraph" if graph_ms is not None else "eager"},
+        "step": {"eager_ms": round(eager_ms, 4), "graph_ms": None if graph_ms is None else round(graph_ms, 4),
+                 "draft_block_ms": round(float(np.mean(draft_ms)), 4),
+                 "lmhead_ms": round(float(np.mean(lm_ms)), 4),
+                 "algorithmic_bytes": int(total_b), "algorithmic_flops": int(gemm_f + lm_f + attn_f),
+                 "hbm_gbs": round(total_b / (ms / 1e3) / 1e9, 1),
+                 "hbm_frac": round(total_b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {"kernel": "lmhead_argmax (vocabulary GEMM with argmax epilogue + argmax reduce)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(lm_b), "avg_launch_us": round(lm_s * 1e6, 2)},
+    }
+    if args.inject:
+        fe = R.to_device(S.features(cfg, B * b, seed=1))
+        sq = torch.arange(b, dtype=torch.int32, device="cuda").repeat_interleave(B)
+        ps = (torch.from_numpy(lens).cuda().repeat_interleave(B) +
+              torch.arange(B, dtype=torch.int32, device="cuda").repeat(b)).to(torch.int32)
+        for _ in range(3):
+            dr.inject_context(fe, sq, ps, kv)
+        i0, i1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        i0.record()
+        for _ in range(K):
+            dr.inject_context(fe, sq, ps, kv)
+        i1.record()
+        torch.cuda.synchronize()
+        out["inject_steady_ms"] = round(i0.elapsed_time(i1) / K, 4)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, w, Kp, Vp, lay, lens, anchors, y)
+    dr.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

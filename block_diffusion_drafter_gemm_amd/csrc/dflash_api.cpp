@@ -39,16 +39,9 @@ struct Carve {
 
 // ---- draft_block layout --------------------------------------------------
 struct DraftLayout {
-  size_t X, Y, Q, Kb, Vb, O, Hs, part, attn_part, attn_stats, total;
+  size_t X, Y, Q, Kb, Vb, O, Hs, attn_part, attn_stats, total;
   int chunk, max_items;
 };
-
-size_t gemm_partial_floats(const dflash_handle_s *h, int M, int N_groups, int K, int z) {
-  int ks, kps;
-  return gemm_plan(M, N_groups, K, z, h->bf16, &ks, &kps);
-}
-
-int groups_of(int N) { return (N + kColGroup - 1) / kColGroup; }
 
 DraftLayout draft_layout(const dflash_handle_s *h, int batch, int max_ctx) {
   const dflash_config &c = h->cfg;
@@ -63,12 +56,6 @@ DraftLayout draft_layout(const dflash_handle_s *h, int batch, int max_ctx) {
   L.Vb = cv.take((size_t)R * kvd * h->esz);
   L.O = cv.take((size_t)R * qd * h->esz);
   L.Hs = cv.take((size_t)R * c.ffn * h->esz);
-  size_t pf = 0, t;
-  t = gemm_partial_floats(h, R, groups_of(qd + 2 * kvd), c.hidden, 1); pf = t > pf ? t : pf;
-  t = gemm_partial_floats(h, R, groups_of(c.hidden), qd, 1); pf = t > pf ? t : pf;
-  t = gemm_partial_floats(h, R, c.ffn / 64, c.hidden, 1); pf = t > pf ? t : pf;
-  t = gemm_partial_floats(h, R, groups_of(c.hidden), c.ffn, 1); pf = t > pf ? t : pf;
-  L.part = cv.take(pf * 4);
   L.chunk = attn_chunk(batch, max_ctx, B, c.n_kv_heads);
   L.max_items = attn_max_items(batch, max_ctx, B, c.n_kv_heads, L.chunk);
   const int GB = (c.n_q_heads / c.n_kv_heads) * B, GBP = (GB + 15) / 16 * 16;
@@ -79,15 +66,14 @@ DraftLayout draft_layout(const dflash_handle_s *h, int batch, int max_ctx) {
 }
 
 struct LmLayout {
-  size_t part, val, idx, total;
+  size_t val, idx, total;
 };
 
 LmLayout lm_layout(const dflash_handle_s *h, int rows) {
   const dflash_config &c = h->cfg;
   LmLayout L;
   Carve cv;
-  const int ng = groups_of(c.vocab);
-  L.part = cv.take(gemm_partial_floats(h, rows, ng, c.hidden, 1) * 4);
+  const int ng = gemm_tiles(EPI_ARGMAX, c.vocab, c.ffn);
   L.val = cv.take((size_t)rows * ng * 4);
   L.idx = cv.take((size_t)rows * ng * 4);
   L.total = cv.off;
@@ -95,7 +81,7 @@ LmLayout lm_layout(const dflash_handle_s *h, int rows) {
 }
 
 struct InjectLayout {
-  size_t c, part, total;
+  size_t c, total;
 };
 
 InjectLayout inject_layout(const dflash_handle_s *h, int n_new) {
@@ -103,30 +89,16 @@ InjectLayout inject_layout(const dflash_handle_s *h, int n_new) {
   InjectLayout L;
   Carve cv;
   L.c = cv.take((size_t)n_new * c.hidden * h->esz);
-  size_t pf = gemm_partial_floats(h, n_new, groups_of(c.hidden), c.n_feat_layers * c.hidden, 1);
-  size_t t = gemm_partial_floats(h, n_new, groups_of(2 * c.n_kv_heads * c.head_dim), c.hidden, c.n_layers);
-  L.part = cv.take((pf > t ? pf : t) * 4);
   L.total = cv.off;
   return L;
 }
 
-int counters_needed(int M, int n_groups, int z) {
-  const int MP = gemm_rows_per_group(M);
-  return ((M + MP - 1) / MP) * z * n_groups;
-}
-
-bool counters_fit(int M, int n_groups, int z) {
-  return (size_t)counters_needed(M, n_groups, z) * sizeof(int) <= kCounterBytes;
-}
-
-// Fill the GEMM plan fields of ``a`` (row groups, split-K, scratch) and launch.
-int launch(const dflash_handle_s *h, Epilogue epi, GemmArgs &a, int z, char *ws, size_t part_off, hipStream_t st) {
+// Fill the launch geometry of ``a`` (tiles, row groups) and launch.
+int launch(const dflash_handle_s *h, Epilogue epi, GemmArgs &a, int z, hipStream_t st) {
   const int MP = gemm_rows_per_group(a.M);
   a.m_groups = (a.M + MP - 1) / MP;
-  gemm_plan(a.M, a.n_groups, a.K, z, h->bf16, &a.k_split, &a.k_per_split);
-  a.partial = reinterpret_cast<float *>(ws + part_off);
-  a.counters = reinterpret_cast<int *>(ws);
-  if (!counters_fit(a.M, a.n_groups, z)) return DFLASH_ERR_SHAPE;
+  a.n_groups = gemm_tiles(epi, a.N, a.ffn);
+  if ((long)a.m_groups * z > 65535) return DFLASH_ERR_SHAPE;
   return launch_gemm(h->bf16, epi, a, z, st) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
@@ -254,11 +226,9 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
   a.M = n_new;
   a.N = c.hidden;
   a.K = c.n_feat_layers * c.hidden;
-  a.n_groups = groups_of(c.hidden);
   a.out = w + L.c;
   a.ldo = c.hidden;
-  if (!counters_fit(n_new, a.n_groups, 1)) return DFLASH_ERR_SHAPE;
-  if ((st = launch(h, EPI_STORE, a, 1, w, L.part, s)) != DFLASH_OK) return st;
+  if ((st = launch(h, EPI_STORE, a, 1, s)) != DFLASH_OK) return st;
 
   GemmArgs b;
   memset(&b, 0, sizeof(b));
@@ -270,7 +240,6 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
   b.M = n_new;
   b.N = 2 * kvd;
   b.K = c.hidden;
-  b.n_groups = groups_of(2 * kvd);
   b.k_out = kv->k;
   b.v_out = kv->v;
   b.nq = c.n_q_heads;
@@ -283,7 +252,7 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
   b.max_pages = kv->max_pages;
   b.page_size = c.page_size;
   b.cache_layer_stride = (size_t)kv->n_pages * c.page_size * kvd;
-  return launch(h, EPI_INJECT, b, c.n_layers, w, L.part, s);
+  return launch(h, EPI_INJECT, b, c.n_layers, s);
 }
 
 int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_kv *kv, void *hidden_out, void *ws,
@@ -316,7 +285,6 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     q.M = R;
     q.N = qd + 2 * kvd;
     q.K = c.hidden;
-    q.n_groups = groups_of(q.N);
     q.q_out = w + L.Q;
     q.k_out = w + L.Kb;
     q.v_out = w + L.Vb;
@@ -326,7 +294,7 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     q.nkv = c.n_kv_heads;
     q.hd = c.head_dim;
     q.log2_theta = log2((double)c.rope_theta);
-    if ((st = launch(h, EPI_QKV, q, 1, w, L.part, s)) != DFLASH_OK) return st;
+    if ((st = launch(h, EPI_QKV, q, 1, s)) != DFLASH_OK) return st;
 
     AttnArgs at;
     memset(&at, 0, sizeof(at));
@@ -360,10 +328,9 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     o.M = R;
     o.N = c.hidden;
     o.K = qd;
-    o.n_groups = groups_of(c.hidden);
     o.X = X;
     o.ldx = c.hidden;
-    if ((st = launch(h, EPI_RESID, o, 1, w, L.part, s)) != DFLASH_OK) return st;
+    if ((st = launch(h, EPI_RESID, o, 1, s)) != DFLASH_OK) return st;
 
     if (launch_rmsnorm(h->bf16, X, h->mlp_norm[l], c.rms_eps, R, c.hidden, B, false, w + L.Y, s) != hipSuccess)
       return DFLASH_ERR_HIP;
@@ -376,11 +343,10 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     gu.M = R;
     gu.N = 2 * c.ffn;
     gu.K = c.hidden;
-    gu.n_groups = c.ffn / 64;
     gu.ffn = c.ffn;
     gu.out = w + L.Hs;
     gu.ldo = c.ffn;
-    if ((st = launch(h, EPI_SWIGLU, gu, 1, w, L.part, s)) != DFLASH_OK) return st;
+    if ((st = launch(h, EPI_SWIGLU, gu, 1, s)) != DFLASH_OK) return st;
 
     GemmArgs dn;
     memset(&dn, 0, sizeof(dn));
@@ -391,10 +357,9 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     dn.M = R;
     dn.N = c.hidden;
     dn.K = c.ffn;
-    dn.n_groups = groups_of(c.hidden);
     dn.X = X;
     dn.ldx = c.hidden;
-    if ((st = launch(h, EPI_RESID, dn, 1, w, L.part, s)) != DFLASH_OK) return st;
+    if ((st = launch(h, EPI_RESID, dn, 1, s)) != DFLASH_OK) return st;
   }
   if (launch_rmsnorm(h->bf16, X, h->final_norm, c.rms_eps, batch * (B - 1), c.hidden, B, true, hidden_out, s) !=
       hipSuccess)
@@ -422,10 +387,9 @@ int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int3
   a.M = rows;
   a.N = c.vocab;
   a.K = c.hidden;
-  a.n_groups = groups_of(c.vocab);
   a.amax_val = reinterpret_cast<float *>(w + L.val);
   a.amax_idx = reinterpret_cast<int *>(w + L.idx);
-  int st = launch(h, EPI_ARGMAX, a, 1, w, L.part, s);
+  int st = launch(h, EPI_ARGMAX, a, 1, s);
   if (st != DFLASH_OK) return st;
   if (launch_argmax_reduce(a.amax_val, a.amax_idx, rows, a.n_groups, ids_out, max_logit_out, s) != hipSuccess)
     return DFLASH_ERR_HIP;
@@ -433,7 +397,7 @@ int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int3
     GemmArgs b = a;
     b.out = logits_out;
     b.ldo = c.vocab;
-    if ((st = launch(h, EPI_STORE_F32, b, 1, w, L.part, s)) != DFLASH_OK) return st;
+    if ((st = launch(h, EPI_STORE_F32, b, 1, s)) != DFLASH_OK) return st;
   }
   return DFLASH_OK;
 }

@@ -8,7 +8,6 @@
 namespace dflash {
 
 constexpr int kMaxLayers = 16;
-constexpr int kColGroup = 128;   // output columns per GEMM workgroup
 
 enum Epilogue {
   EPI_STORE = 0,      // out[row, col] = acc (storage type)
@@ -26,12 +25,9 @@ struct GemmArgs {
   int lda;
   const void *W[kMaxLayers];  // per z-slice weights [N_phys, K], row stride ldw
   int ldw;
-  int M, N, K;            // N: logical output columns
-  int n_groups;           // ceil(N / 128) (SwiGLU: ffn / 64)
-  int m_groups;           // ceil(M / MP)
-  int k_split, k_per_split;
-  float *partial;         // [z][n_groups][k_split][MP][128]
-  int *counters;          // [z][n_groups]
+  int M, N, K;            // N: output columns (SwiGLU: 2 * ffn)
+  int n_groups;           // 16-column tiles (gemm_tiles)
+  int m_groups;           // ceil(M / rows per group)
   // EPI_STORE / EPI_STORE_F32 / EPI_SWIGLU
   void *out;
   int ldo;
@@ -60,8 +56,8 @@ hipError_t launch_gemm(bool is_bf16, Epilogue epi, const GemmArgs &a, int z_slic
 // Rows per GEMM workgroup for M rows (16, 32 or 64).
 int gemm_rows_per_group(int M);
 
-// Pick k_split / k_per_split for a GEMM; returns partial floats needed.
-size_t gemm_plan(int M, int N_groups, int K, int z_slices, bool is_bf16, int *k_split, int *k_per_split);
+// Number of 16-column tiles (workgroups per row group and slice).
+int gemm_tiles(Epilogue epi, int N, int ffn);
 
 struct AttnArgs {
   const void *q;          // [R, nq*hd]
