@@ -214,8 +214,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
             const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
             reinterpret_cast<Frag<bf16_t> &>(vf).v = make_uint4(lo.x, lo.y, hi.x, hi.y);
           } else {
-            reinterpret_cast<Frag<float> &>(vf).lo = *reinterpret_cast<const float4 *>(vr);
-            reinterpret_cast<Frag<float> &>(vf).hi = *reinterpret_cast<const float4 *>(vr + 16);
+            const float4 lo = *reinterpret_cast<const float4 *>(vr);
+            const float4 hi = *reinterpret_cast<const float4 *>(vr + 16);
+            reinterpret_cast<Frag<float> &>(vf).v = f32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
           }
           o[t][d] = mma(o[t][d], vf, pf);
           if constexpr (sizeof(T) == 2) o[t][d] = mma(o[t][d], vf, pf_lo);
@@ -247,6 +248,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
 }
 
 // One wave per (sequence, KV head, query row): combine the chunk partials.
+// Lanes fetch the chunks' (max, sum) statistics in parallel; the weighted sum
+// of the partial outputs then runs over chunks with the loads of 8 chunks in
+// flight at a time, in chunk order (deterministic).
 template <typename T, int HD>
 __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnArgs a) {
   const int lane = threadIdx.x;
@@ -268,23 +272,40 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnArgs a) {
   // chunks past the launched item range were never computed (ctx_len above the
   // declared maximum); never read beyond the partial buffers
   if ((base + nch) * a.nkv > a.max_items) nch = max(0, a.max_items / a.nkv - base);
+  auto stat = [&](int c, int k) { return a.stats[(((size_t)(base + c) * a.nkv + g) * GBP + r) * 2 + k]; };
+  // global max over chunks, then the normaliser
   float M = -1e30f;
-  for (int c = 0; c < nch; ++c) {
-    const size_t item = (size_t)(base + c) * a.nkv + g;
-    M = fmaxf(M, a.stats[(item * GBP + r) * 2]);
-  }
+  for (int c = lane; c < nch; c += 64) M = fmaxf(M, stat(c, 0));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float lsum = 0.f;
+  for (int c = lane; c < nch; c += 64) lsum += exp2f(stat(c, 0) - M) * stat(c, 1);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
   constexpr int PER = HD / 64;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float lsum = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const size_t item = (size_t)(base + c) * a.nkv + g;
-    const float w = exp2f(a.stats[(item * GBP + r) * 2] - M);
-    lsum += w * a.stats[(item * GBP + r) * 2 + 1];
-    const float *po = a.partial + (item * GBP + r) * HD;
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    // weight of chunk c0 + lane, broadcast below
+    const float wl = c0 + lane < nch ? exp2f(stat(c0 + lane, 0) - M) : 0.f;
+    const int cn = min(64, nch - c0);
+    for (int j0 = 0; j0 < cn; j0 += 8) {
+      float po[8][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += w * po[lane + 64 * e];
+      for (int j = 0; j < 8; ++j) {
+        const int c = c0 + j0 + j;
+        const float *p = a.partial + (((size_t)(base + (c < nch ? c : 0)) * a.nkv + g) * GBP + r) * HD;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) po[j][e] = (j0 + j < cn) ? p[lane + 64 * e] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float w = __shfl(wl, j0 + j);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += w * po[j][e];
+      }
+    }
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   const int hh = r / B, j = r % B;

@@ -19,6 +19,7 @@ struct dflash_handle_s {
   const void *mlp_norm[kMaxLayers], *w_gate_up[kMaxLayers], *w_down[kMaxLayers];
   bool bf16;
   size_t esz;  // bytes per stored element
+  int n_cu;    // compute units of the current device (queried at the first launch)
 };
 
 namespace {
@@ -101,6 +102,30 @@ int launch(const dflash_handle_s *h, Epilogue epi, GemmArgs &a, int z, hipStream
   if ((long)a.m_groups * z > 65535) return DFLASH_ERR_SHAPE;
   return launch_gemm(h->bf16, epi, a, z, st) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
+
+int compute_units(dflash_handle_s *h) {
+  if (h->n_cu <= 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    h->n_cu = n;
+  }
+  return h->n_cu;
+}
+
+// Streaming GEMM (M <= 16): one persistent workgroup per compute unit.
+int launch_stream(dflash_handle_s *h, Epilogue epi, int amode, GemmArgs &a, int z, hipStream_t st,
+                  int *grid_out = nullptr) {
+  a.m_groups = 1;
+  a.n_groups = gemm_tiles(epi, a.N, a.ffn);
+  int grid = compute_units(h);
+  if (grid > a.n_groups) grid = a.n_groups;
+  if (grid_out) *grid_out = grid;
+  return launch_gemm_stream(h->bf16, epi, amode, a, grid, z, st) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+enum { AM_GLOBAL = 0, AM_COPY = 1, AM_NORM = 2, AM_EMBED_NORM = 3 };
 
 int validate_config(const dflash_config *c) {
   if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return DFLASH_ERR_DTYPE;
@@ -216,7 +241,10 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
   char *w = static_cast<char *>(ws);
   hipStream_t s = (hipStream_t)stream;
   const int kvd = c.n_kv_heads * c.head_dim, qd = c.n_q_heads * c.head_dim;
+  const int KR = stream_res_k(h->bf16);
+  const bool small = n_new <= 16;
 
+  // A1: c = feats * W_fc^T
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.A = feats;
@@ -228,8 +256,10 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
   a.K = c.n_feat_layers * c.hidden;
   a.out = w + L.c;
   a.ldo = c.hidden;
-  if ((st = launch(h, EPI_STORE, a, 1, s)) != DFLASH_OK) return st;
+  st = small ? launch_stream(h, EPI_STORE, a.K <= KR ? AM_COPY : AM_GLOBAL, a, 1, s) : launch(h, EPI_STORE, a, 1, s);
+  if (st != DFLASH_OK) return st;
 
+  // A2: every layer's K and V projections of c, RoPE on K, paged write
   GemmArgs b;
   memset(&b, 0, sizeof(b));
   b.A = w + L.c;
@@ -252,7 +282,8 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
   b.max_pages = kv->max_pages;
   b.page_size = c.page_size;
   b.cache_layer_stride = (size_t)kv->n_pages * c.page_size * kvd;
-  return launch(h, EPI_INJECT, b, c.n_layers, s);
+  return small ? launch_stream(h, EPI_INJECT, c.hidden <= KR ? AM_COPY : AM_GLOBAL, b, c.n_layers, s)
+               : launch(h, EPI_INJECT, b, c.n_layers, s);
 }
 
 int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_kv *kv, void *hidden_out, void *ws,
@@ -270,16 +301,17 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
   const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
   float *X = reinterpret_cast<float *>(w + L.X);
   const size_t cache_layer = (size_t)kv->n_pages * c.page_size * kvd * h->esz;
+  const int KR = stream_res_k(h->bf16);
+  // streaming path: up to 16 block rows, hidden states resident in LDS (norms fused)
+  const bool fast = R <= 16 && c.hidden <= KR && qd <= KR;
 
-  if (launch_embed(h->bf16, h->embed, anchor_ids, c.mask_token_id, batch, B, c.hidden, X, s) != hipSuccess)
+  if (!fast &&
+      launch_embed(h->bf16, h->embed, anchor_ids, c.mask_token_id, batch, B, c.hidden, X, s) != hipSuccess)
     return DFLASH_ERR_HIP;
   for (int l = 0; l < c.n_layers; ++l) {
-    if (launch_rmsnorm(h->bf16, X, h->attn_norm[l], c.rms_eps, R, c.hidden, B, false, w + L.Y, s) != hipSuccess)
-      return DFLASH_ERR_HIP;
+    // A4: RMSNorm, QKV projection, RoPE; block q/k/v to the workspace
     GemmArgs q;
     memset(&q, 0, sizeof(q));
-    q.A = w + L.Y;
-    q.lda = c.hidden;
     q.W[0] = h->w_qkv[l];
     q.ldw = c.hidden;
     q.M = R;
@@ -294,8 +326,25 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     q.nkv = c.n_kv_heads;
     q.hd = c.head_dim;
     q.log2_theta = log2((double)c.rope_theta);
-    if ((st = launch(h, EPI_QKV, q, 1, s)) != DFLASH_OK) return st;
+    if (fast) {
+      q.X = X;
+      q.ldx = c.hidden;
+      q.gain = h->attn_norm[l];
+      q.eps = c.rms_eps;
+      q.embed = h->embed;
+      q.anchor = anchor_ids;
+      q.mask_id = c.mask_token_id;
+      st = launch_stream(h, EPI_QKV, l == 0 ? AM_EMBED_NORM : AM_NORM, q, 1, s);
+    } else {
+      if (launch_rmsnorm(h->bf16, X, h->attn_norm[l], c.rms_eps, R, c.hidden, B, false, w + L.Y, s) != hipSuccess)
+        return DFLASH_ERR_HIP;
+      q.A = w + L.Y;
+      q.lda = c.hidden;
+      st = launch(h, EPI_QKV, q, 1, s);
+    }
+    if (st != DFLASH_OK) return st;
 
+    // A5: attention over the paged context plus the block, no mask
     AttnArgs at;
     memset(&at, 0, sizeof(at));
     at.q = w + L.Q;
@@ -319,6 +368,7 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     at.max_items = L.max_items;
     if (launch_attention(h->bf16, at, s) != hipSuccess) return DFLASH_ERR_HIP;
 
+    // A6: O projection + residual
     GemmArgs o;
     memset(&o, 0, sizeof(o));
     o.A = w + L.O;
@@ -330,14 +380,12 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     o.K = qd;
     o.X = X;
     o.ldx = c.hidden;
-    if ((st = launch(h, EPI_RESID, o, 1, s)) != DFLASH_OK) return st;
+    st = fast ? launch_stream(h, EPI_RESID, AM_COPY, o, 1, s) : launch(h, EPI_RESID, o, 1, s);
+    if (st != DFLASH_OK) return st;
 
-    if (launch_rmsnorm(h->bf16, X, h->mlp_norm[l], c.rms_eps, R, c.hidden, B, false, w + L.Y, s) != hipSuccess)
-      return DFLASH_ERR_HIP;
+    // A7: RMSNorm, gate/up + SwiGLU, down + residual
     GemmArgs gu;
     memset(&gu, 0, sizeof(gu));
-    gu.A = w + L.Y;
-    gu.lda = c.hidden;
     gu.W[0] = h->w_gate_up[l];
     gu.ldw = c.hidden;
     gu.M = R;
@@ -346,7 +394,20 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     gu.ffn = c.ffn;
     gu.out = w + L.Hs;
     gu.ldo = c.ffn;
-    if ((st = launch(h, EPI_SWIGLU, gu, 1, s)) != DFLASH_OK) return st;
+    if (fast) {
+      gu.X = X;
+      gu.ldx = c.hidden;
+      gu.gain = h->mlp_norm[l];
+      gu.eps = c.rms_eps;
+      st = launch_stream(h, EPI_SWIGLU, AM_NORM, gu, 1, s);
+    } else {
+      if (launch_rmsnorm(h->bf16, X, h->mlp_norm[l], c.rms_eps, R, c.hidden, B, false, w + L.Y, s) != hipSuccess)
+        return DFLASH_ERR_HIP;
+      gu.A = w + L.Y;
+      gu.lda = c.hidden;
+      st = launch(h, EPI_SWIGLU, gu, 1, s);
+    }
+    if (st != DFLASH_OK) return st;
 
     GemmArgs dn;
     memset(&dn, 0, sizeof(dn));
@@ -359,8 +420,11 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     dn.K = c.ffn;
     dn.X = X;
     dn.ldx = c.hidden;
-    if ((st = launch(h, EPI_RESID, dn, 1, s)) != DFLASH_OK) return st;
+    st = fast ? launch_stream(h, EPI_RESID, c.ffn <= KR ? AM_COPY : AM_GLOBAL, dn, 1, s)
+              : launch(h, EPI_RESID, dn, 1, s);
+    if (st != DFLASH_OK) return st;
   }
+  // A8: final RMSNorm of the mask rows
   if (launch_rmsnorm(h->bf16, X, h->final_norm, c.rms_eps, batch * (B - 1), c.hidden, B, true, hidden_out, s) !=
       hipSuccess)
     return DFLASH_ERR_HIP;
@@ -378,6 +442,8 @@ int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int3
   if (ws_bytes < L.total) return DFLASH_ERR_WORKSPACE;
   char *w = static_cast<char *>(ws);
   hipStream_t s = (hipStream_t)stream;
+  const bool small = rows <= 16;
+  const int KR = stream_res_k(h->bf16);
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.A = hidden;
@@ -389,15 +455,19 @@ int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int3
   a.K = c.hidden;
   a.amax_val = reinterpret_cast<float *>(w + L.val);
   a.amax_idx = reinterpret_cast<int *>(w + L.idx);
-  int st = launch(h, EPI_ARGMAX, a, 1, s);
+  const int am = c.hidden <= KR ? AM_COPY : AM_GLOBAL;
+  int parts = 0;
+  int st = small ? launch_stream(h, EPI_ARGMAX, am, a, 1, s, &parts) : launch(h, EPI_ARGMAX, a, 1, s);
   if (st != DFLASH_OK) return st;
-  if (launch_argmax_reduce(a.amax_val, a.amax_idx, rows, a.n_groups, ids_out, max_logit_out, s) != hipSuccess)
+  if (!small) parts = a.n_groups;
+  if (launch_argmax_reduce(a.amax_val, a.amax_idx, rows, parts, ids_out, max_logit_out, s) != hipSuccess)
     return DFLASH_ERR_HIP;
   if (logits_out) {
     GemmArgs b = a;
     b.out = logits_out;
     b.ldo = c.vocab;
-    if ((st = launch(h, EPI_STORE_F32, b, 1, s)) != DFLASH_OK) return st;
+    st = small ? launch_stream(h, EPI_STORE_F32, am, b, 1, s) : launch(h, EPI_STORE_F32, b, 1, s);
+    if (st != DFLASH_OK) return st;
   }
   return DFLASH_OK;
 }

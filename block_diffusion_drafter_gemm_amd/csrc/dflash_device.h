@@ -79,30 +79,14 @@ template <> struct Frag<bf16_t> {
   }
 };
 
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 template <> struct Frag<float> {
-  float4 lo, hi;  // 8 fp32
-  __device__ __forceinline__ void zero() {
-    lo = make_float4(0.f, 0.f, 0.f, 0.f);
-    hi = lo;
-  }
-  __device__ __forceinline__ void load(const float *p) {
-    lo = *reinterpret_cast<const float4 *>(p);
-    hi = *reinterpret_cast<const float4 *>(p + 4);
-  }
-  __device__ __forceinline__ void store(float *p) const {
-    *reinterpret_cast<float4 *>(p) = lo;
-    *reinterpret_cast<float4 *>(p + 4) = hi;
-  }
-  __device__ __forceinline__ float get(int e) const {
-    switch (e) {
-      case 0: return lo.x; case 1: return lo.y; case 2: return lo.z; case 3: return lo.w;
-      case 4: return hi.x; case 5: return hi.y; case 6: return hi.z; default: return hi.w;
-    }
-  }
-  __device__ __forceinline__ void set(const float *f) {
-    lo = make_float4(f[0], f[1], f[2], f[3]);
-    hi = make_float4(f[4], f[5], f[6], f[7]);
-  }
+  f32x8 v;
+  __device__ __forceinline__ void zero() { v = f32x8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ void load(const float *p) { v = *reinterpret_cast<const f32x8 *>(p); }
+  __device__ __forceinline__ void store(float *p) const { *reinterpret_cast<f32x8 *>(p) = v; }
+  __device__ __forceinline__ float get(int e) const { return v[e]; }
+  __device__ __forceinline__ void set(const float *f) { v = f32x8{f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]}; }
 };
 
 // acc += A_chunk * B_chunk for one 16 x 16 tile and one 32-wide k-chunk.
@@ -111,14 +95,8 @@ __device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<bf16_t> &a, const Fra
                                                  acc, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<float> &a, const Frag<float> &b) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
   return acc;
 }
 
@@ -126,35 +104,17 @@ __device__ __forceinline__ float f4get(const f32x4 &v, int i) {
   return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
 }
 
-// ---------------------------------------------------------------------------
-// cross-workgroup completion counters (agent scope)
-// ---------------------------------------------------------------------------
-// Called by all threads of a workgroup after its partial results are stored.
-// Returns true in every thread of the workgroup that arrives last; that
-// workgroup then sees every other workgroup's stores and resets the counter.
-__device__ __forceinline__ bool arrive_last(int *counter, int expected, int *lds_flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    int last = (prev == expected - 1);
-    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *lds_flag = last;
-  }
-  __syncthreads();
-  bool last = *lds_flag != 0;
-  if (last) __threadfence();
-  return last;
+// RoPE angle pos * inv_freq with inv_freq = theta^(-2i/d): the product and its
+// reduction to [-pi, pi] in double, then fp32 sincos of the reduced angle.
+__device__ __forceinline__ void rope_cs_inv(int pos, double inv_freq, float *c, float *s) {
+  const double a = static_cast<double>(pos) * inv_freq;
+  const double k = rint(a * 0.15915494309189535);              // a / (2 pi)
+  const float r = static_cast<float>(fma(-k, 6.283185307179586, a));
+  sincosf(r, s, c);
 }
 
-// RoPE angle pos * theta^(-2i/d), evaluated in double, returned as (cos, sin).
-__device__ __forceinline__ void rope_cs(int pos, int i, int d, double log2_theta, float *c, float *s) {
-  double inv = exp2(-2.0 * static_cast<double>(i) / static_cast<double>(d) * log2_theta);
-  double a = static_cast<double>(pos) * inv;
-  double sn, cs;
-  sincos(a, &sn, &cs);
-  *c = static_cast<float>(cs);
-  *s = static_cast<float>(sn);
+__device__ __forceinline__ double rope_inv_freq(int i, int d, double log2_theta) {
+  return exp2(-2.0 * static_cast<double>(i) / static_cast<double>(d) * log2_theta);
 }
 
 }  // namespace dflash

@@ -47,6 +47,12 @@ struct GemmArgs {
   // EPI_ARGMAX
   float *amax_val;
   int *amax_idx;
+  // fused activation staging (streaming GEMM): RMSNorm gain/eps, embedding gather
+  const void *gain;
+  float eps;
+  const void *embed;
+  const int *anchor;
+  int mask_id;
 };
 
 // Launch a skinny GEMM; ``z_slices`` = number of weight slices (layers) in the
@@ -58,6 +64,14 @@ int gemm_rows_per_group(int M);
 
 // Number of 16-column tiles (workgroups per row group and slice).
 int gemm_tiles(Epilogue epi, int N, int ffn);
+
+// Streaming GEMM for M <= 16 rows (persistent, one workgroup per compute unit).
+// amode: 0 = activations read from global memory, 1 = copied into LDS,
+// 2 = RMSNorm of the fp32 residual X into LDS, 3 = embedding gather + RMSNorm.
+hipError_t launch_gemm_stream(bool is_bf16, Epilogue epi, int amode, const GemmArgs &a, int grid_x, int z_slices,
+                              hipStream_t st);
+// Largest K whose 16 activation rows stay resident in LDS.
+int stream_res_k(bool is_bf16);
 
 struct AttnArgs {
   const void *q;          // [R, nq*hd]

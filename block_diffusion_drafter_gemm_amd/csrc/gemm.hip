@@ -87,7 +87,7 @@ __device__ void gemm_epilogue(const GemmArgs &a, const float *ct, int MP, int ro
       float lo = x1, hi = x2;
       if (n < qcols + kcols) {
         float cs, sn;
-        rope_cs(pos, j0 + c, hd, a.log2_theta, &cs, &sn);
+        rope_cs_inv(pos, rope_inv_freq(j0 + c, hd, a.log2_theta), &cs, &sn);
         lo = x1 * cs - x2 * sn;
         hi = x2 * cs + x1 * sn;
       }
