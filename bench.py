@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="report eager launches only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--inject", action="store_true", help="also time steady-state inject (B positions)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -56,6 +58,29 @@ def step_flops(cfg, lens):
     lm = 2 * cfg.batch * (B - 1) * cfg.vocab * H
     attn = sum(4 * B * nq * d * (int(p) + B) for p in lens) * cfg.n_layers
     return gemm, lm, attn
+
+
+PROFILE = os.path.join(ROOT, "profiles", "lmhead_argmax_qwen3_8b_b1.md")
+KERNEL_SOURCES = ["block_diffusion_drafter_gemm_amd/csrc/gemm_stream.hip",
+                  "block_diffusion_drafter_gemm_amd/csrc/dflash_device.h"]
+
+
+def recorded_traffic():
+    """HBM bytes per LM-head launch from the committed counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(PROFILE).read()
+        h = hashlib.sha256()
+        for s in KERNEL_SOURCES:
+            h.update(open(os.path.join(ROOT, s), "rb").read())
+        sha = re.search(r"kernel_source_sha256_16: (\w+)", text).group(1)
+        if sha != h.hexdigest()[:16]:
+            return None
+        return int(re.search(r"traffic_bytes_per_launch: (\d+)", text).group(1))
+    except (OSError, AttributeError):
+        return None
 
 
 def cpu_baseline(cfg, w, Kp, Vp, lay, lens, anchors, y):
@@ -96,6 +121,14 @@ def main():
     from block_diffusion_drafter_gemm_amd import runtime as R
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}), flush=True)
+        return
     cfg = S.get_config(args.config)
     b, B = cfg.batch, cfg.block_size
     w = S.drafter_weights(cfg, seed=0)
@@ -222,7 +255,8 @@ def main():
                  "hbm_frac": round(total_b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": {"kernel": "lmhead_argmax (vocabulary GEMM with argmax epilogue + argmax reduce)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic() if args.config == "qwen3_8b" else None,
                      "bytes_per_launch": int(lm_b), "avg_launch_us": round(lm_s * 1e6, 2)},
     }
     if args.inject:
