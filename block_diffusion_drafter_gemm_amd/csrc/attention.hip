@@ -78,6 +78,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
   __shared__ __align__(16) T k_lds[kSub * KSTR];
   __shared__ __align__(16) T vt_lds[HD * VSTR];
   __shared__ int s_seq, s_first;
+  __shared__ int s_pages[1024 / 16 + 1];          // page ids of this item's context keys
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, ln = lane & 15;
   const int item = blockIdx.x;
@@ -126,32 +127,94 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
     for (int d = 0; d < ND; ++d) o[t][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int sub = kbeg; sub < kend; sub += kSub) {
-    __syncthreads();
-    for (int i = tid; i < kSub * VPK; i += 256) {
-      const int kk = i / VPK, vv = i - kk * VPK;
-      const int t = sub + kk;
-      uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-      if (t < kend) {
-        size_t off;
-        const T *kp, *vp;
-        if (t < ctx) {
-          const int page = a.block_table[(size_t)s * a.max_pages + t / a.page_size];
-          off = (((size_t)page * a.page_size + t % a.page_size) * a.nkv + g) * HD;
-          kp = Kc; vp = Vc;
-        } else {
-          off = ((size_t)(s * B + (t - ctx)) * a.nkv + g) * HD;
-          kp = Kb; vp = Vb;
-        }
-        kx = *reinterpret_cast<const uint4 *>(kp + off + vv * EPV);
-        vx = *reinterpret_cast<const uint4 *>(vp + off + vv * EPV);
-      }
-      *reinterpret_cast<uint4 *>(k_lds + kk * KSTR + vv * EPV) = kx;
-      const T *ve = reinterpret_cast<const T *>(&vx);
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) vt_lds[(vv * EPV + e) * VSTR + kk] = ve[e];
+  // Sub-block staging.  bf16: threads 0..127 each carry 8 16-byte chunks of K
+  // (straight rows); threads 128..255 each carry an 8-key x 8-dim block of V,
+  // transposed in registers and written as 8 rows of V^T.  The next sub-block's
+  // chunks are loaded while the current one is processed.  fp32 (small head
+  // dims only) stages element by element.
+  uint4 pre[8];
+  // page ids of the item's context keys, read once (a dependent global load per
+  // key would serialise every in-flight K/V load behind it)
+  const int p0 = kbeg / a.page_size;
+  for (int i = tid; i <= (min(kend, ctx) - 1) / a.page_size - p0 && kbeg < ctx; i += 256)
+    s_pages[i] = a.block_table[(size_t)s * a.max_pages + p0 + i];
+  __syncthreads();
+  auto key_ptr = [&](int t, const T *ctxp, const T *blkp) -> const T * {
+    if (t < ctx) {
+      const int page = s_pages[t / a.page_size - p0];
+      return ctxp + (((size_t)page * a.page_size + t % a.page_size) * a.nkv + g) * HD;
     }
-    __syncthreads();
+    return blkp + ((size_t)(s * B + (t - ctx)) * a.nkv + g) * HD;
+  };
+  auto load_sub = [&](int sub) {
+    if constexpr (sizeof(T) == 2) {
+      if (tid < 128) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = tid + 128 * j, kk = i / VPK, vv = i % VPK, t = sub + kk;
+          pre[j] = (i < kSub * VPK && t < kend) ? *reinterpret_cast<const uint4 *>(key_ptr(t, Kc, Kb) + vv * EPV)
+                                                 : make_uint4(0, 0, 0, 0);
+        }
+      } else {
+        const int u = tid - 128, kg = u / (HD / 8), dg = u % (HD / 8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = sub + kg * 8 + j;
+          pre[j] = (kg * 8 < kSub && t < kend) ? *reinterpret_cast<const uint4 *>(key_ptr(t, Vc, Vb) + dg * 8)
+                                                : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  };
+  auto store_sub = [&](int sub) {
+    if constexpr (sizeof(T) == 2) {
+      if (tid < 128) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = tid + 128 * j, kk = i / VPK, vv = i % VPK;
+          if (i < kSub * VPK) *reinterpret_cast<uint4 *>(k_lds + kk * KSTR + vv * EPV) = pre[j];
+        }
+      } else {
+        const int u = tid - 128, kg = u / (HD / 8), dg = u % (HD / 8);
+        if (kg * 8 < kSub) {
+          // pre[j] holds dims dg*8..+7 of key kg*8+j; row e of V^T gets key j's dim e
+          const uint32_t *w = reinterpret_cast<const uint32_t *>(pre);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            uint32_t o[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const uint32_t lo = (w[(2 * m) * 4 + e / 2] >> (16 * (e & 1))) & 0xffffu;
+              const uint32_t hi = (w[(2 * m + 1) * 4 + e / 2] >> (16 * (e & 1))) & 0xffffu;
+              o[m] = lo | (hi << 16);
+            }
+            *reinterpret_cast<uint4 *>(vt_lds + (dg * 8 + e) * VSTR + kg * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+          }
+        }
+      }
+    } else {
+      for (int i = tid; i < kSub * VPK; i += 256) {
+        const int kk = i / VPK, vv = i - kk * VPK;
+        const int t = sub + kk;
+        uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+        if (t < kend) {
+          kx = *reinterpret_cast<const uint4 *>(key_ptr(t, Kc, Kb) + vv * EPV);
+          vx = *reinterpret_cast<const uint4 *>(key_ptr(t, Vc, Vb) + vv * EPV);
+        }
+        *reinterpret_cast<uint4 *>(k_lds + kk * KSTR + vv * EPV) = kx;
+        const T *ve = reinterpret_cast<const T *>(&vx);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) vt_lds[(vv * EPV + e) * VSTR + kk] = ve[e];
+      }
+    }
+  };
+
+  load_sub(kbeg);
+  for (int sub = kbeg; sub < kend; sub += kSub) {
+    lds_barrier();
+    store_sub(sub);
+    if (sub + kSub < kend) load_sub(sub + kSub);
+    lds_barrier();
 #pragma unroll
     for (int kb2 = 0; kb2 < kSub; kb2 += 32) {
       if (sub + kb2 >= kend) break;

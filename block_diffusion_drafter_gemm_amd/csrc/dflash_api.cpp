@@ -94,8 +94,14 @@ InjectLayout inject_layout(const dflash_handle_s *h, int n_new) {
   return L;
 }
 
-// Fill the launch geometry of ``a`` (tiles, row groups) and launch.
+// Fill the launch geometry of ``a`` and launch: the LDS-tiled kernel for many
+// rows (bf16), otherwise the few-rows kernel.
 int launch(const dflash_handle_s *h, Epilogue epi, GemmArgs &a, int z, hipStream_t st) {
+  if (h->bf16 && a.M > 64 && gemm_tiled_ok(epi, a.N, a.K, a.ffn, a.hd)) {
+    a.m_groups = 1;
+    a.n_groups = gemm_tiled_cols(epi, a.N, a.ffn);
+    return launch_gemm_tiled(epi, a, z, st) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+  }
   const int MP = gemm_rows_per_group(a.M);
   a.m_groups = (a.M + MP - 1) / MP;
   a.n_groups = gemm_tiles(epi, a.N, a.ffn);

@@ -104,6 +104,16 @@ __device__ __forceinline__ float f4get(const f32x4 &v, int i) {
   return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
 }
 
+// Workgroup barrier ordering LDS accesses only.  Global loads and stores in
+// flight stay in flight (a full __syncthreads would drain them when the wave
+// has stored to global memory), so prefetched weights survive the barrier.
+// Only for barriers that protect LDS data.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // RoPE angle pos * inv_freq with inv_freq = theta^(-2i/d): the product and its
 // reduction to [-pi, pi] in double, then fp32 sincos of the reduced angle.
 __device__ __forceinline__ void rope_cs_inv(int pos, double inv_freq, float *c, float *s) {

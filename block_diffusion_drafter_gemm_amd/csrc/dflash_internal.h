@@ -73,6 +73,11 @@ hipError_t launch_gemm_stream(bool is_bf16, Epilogue epi, int amode, const GemmA
 // Largest K whose 16 activation rows stay resident in LDS.
 int stream_res_k(bool is_bf16);
 
+// LDS-tiled GEMM for many rows (bf16, 128 x 128 x 64 tiles).
+bool gemm_tiled_ok(Epilogue epi, int N, int K, int ffn, int hd);
+int gemm_tiled_cols(Epilogue epi, int N, int ffn);
+hipError_t launch_gemm_tiled(Epilogue epi, const GemmArgs &a, int z_slices, hipStream_t st);
+
 struct AttnArgs {
   const void *q;          // [R, nq*hd]
   const void *kb, *vb;    // [R, nkv*hd] block keys / values

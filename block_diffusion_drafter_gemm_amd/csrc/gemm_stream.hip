@@ -177,14 +177,14 @@ __device__ __forceinline__ void s_finish_tile(const GemmArgs &a, f32x4 &acc, flo
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][(4 * g + i) * 16 + ln] = f4get(acc, i);
   acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();
+  lds_barrier();
   if (tid < 256) {
     float sm = 0.f;
 #pragma unroll
     for (int w = 0; w < kSWaves; ++w) sm += red[w][tid];
     ct[tid] = sm;
   }
-  __syncthreads();
+  lds_barrier();
   s_epilogue<T, EPI>(a, ct, t, layer, best_v, best_i, inv_freq);
 }
 

@@ -41,6 +41,10 @@ MINI = {
     "mini_f32": mini("mini_f32", 104, dtype="f32", hidden=256, n_q_heads=8, n_kv_heads=2, head_dim=128,
                      ffn=256, vocab=528, n_layers=2, n_feat_layers=2, block_size=8, batch=2,
                      ctx_min=17, ctx_max=150, rope_theta=1e6),
+    # batch 8 x B 16 = 128 block rows: the many-rows (LDS-tiled) GEMM path
+    "mini_b8": mini("mini_b8", 105, dtype="bf16", hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                    ffn=1088, vocab=4096, n_layers=2, n_feat_layers=3, block_size=16, batch=8,
+                    ctx_min=3, ctx_max=400, rope_theta=1e6),
     "tiny": S.get_config("tiny"),
 }
 

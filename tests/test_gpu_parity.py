@@ -61,8 +61,8 @@ def test_accept_len(B):
 # ----------------------------------------------------------------------------
 # A9 LM head + argmax
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["tiny", "mini_bf16", "mini_f32", "mini_b10"])
-@pytest.mark.parametrize("rows", [1, 15, 33, 70])
+@pytest.mark.parametrize("name,rows", [(n, r) for n in ["tiny", "mini_bf16", "mini_f32", "mini_b10"]
+                                       for r in [1, 15, 33, 70]] + [("mini_b8", r) for r in [65, 130, 300]])
 def test_lmhead_argmax(name, rows):
     cfg = MINI[name]
     log(f"lmhead_argmax {name} rows={rows}")
@@ -91,8 +91,8 @@ def test_lmhead_argmax(name, rows):
 # ----------------------------------------------------------------------------
 # A1 + A2 inject
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["tiny", "mini_bf16", "mini_d64", "mini_f32"])
-@pytest.mark.parametrize("n_new", [1, 16, 90])
+@pytest.mark.parametrize("name,n_new", [(n, k) for n in ["tiny", "mini_bf16", "mini_d64", "mini_f32"]
+                                        for k in [1, 16, 90]] + [("mini_bf16", 200), ("mini_d64", 300)])
 def test_inject_context(name, n_new):
     cfg = MINI[name]
     log(f"inject {name} n_new={n_new}")
@@ -161,7 +161,7 @@ def run_draft_case(cfg, seed=0, lens=None, check_seqs=None):
     return hid_h, ids_h
 
 
-@pytest.mark.parametrize("name", ["tiny", "mini_bf16", "mini_b10", "mini_d64", "mini_f32"])
+@pytest.mark.parametrize("name", ["tiny", "mini_bf16", "mini_b10", "mini_d64", "mini_f32", "mini_b8"])
 def test_draft_block(name):
     log(f"draft_block {name}")
     run_draft_case(MINI[name], seed=0)
