@@ -120,18 +120,18 @@ int compute_units(dflash_handle_s *h) {
   return h->n_cu;
 }
 
+enum { AM_GLOBAL = 0, AM_COPY = 1, AM_NORM = 2, AM_EMBED_NORM = 3, AM_PORTION = 4 };
+
 // Streaming GEMM (M <= 16): one persistent workgroup per compute unit.
 int launch_stream(dflash_handle_s *h, Epilogue epi, int amode, GemmArgs &a, int z, hipStream_t st,
                   int *grid_out = nullptr) {
   a.m_groups = 1;
   a.n_groups = gemm_tiles(epi, a.N, a.ffn);
   int grid = compute_units(h);
-  if (grid > a.n_groups) grid = a.n_groups;
+  if (grid > a.n_groups || amode == AM_PORTION) grid = a.n_groups;   // portions: one tile per workgroup
   if (grid_out) *grid_out = grid;
   return launch_gemm_stream(h->bf16, epi, amode, a, grid, z, st) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
-
-enum { AM_GLOBAL = 0, AM_COPY = 1, AM_NORM = 2, AM_EMBED_NORM = 3 };
 
 int validate_config(const dflash_config *c) {
   if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return DFLASH_ERR_DTYPE;
@@ -262,7 +262,7 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
   a.K = c.n_feat_layers * c.hidden;
   a.out = w + L.c;
   a.ldo = c.hidden;
-  st = small ? launch_stream(h, EPI_STORE, a.K <= KR ? AM_COPY : AM_GLOBAL, a, 1, s) : launch(h, EPI_STORE, a, 1, s);
+  st = small ? launch_stream(h, EPI_STORE, a.K <= KR ? AM_COPY : AM_PORTION, a, 1, s) : launch(h, EPI_STORE, a, 1, s);
   if (st != DFLASH_OK) return st;
 
   // A2: every layer's K and V projections of c, RoPE on K, paged write
@@ -426,7 +426,7 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     dn.K = c.ffn;
     dn.X = X;
     dn.ldx = c.hidden;
-    st = fast ? launch_stream(h, EPI_RESID, c.ffn <= KR ? AM_COPY : AM_GLOBAL, dn, 1, s)
+    st = fast ? launch_stream(h, EPI_RESID, c.ffn <= KR ? AM_COPY : AM_PORTION, dn, 1, s)
               : launch(h, EPI_RESID, dn, 1, s);
     if (st != DFLASH_OK) return st;
   }

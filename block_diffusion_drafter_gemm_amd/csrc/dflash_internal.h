@@ -67,7 +67,8 @@ int gemm_tiles(Epilogue epi, int N, int ffn);
 
 // Streaming GEMM for M <= 16 rows (persistent, one workgroup per compute unit).
 // amode: 0 = activations read from global memory, 1 = copied into LDS,
-// 2 = RMSNorm of the fp32 residual X into LDS, 3 = embedding gather + RMSNorm.
+// 2 = RMSNorm of the fp32 residual X into LDS, 3 = embedding gather + RMSNorm,
+// 4 = copied into LDS one K-portion at a time (one tile per workgroup).
 hipError_t launch_gemm_stream(bool is_bf16, Epilogue epi, int amode, const GemmArgs &a, int grid_x, int z_slices,
                               hipStream_t st);
 // Largest K whose 16 activation rows stay resident in LDS.

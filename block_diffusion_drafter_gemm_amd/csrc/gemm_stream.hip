@@ -319,6 +319,126 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   }
 }
 
+// K longer than the resident capacity: one 16-column tile per workgroup, the
+// activation rows staged into LDS one K-portion at a time (each wave takes an
+// even share of the portion's k-chunks); the weight fragments of the next
+// batch are in flight across portion boundaries, the accumulator stays in
+// registers until the whole K is done.
+template <typename T, int EPI>
+__global__ __launch_bounds__(kSThreads) void gemm_portion_kernel(const GemmArgs a) {
+  constexpr int KR = stream_res_k<T>();
+  constexpr int ASTR = KR * (int)sizeof(T) + 16;
+  constexpr int U = 8 / (int)(sizeof(T) / 2);
+  constexpr int EPV = 16 / (int)sizeof(T);
+  __shared__ __align__(16) unsigned char a_lds[16 * ASTR];
+  __shared__ float red[kSWaves][256];
+  __shared__ float ct[256];
+  __shared__ double inv_freq[64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, ln = lane & 15;
+  const int layer = blockIdx.y, t = blockIdx.x;
+  if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
+    if (tid < a.hd / 2) inv_freq[tid] = rope_inv_freq(tid, a.hd, a.log2_theta);
+  }
+  const T *W = (const T *)a.W[layer];
+  const T *A = (const T *)a.A;
+  const int np = (a.K + KR - 1) / KR;               // portions
+  const int CPP = KR / 32;                          // chunks per full portion
+  const int CPW = (CPP + kSWaves - 1) / kSWaves;    // chunks per wave per portion
+  const int nb = (CPW + U - 1) / U;                 // batches per wave per portion
+  const int total = np * nb;
+  const T *wrow = W + (size_t)s_weight_row<EPI>(a, t, ln) * a.ldw + 8 * g;
+  const T *arow = reinterpret_cast<const T *>(a_lds + ln * ASTR) + 8 * g;
+  // chunk range of unit q (portion q / nb, batch q % nb), in absolute chunks
+  auto range = [&](int q, int *c0, int *c1) {
+    const int p = q / nb, b = q % nb;
+    const int pc = min(CPP, a.K / 32 - p * CPP);    // chunks in this portion
+    const int wb = min(pc, wave * CPW), we = min(pc, wb + CPW);
+    *c0 = p * CPP + min(we, wb + b * U);
+    *c1 = p * CPP + min(we, wb + b * U + U);
+  };
+  auto stage = [&](int p) {                         // wave w copies row w of portion p
+    const int r = wave;
+    T *dst = reinterpret_cast<T *>(a_lds + r * ASTR);
+    const int kk = min(KR, a.K - p * KR);
+    for (int i = lane; i < kk / EPV; i += 64)
+      *reinterpret_cast<uint4 *>(dst + i * EPV) =
+          r < a.M ? *reinterpret_cast<const uint4 *>(A + (size_t)r * a.lda + p * KR + i * EPV) : make_uint4(0, 0, 0, 0);
+  };
+  Frag<T> wa[U], wb[U];
+  int c0, c1;
+  range(0, &c0, &c1);
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    if (c0 + j < c1) wa[j].load(wrow + 32 * (c0 + j)); else wa[j].zero();
+  }
+  stage(0);
+  __syncthreads();
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < total; q += 2) {
+    // --- unit q from wa, prefetch q + 1 into wb
+    int n0, n1;
+    if (q + 1 < total) {
+      range(q + 1, &n0, &n1);
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        if (n0 + j < n1) wb[j].load(wrow + 32 * (n0 + j)); else wb[j].zero();
+      }
+    }
+    range(q, &c0, &c1);
+    {
+      const int pbase = (q / nb) * CPP;
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        if (c0 + j < c1) {
+          Frag<T> af;
+          af.load(arow + 32 * (c0 + j - pbase));
+          acc = mma(acc, af, wa[j]);
+        }
+      }
+    }
+    if (q + 1 < total && (q + 1) % nb == 0) {       // next unit starts a new portion
+      lds_barrier();
+      stage((q + 1) / nb);
+      lds_barrier();
+    }
+    if (q + 1 >= total) break;
+    // --- unit q + 1 from wb, prefetch q + 2 into wa
+    if (q + 2 < total) {
+      range(q + 2, &n0, &n1);
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        if (n0 + j < n1) wa[j].load(wrow + 32 * (n0 + j)); else wa[j].zero();
+      }
+    }
+    range(q + 1, &c0, &c1);
+    {
+      const int pbase = ((q + 1) / nb) * CPP;
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        if (c0 + j < c1) {
+          Frag<T> af;
+          af.load(arow + 32 * (c0 + j - pbase));
+          acc = mma(acc, af, wb[j]);
+        }
+      }
+    }
+    if (q + 2 < total && (q + 2) % nb == 0) {
+      lds_barrier();
+      stage((q + 2) / nb);
+      lds_barrier();
+    }
+  }
+  float best_v = -INFINITY;
+  int best_i = 0x7fffffff;
+  s_finish_tile<T, EPI>(a, acc, red, ct, t, layer, &best_v, &best_i, inv_freq);
+  if constexpr (EPI == EPI_ARGMAX) {
+    if (tid < 16 && tid < a.M) {
+      a.amax_val[(size_t)tid * gridDim.x + blockIdx.x] = best_v;
+      a.amax_idx[(size_t)tid * gridDim.x + blockIdx.x] = best_i;
+    }
+  }
+}
+
 template <typename T, int EPI>
 static hipError_t launch_s(int am, const GemmArgs &a, dim3 grid, hipStream_t st) {
   const dim3 block(kSThreads);
@@ -328,6 +448,9 @@ static hipError_t launch_s(int am, const GemmArgs &a, dim3 grid, hipStream_t st)
     case A_NORM: hipLaunchKernelGGL((gemm_stream_kernel<T, EPI, A_NORM>), grid, block, 0, st, a); break;
     case A_EMBED_NORM:
       hipLaunchKernelGGL((gemm_stream_kernel<T, EPI, A_EMBED_NORM>), grid, block, 0, st, a);
+      break;
+    case 4:   // K-portions, one tile per workgroup (grid.x = tiles)
+      hipLaunchKernelGGL((gemm_portion_kernel<T, EPI>), dim3(a.n_groups, grid.y), block, 0, st, a);
       break;
     default: return hipErrorInvalidValue;
   }

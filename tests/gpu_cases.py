@@ -45,6 +45,10 @@ MINI = {
     "mini_b8": mini("mini_b8", 105, dtype="bf16", hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
                     ffn=1088, vocab=4096, n_layers=2, n_feat_layers=3, block_size=16, batch=8,
                     ctx_min=3, ctx_max=400, rope_theta=1e6),
+    # FFN and feature widths above one 4096-wide LDS portion (ragged last portion)
+    "mini_port": mini("mini_port", 106, dtype="bf16", hidden=256, n_q_heads=2, n_kv_heads=1, head_dim=128,
+                      ffn=4352, vocab=1040, n_layers=2, n_feat_layers=17, block_size=8, batch=2,
+                      ctx_min=30, ctx_max=200, rope_theta=1e6),
     "tiny": S.get_config("tiny"),
 }
 

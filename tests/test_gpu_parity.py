@@ -92,7 +92,7 @@ def test_lmhead_argmax(name, rows):
 # A1 + A2 inject
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("name,n_new", [(n, k) for n in ["tiny", "mini_bf16", "mini_d64", "mini_f32"]
-                                        for k in [1, 16, 90]] + [("mini_bf16", 200), ("mini_d64", 300)])
+                                        for k in [1, 16, 90]] + [("mini_bf16", 200), ("mini_d64", 300), ("mini_port", 5), ("mini_port", 16)])
 def test_inject_context(name, n_new):
     cfg = MINI[name]
     log(f"inject {name} n_new={n_new}")
@@ -161,7 +161,7 @@ def run_draft_case(cfg, seed=0, lens=None, check_seqs=None):
     return hid_h, ids_h
 
 
-@pytest.mark.parametrize("name", ["tiny", "mini_bf16", "mini_b10", "mini_d64", "mini_f32", "mini_b8"])
+@pytest.mark.parametrize("name", ["tiny", "mini_bf16", "mini_b10", "mini_d64", "mini_f32", "mini_b8", "mini_port"])
 def test_draft_block(name):
     log(f"draft_block {name}")
     run_draft_case(MINI[name], seed=0)
