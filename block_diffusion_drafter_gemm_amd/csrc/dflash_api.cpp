@@ -127,15 +127,18 @@ int launch_stream(dflash_handle_s *h, Epilogue epi, int amode, GemmArgs &a, int 
                   int *grid_out = nullptr) {
   a.m_groups = 1;
   a.n_groups = gemm_tiles(epi, a.N, a.ffn);
-  int grid = compute_units(h);
-  if (grid > a.n_groups || amode == AM_PORTION) grid = a.n_groups;   // portions: one tile per workgroup
+  // the fewest workgroups that keep the largest per-workgroup tile count (a
+  // balanced grid); portions run one tile per workgroup
+  const int per = (a.n_groups + compute_units(h) - 1) / compute_units(h);
+  int grid = (a.n_groups + per - 1) / per;
+  if (amode == AM_PORTION) grid = a.n_groups;
   if (grid_out) *grid_out = grid;
   return launch_gemm_stream(h->bf16, epi, amode, a, grid, z, st) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
 int validate_config(const dflash_config *c) {
   if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return DFLASH_ERR_DTYPE;
-  if (c->hidden <= 0 || c->hidden % 64) return DFLASH_ERR_SHAPE;
+  if (c->hidden <= 0 || c->hidden % 64 || c->hidden > 16384) return DFLASH_ERR_SHAPE;
   if (c->head_dim != 64 && c->head_dim != 128) return DFLASH_ERR_SHAPE;
   if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->n_q_heads % c->n_kv_heads) return DFLASH_ERR_SHAPE;
   if ((c->n_q_heads * c->head_dim) % 64) return DFLASH_ERR_SHAPE;
@@ -386,7 +389,9 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     o.K = qd;
     o.X = X;
     o.ldx = c.hidden;
-    st = fast ? launch_stream(h, EPI_RESID, AM_COPY, o, 1, s) : launch(h, EPI_RESID, o, 1, s);
+    // one tile per workgroup: activation fragments read straight from L2 beat
+    // staging the rows through LDS first
+    st = fast ? launch_stream(h, EPI_RESID, AM_GLOBAL, o, 1, s) : launch(h, EPI_RESID, o, 1, s);
     if (st != DFLASH_OK) return st;
 
     // A7: RMSNorm, gate/up + SwiGLU, down + residual

@@ -100,6 +100,22 @@ __device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<float> &a, const Frag
   return acc;
 }
 
+// Four consecutive elements (group q4) of a row as floats, and the reverse
+// (rounded to the storage type).
+__device__ __forceinline__ float4 load4(const float *p, int q4) { return reinterpret_cast<const float4 *>(p)[q4]; }
+__device__ __forceinline__ float4 load4(const bf16_t *p, int q4) {
+  const uint2 u = reinterpret_cast<const uint2 *>(p)[q4];
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ void store4(float *p, int q4, float4 v) { reinterpret_cast<float4 *>(p)[q4] = v; }
+__device__ __forceinline__ void store4(bf16_t *p, int q4, float4 v) {
+  uint2 u;
+  u.x = f32_to_bf16(v.x) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
+  u.y = f32_to_bf16(v.z) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
+  reinterpret_cast<uint2 *>(p)[q4] = u;
+}
+
 __device__ __forceinline__ float f4get(const f32x4 &v, int i) {
   return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
 }

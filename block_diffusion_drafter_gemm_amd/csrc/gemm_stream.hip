@@ -47,10 +47,34 @@ __device__ __forceinline__ int s_weight_row(const GemmArgs &a, int t, int c) {
   }
 }
 
-// Epilogue of one 16 x 16 tile held in LDS (ct, row-major [16][16]).
+// Epilogue operands that do not depend on the weights, read at kernel start so
+// that the epilogue issues no dependent global load: the residual element of
+// the workgroup's first tile (thread tid < 256 owns row tid / 16, column
+// tid % 16) and the context length of the thread's row (QKV, tid < 128).
+// Indices are clamped so every thread loads from a valid address.
+struct EpiPre {
+  float x;
+  int ctx;
+};
+
+template <int EPI>
+__device__ __forceinline__ EpiPre s_epi_pre(const GemmArgs &a, int t0) {
+  EpiPre p{0.f, 0};
+  const int tid = threadIdx.x;
+  if constexpr (EPI == EPI_RESID) {
+    const int r = min(tid >> 4, a.M - 1), c = tid & 15;
+    p.x = a.X[(size_t)r * a.ldx + t0 * 16 + c];
+  } else if constexpr (EPI == EPI_QKV) {
+    p.ctx = a.ctx_len[min(tid >> 3, a.M - 1) / a.block_size];
+  }
+  return p;
+}
+
+// Epilogue of one 16 x 16 tile held in LDS (ct, row-major [16][16]); ``first``
+// marks the workgroup's first tile, whose residual elements are in ``pre``.
 template <typename T, int EPI>
 __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, int t, int layer, float *best_v,
-                                           int *best_i, const double *inv_freq) {
+                                           int *best_i, const double *inv_freq, const EpiPre &pre, bool first) {
   const int tid = threadIdx.x;
   if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_F32 || EPI == EPI_RESID) {
     if (tid < 256) {
@@ -60,7 +84,10 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
         const float v = ct[tid];
         if constexpr (EPI == EPI_STORE) Storage<T>::store((T *)a.out, (size_t)r * a.ldo + n, v);
         else if constexpr (EPI == EPI_STORE_F32) ((float *)a.out)[(size_t)r * a.ldo + n] = v;
-        else a.X[(size_t)r * a.ldx + n] += v;
+        else {
+          float *xp = a.X + (size_t)r * a.ldx + n;
+          *xp = (first ? pre.x : *xp) + v;
+        }
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
@@ -76,16 +103,17 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
       const int r = tid >> 3, c = tid & 7;
       if (r < a.M) {
         const int hd = a.hd, half = hd / 2;
-        const int qcols = (EPI == EPI_QKV) ? a.nq * hd : 0;
+        const int nqh = (EPI == EPI_QKV) ? a.nq : 0;  // q heads in the output
+        const int qcols = nqh * hd;
         const int kcols = a.nkv * hd;
+        const int h = t / (hd / 16);                  // head of this tile (uniform)
         const int j0 = (t % (hd / 16)) * 8;
         const int n = s_weight_row<EPI>(a, t, c);
         const float x1 = ct[r * 16 + c], x2 = ct[r * 16 + 8 + c];
         int pos;
         size_t slot = 0;
         if constexpr (EPI == EPI_QKV) {
-          const int s = r / a.block_size, j = r - s * a.block_size;
-          pos = a.ctx_len[s] + j;
+          pos = pre.ctx + r % a.block_size;
         } else {
           pos = a.pos[r];
           const int s = a.seq[r];
@@ -93,18 +121,19 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
           slot = (size_t)layer * a.cache_layer_stride + ((size_t)page * a.page_size + (pos % a.page_size)) * kcols;
         }
         float lo = x1, hi = x2;
-        if (n < qcols + kcols) {
+        if (h < nqh + a.nkv) {                        // q and k heads rotate
           float cs, sn;
           rope_cs_inv(pos, inv_freq[j0 + c], &cs, &sn);
           lo = x1 * cs - x2 * sn;
           hi = x2 * cs + x1 * sn;
         }
+        // the destination depends on the head only, so it is chosen per tile
         T *dst;
         size_t off;
-        if (n < qcols) {
+        if (h < nqh) {
           dst = (T *)a.q_out;
           off = (size_t)r * qcols + n;
-        } else if (n < qcols + kcols) {
+        } else if (h < nqh + a.nkv) {
           dst = (T *)a.k_out;
           off = (EPI == EPI_QKV ? (size_t)r * kcols : slot) + (n - qcols);
         } else {
@@ -133,36 +162,44 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
 
 // One batch of U k-chunks: weight fragments (and, when the activations are not
 // resident, activation fragments) for one lane.
+//
+// Loads are issued unconditionally: a chunk past the wave's range reads the
+// last valid chunk of the row instead, and its product is masked to zero at
+// compute time.  Branch-free issue lets the compiler count outstanding loads
+// exactly, so consuming one buffer waits only for that buffer's loads while
+// the other buffer's batch stays in flight.  Lanes of rows >= M read row 0;
+// their output rows are never stored.
 template <typename T, int U, bool RES>
 struct StreamBuf {
   Frag<T> w[U];
   Frag<T> x[RES ? 1 : U];
 
   template <int EPI>
-  __device__ __forceinline__ void issue(const GemmArgs &a, const T *W, const T *arow, bool row_ok, int t, int c0,
-                                        int cend) {
+  __device__ __forceinline__ void issue(const GemmArgs &a, const T *W, const T *arow, int t, int c0, int clast) {
     const int ln = threadIdx.x & 15, g = (threadIdx.x >> 4) & 3;
     const T *wp = W + (size_t)s_weight_row<EPI>(a, t, ln) * a.ldw + 8 * g;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      if (c0 + j < cend) w[j].load(wp + 32 * (c0 + j)); else w[j].zero();
-      if constexpr (!RES) {
-        if (c0 + j < cend && row_ok) x[j].load(arow + 32 * (c0 + j)); else x[j].zero();
-      }
+      const int c = min(c0 + j, clast);
+      w[j].load(wp + 32 * c);
+      if constexpr (!RES) x[j].load(arow + 32 * c);
     }
+    // the scheduler would otherwise sink the loads below the products that
+    // free their registers, which serialises the stream
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  __device__ __forceinline__ f32x4 compute(f32x4 acc, const T *arow, int c0, int cend) const {
+  __device__ __forceinline__ f32x4 compute(f32x4 acc, const T *arow, int c0, int cend, int clast) const {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      if (c0 + j < cend) {
-        if constexpr (RES) {
-          Frag<T> af;
-          af.load(arow + 32 * (c0 + j));
-          acc = mma(acc, af, w[j]);
-        } else {
-          acc = mma(acc, x[j], w[j]);
-        }
+      Frag<T> wj = w[j];
+      if (c0 + j >= cend) wj.zero();
+      if constexpr (RES) {
+        Frag<T> af;
+        af.load(arow + 32 * min(c0 + j, clast));
+        acc = mma(acc, af, wj);
+      } else {
+        acc = mma(acc, x[j], wj);
       }
     }
     return acc;
@@ -172,7 +209,8 @@ struct StreamBuf {
 // Tile finished: sum the 16 waves' partial tiles in wave order, run the epilogue.
 template <typename T, int EPI>
 __device__ __forceinline__ void s_finish_tile(const GemmArgs &a, f32x4 &acc, float (*red)[256], float *ct, int t,
-                                              int layer, float *best_v, int *best_i, const double *inv_freq) {
+                                              int layer, float *best_v, int *best_i, const double *inv_freq,
+                                              const EpiPre &pre, bool first) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, ln = lane & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][(4 * g + i) * 16 + ln] = f4get(acc, i);
@@ -185,7 +223,7 @@ __device__ __forceinline__ void s_finish_tile(const GemmArgs &a, f32x4 &acc, flo
     ct[tid] = sm;
   }
   lds_barrier();
-  s_epilogue<T, EPI>(a, ct, t, layer, best_v, best_i, inv_freq);
+  s_epilogue<T, EPI>(a, ct, t, layer, best_v, best_i, inv_freq, pre, first);
 }
 
 template <typename T, int EPI, int AM>
@@ -199,7 +237,8 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   __shared__ float red[kSWaves][256];
   __shared__ float ct[256];
   __shared__ double inv_freq[64];   // RoPE inverse frequencies (head_dim <= 128)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, ln = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, ln = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int layer = blockIdx.y;
   if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
     if (tid < a.hd / 2) inv_freq[tid] = rope_inv_freq(tid, a.hd, a.log2_theta);
@@ -210,106 +249,134 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   const int CPT = a.K / 32;                                    // chunks per tile
   const int CPW = (CPT + kSWaves - 1) / kSWaves;               // chunks per wave
   const int cbeg = min(CPT, wave * CPW), cend = min(CPT, cbeg + CPW);
+  const int clast = CPT - 1;                                   // always a valid chunk
   const int nb = (CPW + U - 1) / U;                            // batches per tile per wave
   const int my_tiles = blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
   const int total = my_tiles * nb;
+  // tile of batch q of this workgroup, clamped to a valid tile
+  const int grid = gridDim.x;
+  auto tile_of = [&](int q) { return min((int)blockIdx.x + (q / nb) * grid, ntiles - 1); };
 
+  // batch Q: its tile and first chunk, or the dummy read past the end
+#define DF_ISSUE(BUF, Q)                                                                        \
+  {                                                                                            \
+    const bool live_ = (Q) < total;                                                            \
+    const int d_ = min(cbeg, clast); /* the dummy's chunk, valid even for a wave with no chunks */ \
+    BUF.template issue<EPI>(a, W, arow, tile_of(live_ ? (Q) : 0), live_ ? cbeg + ((Q) % nb) * U : d_, \
+                            live_ ? clast : d_);                                               \
+  }
+  const EpiPre pre = s_epi_pre<EPI>(a, tile_of(0));
   const T *A = (const T *)a.A;
   const bool row_ok = ln < a.M;
   const T *arow = RES ? reinterpret_cast<const T *>(a_lds + ln * ASTR) + 8 * g
                       : A + (size_t)(row_ok ? ln : 0) * a.lda + 8 * g;
-  // first weight batch goes out before the activations are staged
   StreamBuf<T, U, RES> bufa, bufb;
-  if (total > 0) bufa.template issue<EPI>(a, W, arow, row_ok, blockIdx.x, cbeg, cend);
 
   // ---- resident activation rows ---------------------------------------------
+  // Wave w stages row w.  Every load of the row (and of the gain) is issued
+  // unconditionally, from clamped addresses, before the first weight batch, so
+  // waiting for them leaves that batch in flight.  Rows >= M are stored as
+  // zeros.
   if constexpr (RES) {
-    // wave w owns row w; one pass with the row held in registers
-    constexpr int PER = KR / 64;              // elements per lane at most
-    constexpr int EPV = 16 / (int)sizeof(T);  // elements per 16-byte vector
     const int r = wave;
-    T *dst = reinterpret_cast<T *>(a_lds + r * ASTR);
-    const int nvec = a.K / EPV;               // 16-byte vectors in the row
+    const bool have_row = r < a.M;
+    const int rr = min(r, a.M - 1);
     if constexpr (AM == A_COPY) {
-      if (r < a.M) {
-        for (int i = lane; i < nvec; i += 64)
-          *reinterpret_cast<uint4 *>(dst + i * EPV) = *reinterpret_cast<const uint4 *>(A + (size_t)r * a.lda + i * EPV);
-      } else {
-        for (int i = lane; i < nvec; i += 64) *reinterpret_cast<uint4 *>(dst + i * EPV) = make_uint4(0, 0, 0, 0);
+      constexpr int EPV = 16 / (int)sizeof(T);     // elements per 16-byte vector
+      constexpr int NV = KR / EPV / 64;            // vectors per lane at most
+      const int nvec = a.K / EPV;
+      const uint4 *src = reinterpret_cast<const uint4 *>(A + (size_t)rr * a.lda);
+      uint4 cv[NV];
+#pragma unroll
+      for (int k = 0; k < NV; ++k) cv[k] = src[min(lane + 64 * k, nvec - 1)];
+      DF_ISSUE(bufa, 0);
+      uint4 *dst = reinterpret_cast<uint4 *>(a_lds + r * ASTR);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int i = lane + 64 * k;
+        if (i < nvec) dst[i] = have_row ? cv[k] : make_uint4(0, 0, 0, 0);
       }
     } else {
-      // lane owns elements [4*(lane + 64*j), +4) for j < K/256 (fp32 X) or the
-      // same spans of the bf16 embedding row
-      float v[PER];
-      const int nq4 = a.K / 4;                // float4 groups in the row
-      if (r < a.M) {
-        if constexpr (AM == A_EMBED_NORM) {
-          const int s = r / a.block_size, j = r - s * a.block_size;
-          const int id = j == 0 ? a.anchor[s] : a.mask_id;
-          const T *erow = (const T *)a.embed + (size_t)id * a.K;
+      // lane owns the 4-element groups q4 = lane + 64 k of the row; the gain
+      // is read once per workgroup (one group per thread) and parked in the
+      // reduction buffer, which is unused until the first tile finishes
+      constexpr int PQ = KR / 4 / 64;              // groups per lane at most
+      const int nq4 = a.K / 4;
+      float4 xv[PQ];
+      if constexpr (AM == A_EMBED_NORM) {
+        const int s = rr / a.block_size, j = rr - s * a.block_size;
+        const int id = j == 0 ? a.anchor[s] : a.mask_id;
+        const T *erow = (const T *)a.embed + (size_t)id * a.K;
 #pragma unroll
-          for (int k = 0; k < PER / 4; ++k) {
-            const int q4 = lane + 64 * k;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[4 * k + e] = q4 < nq4 ? Storage<T>::load(erow, 4 * q4 + e) : 0.f;
-          }
-        } else {
-          const float4 *x4 = reinterpret_cast<const float4 *>(a.X + (size_t)r * a.ldx);
-#pragma unroll
-          for (int k = 0; k < PER / 4; ++k) {
-            const int q4 = lane + 64 * k;
-            const float4 f = q4 < nq4 ? x4[q4] : make_float4(0.f, 0.f, 0.f, 0.f);
-            v[4 * k] = f.x; v[4 * k + 1] = f.y; v[4 * k + 2] = f.z; v[4 * k + 3] = f.w;
-          }
-        }
-        float ss = 0.f;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) ss += v[k] * v[k];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-        const float rs = 1.0f / sqrtf(ss / (float)a.K + a.eps);
-        const T *gain = (const T *)a.gain;
-        const bool write_x = AM == A_EMBED_NORM && blockIdx.x == 0 && blockIdx.y == 0;
-#pragma unroll
-        for (int k = 0; k < PER / 4; ++k) {
-          const int q4 = lane + 64 * k;
-          if (q4 < nq4) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = 4 * q4 + e;
-              if (write_x) a.X[(size_t)r * a.ldx + i] = v[4 * k + e];   // residual stream
-              Storage<T>::store(dst, i, v[4 * k + e] * rs * Storage<T>::load(gain, i));
-            }
-          }
-        }
+        for (int k = 0; k < PQ; ++k) xv[k] = load4(erow, min(lane + 64 * k, nq4 - 1));
       } else {
-        for (int i = lane; i < nvec; i += 64) *reinterpret_cast<uint4 *>(dst + i * EPV) = make_uint4(0, 0, 0, 0);
+        const float4 *x4 = reinterpret_cast<const float4 *>(a.X + (size_t)rr * a.ldx);
+#pragma unroll
+        for (int k = 0; k < PQ; ++k) xv[k] = x4[min(lane + 64 * k, nq4 - 1)];
+      }
+      const float4 gq = load4((const T *)a.gain, min(tid, nq4 - 1));
+      DF_ISSUE(bufa, 0);
+      float4 *gl = reinterpret_cast<float4 *>(&red[0][0]);
+      if (tid < nq4) gl[tid] = gq;
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < PQ; ++k) {
+        if (lane + 64 * k < nq4) {
+          ss += xv[k].x * xv[k].x;
+          ss += xv[k].y * xv[k].y;
+          ss += xv[k].z * xv[k].z;
+          ss += xv[k].w * xv[k].w;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+      const float rs = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+      const bool write_x = AM == A_EMBED_NORM && have_row && blockIdx.x == 0 && blockIdx.y == 0;
+      T *dst = reinterpret_cast<T *>(a_lds + r * ASTR);
+      lds_barrier();                               // gain visible
+#pragma unroll
+      for (int k = 0; k < PQ; ++k) {
+        const int q4 = lane + 64 * k;
+        if (q4 < nq4) {
+          const float4 gv = gl[q4];
+          float4 o;
+          o.x = xv[k].x * rs * gv.x;
+          o.y = xv[k].y * rs * gv.y;
+          o.z = xv[k].z * rs * gv.z;
+          o.w = xv[k].w * rs * gv.w;
+          if (!have_row) o = make_float4(0.f, 0.f, 0.f, 0.f);
+          store4(dst, q4, o);
+          if (write_x) reinterpret_cast<float4 *>(a.X + (size_t)r * a.ldx)[q4] = xv[k];   // residual stream
+        }
       }
     }
-    __syncthreads();
+    lds_barrier();
+  } else {
+    DF_ISSUE(bufa, 0);
   }
 
-  // ---- weight (and activation) fragment pipeline, two batches in flight ------
   float best_v = -INFINITY;
   int best_i = 0x7fffffff;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   // static ping-pong between two register buffers (dynamic selection would
-  // spill the fragments to scratch)
+  // spill the fragments to scratch).  The next batch is issued whether or not
+  // it exists (past the end it re-reads the wave's first chunk of the
+  // workgroup's first tile, a cache hit, and is never used): with no branch
+  // around the issue, consuming one buffer waits for that buffer only.
+  // Both halves always run (no exit in the middle of the loop, which keeps
+  // the outstanding-load count identical on every path into the loop head); a
+  // second half past the end consumes the dummy batch and finishes nothing.
   for (int q = 0; q < total; q += 2) {
-    if (q + 1 < total)
-      bufb.template issue<EPI>(a, W, arow, row_ok, blockIdx.x + ((q + 1) / nb) * gridDim.x,
-                               cbeg + ((q + 1) % nb) * U, cend);
-    acc = bufa.compute(acc, arow, cbeg + (q % nb) * U, cend);
+    DF_ISSUE(bufb, q + 1);
+    acc = bufa.compute(acc, arow, cbeg + (q % nb) * U, cend, clast);
     if (q % nb == nb - 1)
-      s_finish_tile<T, EPI>(a, acc, red, ct, blockIdx.x + (q / nb) * gridDim.x, layer, &best_v, &best_i, inv_freq);
-    if (q + 1 >= total) break;
-    if (q + 2 < total)
-      bufa.template issue<EPI>(a, W, arow, row_ok, blockIdx.x + ((q + 2) / nb) * gridDim.x,
-                               cbeg + ((q + 2) % nb) * U, cend);
-    acc = bufb.compute(acc, arow, cbeg + ((q + 1) % nb) * U, cend);
-    if ((q + 1) % nb == nb - 1)
-      s_finish_tile<T, EPI>(a, acc, red, ct, blockIdx.x + ((q + 1) / nb) * gridDim.x, layer, &best_v, &best_i, inv_freq);
+      s_finish_tile<T, EPI>(a, acc, red, ct, tile_of(q), layer, &best_v, &best_i, inv_freq, pre, q < nb);
+    DF_ISSUE(bufa, q + 2);
+    acc = bufb.compute(acc, arow, cbeg + ((q + 1) % nb) * U, cend, clast);
+    if ((q + 1) % nb == nb - 1 && q + 1 < total)
+      s_finish_tile<T, EPI>(a, acc, red, ct, tile_of(q + 1), layer, &best_v, &best_i, inv_freq, pre, q + 1 < nb);
   }
+#undef DF_ISSUE
 
   if constexpr (EPI == EPI_ARGMAX) {
     if (tid < 16 && tid < a.M) {
@@ -320,117 +387,100 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
 }
 
 // K longer than the resident capacity: one 16-column tile per workgroup, the
-// activation rows staged into LDS one K-portion at a time (each wave takes an
-// even share of the portion's k-chunks); the weight fragments of the next
-// batch are in flight across portion boundaries, the accumulator stays in
-// registers until the whole K is done.
+// activation rows staged into LDS one K-portion at a time.  A portion has
+// KR / 32 k-chunks, exactly one batch of U chunks per wave.  While portion p
+// is multiplied, the rows of portion p + 1 (registers) and its weight batch
+// are already in flight; the accumulator stays in registers until the whole K
+// is done.
 template <typename T, int EPI>
 __global__ __launch_bounds__(kSThreads) void gemm_portion_kernel(const GemmArgs a) {
   constexpr int KR = stream_res_k<T>();
   constexpr int ASTR = KR * (int)sizeof(T) + 16;
   constexpr int U = 8 / (int)(sizeof(T) / 2);
-  constexpr int EPV = 16 / (int)sizeof(T);
+  constexpr int EPV = 16 / (int)sizeof(T);       // elements per 16-byte vector
+  constexpr int CPP = KR / 32;                   // chunks per full portion
+  constexpr int NV = KR / EPV / 64;              // staged vectors per lane
+  static_assert(CPP == kSWaves * U, "one batch per wave per portion");
   __shared__ __align__(16) unsigned char a_lds[16 * ASTR];
   __shared__ float red[kSWaves][256];
   __shared__ float ct[256];
   __shared__ double inv_freq[64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, ln = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, ln = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int layer = blockIdx.y, t = blockIdx.x;
   if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
     if (tid < a.hd / 2) inv_freq[tid] = rope_inv_freq(tid, a.hd, a.log2_theta);
   }
   const T *W = (const T *)a.W[layer];
-  const T *A = (const T *)a.A;
-  const int np = (a.K + KR - 1) / KR;               // portions
-  const int CPP = KR / 32;                          // chunks per full portion
-  const int CPW = (CPP + kSWaves - 1) / kSWaves;    // chunks per wave per portion
-  const int nb = (CPW + U - 1) / U;                 // batches per wave per portion
-  const int total = np * nb;
+  const int nchunk = a.K / 32;
+  const int np = (nchunk + CPP - 1) / CPP;       // portions
+  const int clast = nchunk - 1;
   const T *wrow = W + (size_t)s_weight_row<EPI>(a, t, ln) * a.ldw + 8 * g;
   const T *arow = reinterpret_cast<const T *>(a_lds + ln * ASTR) + 8 * g;
-  // chunk range of unit q (portion q / nb, batch q % nb), in absolute chunks
-  auto range = [&](int q, int *c0, int *c1) {
-    const int p = q / nb, b = q % nb;
-    const int pc = min(CPP, a.K / 32 - p * CPP);    // chunks in this portion
-    const int wb = min(pc, wave * CPW), we = min(pc, wb + CPW);
-    *c0 = p * CPP + min(we, wb + b * U);
-    *c1 = p * CPP + min(we, wb + b * U + U);
-  };
-  auto stage = [&](int p) {                         // wave w copies row w of portion p
-    const int r = wave;
-    T *dst = reinterpret_cast<T *>(a_lds + r * ASTR);
-    const int kk = min(KR, a.K - p * KR);
-    for (int i = lane; i < kk / EPV; i += 64)
-      *reinterpret_cast<uint4 *>(dst + i * EPV) =
-          r < a.M ? *reinterpret_cast<const uint4 *>(A + (size_t)r * a.lda + p * KR + i * EPV) : make_uint4(0, 0, 0, 0);
-  };
+  // wave w stages row w (row 0 stands in for rows >= M, stored as zeros)
+  const bool have_row = wave < a.M;
+  const uint4 *srow = reinterpret_cast<const uint4 *>((const T *)a.A + (size_t)min(wave, a.M - 1) * a.lda);
+  uint4 *drow = reinterpret_cast<uint4 *>(a_lds + wave * ASTR);
+  // portion p: its first chunk and chunk count; past the last portion a dummy
+  // re-read of the tile's chunk 0 (a cache hit, never used) keeps the issue
+  // free of branches
+  auto pfirst = [&](int p) { return p < np ? p * CPP : 0; };
+  auto pcount = [&](int p) { return p < np ? min(CPP, nchunk - p * CPP) : 1; };
+  const EpiPre pre = s_epi_pre<EPI>(a, t);
+
   Frag<T> wa[U], wb[U];
-  int c0, c1;
-  range(0, &c0, &c1);
-#pragma unroll
-  for (int j = 0; j < U; ++j) {
-    if (c0 + j < c1) wa[j].load(wrow + 32 * (c0 + j)); else wa[j].zero();
+  uint4 cv[NV];
+#define DF_PORTION_LOAD(WBUF, P)                                                              \
+  {                                                                                          \
+    const int f_ = pfirst(P), n_ = pcount(P) * 32 / EPV;                                     \
+    _Pragma("unroll") for (int k = 0; k < NV; ++k) cv[k] = srow[f_ * 32 / EPV + min(lane + 64 * k, n_ - 1)]; \
+    const int c0_ = (P) < np ? f_ + wave * U : 0, cl_ = (P) < np ? clast : 0;                 \
+    _Pragma("unroll") for (int j = 0; j < U; ++j) WBUF[j].load(wrow + 32 * min(c0_ + j, cl_)); \
+    __builtin_amdgcn_sched_barrier(0);  /* keep the prefetch ahead of the products */       \
   }
-  stage(0);
-  __syncthreads();
+#define DF_PORTION_STORE(P)                                                                   \
+  {                                                                                          \
+    const int n_ = pcount(P) * 32 / EPV;                                                     \
+    _Pragma("unroll") for (int k = 0; k < NV; ++k) {                                         \
+      const int i_ = lane + 64 * k;                                                          \
+      if (i_ < n_) drow[i_] = have_row ? cv[k] : make_uint4(0, 0, 0, 0);                     \
+    }                                                                                        \
+  }
+#define DF_PORTION_MMA(WBUF, P)                                                               \
+  {                                                                                          \
+    const int pc_ = pcount(P), b_ = min(pc_, wave * U), e_ = min(pc_, b_ + U);               \
+    _Pragma("unroll") for (int j = 0; j < U; ++j) {                                          \
+      Frag<T> wj = WBUF[j], af;                                                              \
+      if (b_ + j >= e_) wj.zero();                                                           \
+      af.load(arow + 32 * min(b_ + j, pc_ - 1));                                             \
+      acc = mma(acc, af, wj);                                                                \
+    }                                                                                        \
+  }
+
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int q = 0; q < total; q += 2) {
-    // --- unit q from wa, prefetch q + 1 into wb
-    int n0, n1;
-    if (q + 1 < total) {
-      range(q + 1, &n0, &n1);
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        if (n0 + j < n1) wb[j].load(wrow + 32 * (n0 + j)); else wb[j].zero();
-      }
-    }
-    range(q, &c0, &c1);
-    {
-      const int pbase = (q / nb) * CPP;
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        if (c0 + j < c1) {
-          Frag<T> af;
-          af.load(arow + 32 * (c0 + j - pbase));
-          acc = mma(acc, af, wa[j]);
-        }
-      }
-    }
-    if (q + 1 < total && (q + 1) % nb == 0) {       // next unit starts a new portion
-      lds_barrier();
-      stage((q + 1) / nb);
-      lds_barrier();
-    }
-    if (q + 1 >= total) break;
-    // --- unit q + 1 from wb, prefetch q + 2 into wa
-    if (q + 2 < total) {
-      range(q + 2, &n0, &n1);
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        if (n0 + j < n1) wa[j].load(wrow + 32 * (n0 + j)); else wa[j].zero();
-      }
-    }
-    range(q + 1, &c0, &c1);
-    {
-      const int pbase = ((q + 1) / nb) * CPP;
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        if (c0 + j < c1) {
-          Frag<T> af;
-          af.load(arow + 32 * (c0 + j - pbase));
-          acc = mma(acc, af, wb[j]);
-        }
-      }
-    }
-    if (q + 2 < total && (q + 2) % nb == 0) {
-      lds_barrier();
-      stage((q + 2) / nb);
-      lds_barrier();
-    }
+  DF_PORTION_LOAD(wa, 0);
+  DF_PORTION_STORE(0);
+  lds_barrier();
+  for (int p = 0; p < np; p += 2) {
+    DF_PORTION_LOAD(wb, p + 1);
+    DF_PORTION_MMA(wa, p);
+    if (p + 1 >= np) break;
+    lds_barrier();
+    DF_PORTION_STORE(p + 1);
+    lds_barrier();
+    DF_PORTION_LOAD(wa, p + 2);
+    DF_PORTION_MMA(wb, p + 1);
+    if (p + 2 >= np) break;
+    lds_barrier();
+    DF_PORTION_STORE(p + 2);
+    lds_barrier();
   }
+#undef DF_PORTION_LOAD
+#undef DF_PORTION_STORE
+#undef DF_PORTION_MMA
   float best_v = -INFINITY;
   int best_i = 0x7fffffff;
-  s_finish_tile<T, EPI>(a, acc, red, ct, t, layer, &best_v, &best_i, inv_freq);
+  s_finish_tile<T, EPI>(a, acc, red, ct, t, layer, &best_v, &best_i, inv_freq, pre, true);
   if constexpr (EPI == EPI_ARGMAX) {
     if (tid < 16 && tid < a.M) {
       a.amax_val[(size_t)tid * gridDim.x + blockIdx.x] = best_v;

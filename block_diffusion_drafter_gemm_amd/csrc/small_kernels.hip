@@ -5,6 +5,8 @@
 
 namespace dflash {
 
+constexpr int kNormThreads = 512;
+
 // X[s*B + j, :] = E[j == 0 ? anchor[s] : mask] as fp32 (the residual stream).
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T *E, const int *anchor, int mask_id, int B, int H,
@@ -31,19 +33,40 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
 // Y[r] = X[src(r)] / sqrt(mean(X^2) + eps) * gain, rounded to the storage type.
 // skip_anchor: output row r reads input row s*B + 1 + (r % (B-1)) with
 // s = r / (B-1) (the mask rows of every block).
-template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float *X, const T *gain, float eps, int H, int B,
-                                                      int skip_anchor, T *Y) {
-  __shared__ float red[4];
-  const int r = blockIdx.x;
+// One workgroup per row; each thread holds up to KV four-element groups of the
+// row in registers (all loads issued at once, one pass over the row).
+template <typename T, int KV>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float *X, const T *gain, float eps, int H, int B,
+                                                               int skip_anchor, T *Y) {
+  __shared__ float red[kNormThreads / 64];
+  const int r = blockIdx.x, tid = threadIdx.x;
   const int src = skip_anchor ? (r / (B - 1)) * B + 1 + r % (B - 1) : r;
-  const float *x = X + (size_t)src * H;
+  const float4 *x4 = reinterpret_cast<const float4 *>(X + (size_t)src * H);
+  const int n4 = H / 4;
+  float4 v[KV];
+#pragma unroll
+  for (int k = 0; k < KV; ++k) v[k] = x4[min(tid + kNormThreads * k, n4 - 1)];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) ss += x[i] * x[i];
+#pragma unroll
+  for (int k = 0; k < KV; ++k) {
+    if (tid + kNormThreads * k < n4) {
+      ss += v[k].x * v[k].x;
+      ss += v[k].y * v[k].y;
+      ss += v[k].z * v[k].z;
+      ss += v[k].w * v[k].w;
+    }
+  }
   ss = block_sum(ss, red);
   const float rs = 1.0f / sqrtf(ss / (float)H + eps);
-  for (int i = threadIdx.x; i < H; i += blockDim.x)
-    Storage<T>::store(Y, (size_t)r * H + i, x[i] * rs * Storage<T>::load(gain, i));
+  T *y = Y + (size_t)r * H;
+#pragma unroll
+  for (int k = 0; k < KV; ++k) {
+    const int q = tid + kNormThreads * k;
+    if (q < n4) {
+      const float4 g = load4(gain, q);
+      store4(y, q, make_float4(v[k].x * rs * g.x, v[k].y * rs * g.y, v[k].z * rs * g.z, v[k].w * rs * g.w));
+    }
+  }
 }
 
 // Second level of the vocabulary argmax: one workgroup per row scans the
@@ -106,15 +129,22 @@ hipError_t launch_embed(bool is_bf16, const void *embed, const int *anchor, int 
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t launch_rmsnorm_t(const float *X, const T *gain, float eps, int rows, int H, int B, bool skip_anchor,
+                                   T *Y, hipStream_t st) {
+  const int n4 = H / 4, sa = skip_anchor ? 1 : 0;
+  const dim3 grid(rows), block(kNormThreads);
+  if (n4 <= 2 * kNormThreads) hipLaunchKernelGGL((rmsnorm_kernel<T, 2>), grid, block, 0, st, X, gain, eps, H, B, sa, Y);
+  else if (n4 <= 4 * kNormThreads) hipLaunchKernelGGL((rmsnorm_kernel<T, 4>), grid, block, 0, st, X, gain, eps, H, B, sa, Y);
+  else if (n4 <= 8 * kNormThreads) hipLaunchKernelGGL((rmsnorm_kernel<T, 8>), grid, block, 0, st, X, gain, eps, H, B, sa, Y);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_rmsnorm(bool is_bf16, const float *X, const void *gain, float eps, int rows, int H, int B,
                           bool skip_anchor, void *Y, hipStream_t st) {
-  if (is_bf16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, X, (const bf16_t *)gain, eps, H, B,
-                       (int)skip_anchor, (bf16_t *)Y);
-  else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, st, X, (const float *)gain, eps, H, B,
-                       (int)skip_anchor, (float *)Y);
-  return hipGetLastError();
+  if (is_bf16) return launch_rmsnorm_t(X, (const bf16_t *)gain, eps, rows, H, B, skip_anchor, (bf16_t *)Y, st);
+  return launch_rmsnorm_t(X, (const float *)gain, eps, rows, H, B, skip_anchor, (float *)Y, st);
 }
 
 hipError_t launch_argmax_reduce(const float *val, const int *idx, int rows, int n_groups, int *ids_out,

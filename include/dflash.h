@@ -60,8 +60,8 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
 /* Drafter shape.  Supported: head_dim in {64, 128}; n_q_heads a multiple of
  * n_kv_heads; (n_q_heads / n_kv_heads) * block_size <= 128; 2 <= block_size
- * <= 64; hidden, n_q_heads*head_dim and ffn multiples of 64; vocab a multiple
- * of 16; page_size 16; 1 <= n_layers <= 16.  The mask token is a row of the
+ * <= 64; hidden, n_q_heads*head_dim and ffn multiples of 64; hidden <= 16384;
+ * vocab a multiple of 16; page_size 16; 1 <= n_layers <= 16.  The mask token is a row of the
  * shared embedding (mask_token_id < vocab). */
 typedef struct {
     int32_t hidden;

@@ -70,7 +70,8 @@ def create(cfg):
 
 
 @pytest.mark.parametrize("bad,code", [
-    (dict(head_dim=96), -2), (dict(n_q_heads=5), -2), (dict(hidden=100), -2), (dict(ffn=100), -2),
+    (dict(head_dim=96), -2), (dict(n_q_heads=5), -2), (dict(hidden=100), -2), (dict(hidden=16384 + 64), -2),
+    (dict(ffn=100), -2),
     (dict(vocab=1000 + 3), -2), (dict(block_size=1), -2), (dict(block_size=65), -2), (dict(n_layers=0), -2),
     (dict(n_layers=17), -2), (dict(mask_token_id=1024), -4), (dict(dtype="bf16", rope_theta=0.0), -4),
     (dict(n_q_heads=32, n_kv_heads=1, block_size=16), -2),
