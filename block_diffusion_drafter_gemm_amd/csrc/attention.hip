@@ -21,6 +21,7 @@
 namespace dflash {
 
 constexpr int kSub = 64;        // keys per LDS sub-block
+constexpr int kPage = 16;       // keys per cache page (the only page size accepted)
 constexpr float kLog2e = 1.4426950408889634f;
 
 int attn_chunk(int batch, int max_ctx, int block_size, int nkv) {
@@ -135,14 +136,14 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
   uint4 pre[8];
   // page ids of the item's context keys, read once (a dependent global load per
   // key would serialise every in-flight K/V load behind it)
-  const int p0 = kbeg / a.page_size;
-  for (int i = tid; i <= (min(kend, ctx) - 1) / a.page_size - p0 && kbeg < ctx; i += 256)
+  const int p0 = kbeg / kPage;
+  for (int i = tid; i <= (min(kend, ctx) - 1) / kPage - p0 && kbeg < ctx; i += 256)
     s_pages[i] = a.block_table[(size_t)s * a.max_pages + p0 + i];
   __syncthreads();
   auto key_ptr = [&](int t, const T *ctxp, const T *blkp) -> const T * {
     if (t < ctx) {
-      const int page = s_pages[t / a.page_size - p0];
-      return ctxp + (((size_t)page * a.page_size + t % a.page_size) * a.nkv + g) * HD;
+      const int page = s_pages[t / kPage - p0];
+      return ctxp + (((size_t)page * kPage + t % kPage) * a.nkv + g) * HD;
     }
     return blkp + ((size_t)(s * B + (t - ctx)) * a.nkv + g) * HD;
   };
@@ -312,8 +313,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
 
 // One wave per (sequence, KV head, query row): combine the chunk partials.
 // Lanes fetch the chunks' (max, sum) statistics in parallel; the weighted sum
-// of the partial outputs then runs over chunks with the loads of 8 chunks in
-// flight at a time, in chunk order (deterministic).
+// of the partial outputs then runs over chunks with the loads of up to 64
+// chunks in flight at once, in chunk order (deterministic).
 template <typename T, int HD>
 __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnArgs a) {
   const int lane = threadIdx.x;
@@ -353,21 +354,20 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnArgs a) {
     // weight of chunk c0 + lane, broadcast below
     const float wl = c0 + lane < nch ? exp2f(stat(c0 + lane, 0) - M) : 0.f;
     const int cn = min(64, nch - c0);
-    for (int j0 = 0; j0 < cn; j0 += 8) {
-      float po[8][PER];
+    // all (up to 64) chunks' partial outputs in flight at once; past cn the
+    // last valid chunk is re-read and weighted 0
+    float po[64][PER];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = c0 + j0 + j;
-        const float *p = a.partial + (((size_t)(base + (c < nch ? c : 0)) * a.nkv + g) * GBP + r) * HD;
+    for (int j = 0; j < 64; ++j) {
+      const float *p = a.partial + (((size_t)(base + c0 + min(j, cn - 1)) * a.nkv + g) * GBP + r) * HD;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) po[j][e] = (j0 + j < cn) ? p[lane + 64 * e] : 0.f;
-      }
+      for (int e = 0; e < PER; ++e) po[j][e] = p[lane + 64 * e];
+    }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float w = __shfl(wl, j0 + j);
+    for (int j = 0; j < 64; ++j) {
+      const float w = j < cn ? __shfl(wl, j) : 0.f;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += w * po[j][e];
-      }
+      for (int e = 0; e < PER; ++e) acc[e] += w * po[j][e];
     }
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;

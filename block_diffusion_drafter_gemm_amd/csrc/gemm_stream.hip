@@ -85,8 +85,18 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
         if constexpr (EPI == EPI_STORE) Storage<T>::store((T *)a.out, (size_t)r * a.ldo + n, v);
         else if constexpr (EPI == EPI_STORE_F32) ((float *)a.out)[(size_t)r * a.ldo + n] = v;
         else {
+          // two separate paths: merged, the wait for the later-tile load would
+          // also stall the first tile (and drain the weights in flight)
           float *xp = a.X + (size_t)r * a.ldx + n;
-          *xp = (first ? pre.x : *xp) + v;
+          float nv;
+          if (first) {
+            nv = pre.x + v;
+            asm volatile("; residual from prefetch" : "+v"(nv));
+          } else {
+            nv = *xp + v;
+            asm volatile("; residual loaded" : "+v"(nv));
+          }
+          *xp = nv;
         }
       }
     }
@@ -178,6 +188,7 @@ struct StreamBuf {
   __device__ __forceinline__ void issue(const GemmArgs &a, const T *W, const T *arow, int t, int c0, int clast) {
     const int ln = threadIdx.x & 15, g = (threadIdx.x >> 4) & 3;
     const T *wp = W + (size_t)s_weight_row<EPI>(a, t, ln) * a.ldw + 8 * g;
+    __builtin_amdgcn_sched_barrier(0);   // loads issued before the batch stay before it
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int c = min(c0 + j, clast);
@@ -282,6 +293,9 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
     const bool have_row = r < a.M;
     const int rr = min(r, a.M - 1);
     if constexpr (AM == A_COPY) {
+      // the row goes through registers (NV 16-byte pieces per lane, all
+      // issued first, clamped source); the first weight batch is issued
+      // before the wait, so it stays in flight while the row is written to LDS
       constexpr int EPV = 16 / (int)sizeof(T);     // elements per 16-byte vector
       constexpr int NV = KR / EPV / 64;            // vectors per lane at most
       const int nvec = a.K / EPV;
@@ -296,6 +310,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
         const int i = lane + 64 * k;
         if (i < nvec) dst[i] = have_row ? cv[k] : make_uint4(0, 0, 0, 0);
       }
+      lds_barrier();
     } else {
       // lane owns the 4-element groups q4 = lane + 64 k of the row; the gain
       // is read once per workgroup (one group per thread) and parked in the
@@ -349,8 +364,8 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
           if (write_x) reinterpret_cast<float4 *>(a.X + (size_t)r * a.ldx)[q4] = xv[k];   // residual stream
         }
       }
+      lds_barrier();
     }
-    lds_barrier();
   } else {
     DF_ISSUE(bufa, 0);
   }
@@ -359,13 +374,14 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   int best_i = 0x7fffffff;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   // static ping-pong between two register buffers (dynamic selection would
-  // spill the fragments to scratch).  The next batch is issued whether or not
-  // it exists (past the end it re-reads the wave's first chunk of the
-  // workgroup's first tile, a cache hit, and is never used): with no branch
-  // around the issue, consuming one buffer waits for that buffer only.
-  // Both halves always run (no exit in the middle of the loop, which keeps
-  // the outstanding-load count identical on every path into the loop head); a
-  // second half past the end consumes the dummy batch and finishes nothing.
+  // spill the fragments to scratch): the next batch is issued before the
+  // current one is consumed.  Every batch is issued whether or not it exists
+  // (past the end it re-reads the wave's first chunk of the workgroup's first
+  // tile, a cache hit, and is never used): with no branch around the issue,
+  // consuming one buffer waits for that buffer only.  Both halves always run
+  // (no exit in the middle of the loop keeps the count of outstanding loads
+  // identical on every path into the loop head); a second half past the end
+  // consumes a dummy batch and finishes nothing.
   for (int q = 0; q < total; q += 2) {
     DF_ISSUE(bufb, q + 1);
     acc = bufa.compute(acc, arow, cbeg + (q % nb) * U, cend, clast);
