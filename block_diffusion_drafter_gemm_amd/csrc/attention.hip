@@ -68,8 +68,10 @@ __device__ void find_seq(const int *ctx_len, int batch, int B, int chunk, int f,
   *first_out = 0;
 }
 
-template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
+// TPW: query tiles (16 rows of the G*B block queries) per wave, 1 when G*B <= 64
+// (the smaller register footprint fits twice the workgroups per compute unit)
+template <typename T, int HD, int TPW>
+__global__ __launch_bounds__(256, TPW == 1 ? 4 : 2) void attn_partial_kernel(const AttnArgs a) {
   constexpr int EPV = 16 / (int)sizeof(T);      // elements per 16-byte vector
   constexpr int VPK = HD / EPV;                 // vectors per key row
   constexpr int KSTR = HD + EPV;                // LDS row stride of K (elements)
@@ -103,10 +105,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
   const float scale = kLog2e / sqrtf((float)HD);
 
   // query fragments of this wave's tiles (B operand: column = query row)
-  Frag<T> qf[2][NU];
-  bool tile_on[2];
+  Frag<T> qf[TPW][NU];
+  bool tile_on[TPW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < TPW; ++t) {
     const int qt = wave + 4 * t;
     tile_on[t] = qt < MTQ;
     const int r = qt * 16 + ln;
@@ -118,10 +120,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
       if (ok) qf[t][u].load(qp + 32 * u); else qf[t][u].zero();
     }
   }
-  f32x4 o[2][ND];
-  float m_run[2], l_run[2];
+  f32x4 o[TPW][ND];
+  float m_run[TPW], l_run[TPW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < TPW; ++t) {
     m_run[t] = -1e30f;
     l_run[t] = 0.f;
 #pragma unroll
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
       if (sub + kb2 >= kend) break;
       // V^T fragments for all d tiles (A operand: row = d, k = keys)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < TPW; ++t) {
         if (!tile_on[t]) continue;
         f32x4 st[2];
 #pragma unroll
@@ -292,7 +294,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(const AttnArgs a) {
   // partial results: O^T (lane: query row ln, d rows 4*g4..), max, sum
   const int GBP = MTQ * 16;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < TPW; ++t) {
     if (!tile_on[t]) continue;
     float l = l_run[t];
     l += __shfl_xor(l, 16);
@@ -380,7 +382,9 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnArgs a) {
 
 template <typename T, int HD>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((attn_partial_kernel<T, HD>), dim3(a.max_items), dim3(256), 0, st, a);
+  const int GBq = (a.nq / a.nkv) * a.block_size;
+  if (GBq <= 64) hipLaunchKernelGGL((attn_partial_kernel<T, HD, 1>), dim3(a.max_items), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_partial_kernel<T, HD, 2>), dim3(a.max_items), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int GB = (a.nq / a.nkv) * a.block_size;

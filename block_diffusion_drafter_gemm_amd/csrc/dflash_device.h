@@ -116,6 +116,33 @@ __device__ __forceinline__ void store4(bf16_t *p, int q4, float4 v) {
   reinterpret_cast<uint2 *>(p)[q4] = u;
 }
 
+// acc += A * B for one 32 x 32 tile and a 16-wide k-chunk (v_mfma_f32_32x32x16_bf16):
+// lane l supplies row (or column) l % 32 and k-elements 8*(l/32) .. +7, and holds
+// column l % 32, rows 8*(i/4) + 4*(l/32) + i%4 of the result in element i.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mma32(f32x16 acc, const Frag<bf16_t> &a, const Frag<bf16_t> &b) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v), __builtin_bit_cast(bf16x8, b.v),
+                                                 acc, 0, 0, 0);
+}
+
+// LDS-direct load: each lane's 16 bytes at gsrc land at LDS byte offset
+// lds_off + 16 * lane (lds_off wave-uniform).  Issued through inline assembly
+// so that the compiler does not treat later LDS reads as waiting on it (it
+// would wait for every such load in flight, not just the ones those reads
+// need); the caller waits with an explicit vmcnt.  Being invisible to the
+// compiler's counters, such loads can only make its own waits stricter.
+__device__ __forceinline__ unsigned lds_offset(const void *p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ void lds_dma16(const void *gsrc, unsigned lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(gsrc) : "memory", "m0");
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (gfx9 encoding: vmcnt split over bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their no-wait maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) & 3) << 14 | 0x7 << 4 | 0xF << 8; }
+
 __device__ __forceinline__ float f4get(const f32x4 &v, int i) {
   return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
 }
