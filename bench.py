@@ -22,6 +22,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E
+MFMA_PEAK_FLOPS = 2.5e15  # MI355X dense bf16 matrix-core peak
 METRIC = "draft-block latency (µs) + drafted tokens/s, Qwen3-8B-shape B=16; % HBM peak"
 
 
@@ -65,6 +66,26 @@ KERNEL_SOURCES = ["block_diffusion_drafter_gemm_amd/csrc/gemm_stream.hip",
                   "block_diffusion_drafter_gemm_amd/csrc/dflash_device.h"]
 
 
+def read_stream_gbs(torch, nbytes=1 << 30, reps=10):
+    """Read bandwidth of the library's plain streaming-read kernel over 1 GiB on
+    this GPU, the practical ceiling of an HBM-bound step."""
+    from block_diffusion_drafter_gemm_amd import _lib as L
+    x = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        L.dflash_stream_read(x, sink)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        L.dflash_stream_read(x, sink)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (a.elapsed_time(b) / 1e3) / 1e9
+    del x
+    return gbs
+
+
 def recorded_traffic():
     """HBM bytes per LM-head launch from the committed counter summary, or None
     when the kernel sources changed since the counters were taken."""
@@ -106,8 +127,20 @@ def cpu_baseline(cfg, w, Kp, Vp, lay, lens, anchors, y, min_seconds=10.0, max_st
         D.accept_len(ids, y[0])
         steps += 1
     dt = time.perf_counter() - t0
+    # one more step on a single host thread
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            Z = D.draft_block(w, cfg, int(anchors[0]), Kc, Vc)
+            D.lm_argmax(w["lm_head"], Z)
+            d1 = time.perf_counter() - t1
+        single = {"value": round((cfg.block_size - 1) / d1, 3), "seconds": round(d1, 2)}
+    except ImportError:
+        pass
     return {"value": round(steps * (cfg.block_size - 1) / dt, 3), "unit": "drafted tokens/s",
-            "cores": int(cores), "kind": "oracle", "seconds": round(dt, 2),
+            "cores": int(cores), "kind": "oracle", "seconds": round(dt, 2), "single_thread": single,
             "sample": f"{steps} draft steps of sequence 0 ({cfg.block_size - 1} drafted tokens each, context "
                       f"{int(lens[0])}) in float64 numpy"}
 
@@ -202,6 +235,7 @@ def main():
     assert np.array_equal(ids.cpu().numpy().reshape(b, B - 1), d0), "drafts changed between steps"
 
     graph_ms = None
+    graph_step_ms = None
     if not args.no_graph:
         g = torch.cuda.CUDAGraph()
         s2 = torch.cuda.Stream()
@@ -220,15 +254,23 @@ def main():
         torch.cuda.synchronize()
         ids.zero_()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
         g0.record()
-        for _ in range(K):
+        gev[0].record()
+        for i in range(K):
             g.replay()
+            gev[i + 1].record()
         g1.record()
         torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / K
+        graph_step_ms = np.array([gev[i].elapsed_time(gev[i + 1]) for i in range(K)])
         assert np.array_equal(ids.cpu().numpy().reshape(b, B - 1), d0), "graph replay drafts differ from eager"
 
     ms = graph_ms if graph_ms is not None else eager_ms
+    per_step = graph_step_ms if graph_step_ms is not None else draft_ms + lm_ms
+    pct = {"median_ms": round(float(np.median(per_step)), 4), "p10_ms": round(float(np.percentile(per_step, 10)), 4),
+           "p90_ms": round(float(np.percentile(per_step, 90)), 4)}
+    stream_gbs = read_stream_gbs(torch)
     layers_b, lm_b, kv_b, emb_b = step_bytes(cfg, lens)
     total_b = layers_b + lm_b + kv_b + emb_b
     gemm_f, lm_f, attn_f = step_flops(cfg, lens)
@@ -256,8 +298,12 @@ def main():
                  "draft_block_ms": round(float(np.mean(draft_ms)), 4),
                  "lmhead_ms": round(float(np.mean(lm_ms)), 4),
                  "algorithmic_bytes": int(total_b), "algorithmic_flops": int(gemm_f + lm_f + attn_f),
+                 **pct,
                  "hbm_gbs": round(total_b / (ms / 1e3) / 1e9, 1),
-                 "hbm_frac": round(total_b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+                 "hbm_frac": round(total_b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "read_stream_gbs": round(stream_gbs, 1),
+                 "hbm_frac_of_read_stream": round(total_b / (ms / 1e3) / 1e9 / stream_gbs, 4),
+                 "mfma_frac_step": round((gemm_f + lm_f) / (ms / 1e3) / MFMA_PEAK_FLOPS, 4)},
         "roofline": {"kernel": "lmhead_argmax (vocabulary GEMM with argmax epilogue + argmax reduce)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -278,6 +324,24 @@ def main():
         i1.record()
         torch.cuda.synchronize()
         out["inject_steady_ms"] = round(i0.elapsed_time(i1) / K, 4)
+        out["cycle_ms"] = round(ms + out["inject_steady_ms"], 4)
+        # prefill injection: every context position of the first sequence at once
+        T = int(lens[0])
+        fp = R.to_device(S.features(cfg, T, seed=2))
+        sp = torch.zeros(T, dtype=torch.int32, device="cuda")
+        pp = torch.arange(T, dtype=torch.int32, device="cuda")
+        drp = R.Drafter(cfg, w, max_batch=b, max_ctx=int(lens.max()), max_new=T)
+        drp.inject_context(fp, sp, pp, kv)
+        torch.cuda.synchronize()
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record()
+        for _ in range(3):
+            drp.inject_context(fp, sp, pp, kv)
+        p1.record()
+        torch.cuda.synchronize()
+        out["inject_prefill_ms"] = round(p0.elapsed_time(p1) / 3, 4)
+        out["inject_prefill_positions"] = T
+        drp.close()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, w, Kp, Vp, lay, lens, anchors, y)
     dr.close()

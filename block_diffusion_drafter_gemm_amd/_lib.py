@@ -19,7 +19,7 @@ DFLASH_F32, DFLASH_BF16 = 0, 1
 
 EXPORTS = ("dflash_create", "dflash_destroy", "dflash_workspace_size", "dflash_workspace_init",
            "dflash_inject_context", "dflash_draft_block", "dflash_lmhead_argmax", "dflash_accept_len",
-           "dflash_status_str")
+           "dflash_stream_read", "dflash_status_str")
 
 
 class DflashError(RuntimeError):
@@ -72,6 +72,7 @@ def load() -> ctypes.CDLL:
     lib.dflash_draft_block.argtypes = [vp, vp, ctypes.POINTER(DflashKV), vp, vp, sz, vp]
     lib.dflash_lmhead_argmax.argtypes = [vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.dflash_accept_len.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    lib.dflash_stream_read.argtypes = [vp, sz, vp, vp]
     lib.dflash_status_str.argtypes = [ctypes.c_int]
     lib.dflash_status_str.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -181,3 +182,10 @@ def make_weights(embed, lm_head, w_fc, final_norm, attn_norm: Sequence, w_qkv: S
 def make_kv(k, v, block_table, ctx_len, batch: int, max_pages: int, n_pages: int, max_ctx: int) -> DflashKV:
     return DflashKV(k.data_ptr(), v.data_ptr(), block_table.data_ptr(), ctx_len.data_ptr(), batch, max_pages,
                     n_pages, max_ctx)
+
+
+def dflash_stream_read(src, sink, stream: Optional[int] = None) -> None:
+    """Streaming read of the whole of ``src`` (device tensor), XOR-folded into
+    ``sink`` (one int32 on the device, zeroed by the caller)."""
+    _check(load().dflash_stream_read(ptr(src), src.numel() * src.element_size(), ptr(sink),
+                                     current_stream() if stream is None else stream), "dflash_stream_read")

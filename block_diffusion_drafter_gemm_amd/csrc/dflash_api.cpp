@@ -495,4 +495,15 @@ int dflash_accept_len(const int32_t *draft_ids, const int32_t *target_ids, int32
              : DFLASH_ERR_HIP;
 }
 
+int dflash_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+  if (!src || !sink) return DFLASH_ERR_NULL;
+  if (bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16) return DFLASH_ERR_SHAPE;
+  if (bytes == 0) return DFLASH_OK;
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || n_cu <= 0)
+    n_cu = 256;
+  return launch_stream_read(src, bytes, sink, n_cu, (hipStream_t)stream) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
 }  // extern "C"

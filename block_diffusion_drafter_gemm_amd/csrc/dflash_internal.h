@@ -102,5 +102,6 @@ hipError_t launch_argmax_reduce(const float *val, const int *idx, int rows, int 
 hipError_t launch_accept(const int *draft, const int *target, int batch, int block_size, int *tau, int *bonus,
                          hipStream_t st);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int n_cu, hipStream_t st);
 
 }  // namespace dflash

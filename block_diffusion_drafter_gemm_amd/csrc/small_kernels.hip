@@ -159,6 +159,37 @@ hipError_t launch_accept(const int *draft, const int *target, int batch, int B, 
   return hipGetLastError();
 }
 
+// Plain streaming read: each thread keeps 8 16-byte loads in flight per
+// iteration (clamped addresses, out-of-range words masked), XOR-folds them and
+// one lane per wave folds its wave's result into *sink.
+constexpr int kReadThreads = 1024, kReadUnroll = 8;
+
+__global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const uint4 *src, size_t n16, uint32_t *sink) {
+  unsigned acc = 0;
+  const size_t step = (size_t)gridDim.x * kReadThreads * kReadUnroll;
+  for (size_t base = (size_t)blockIdx.x * kReadThreads * kReadUnroll + threadIdx.x; base < n16; base += step) {
+    uint4 v[kReadUnroll];
+#pragma unroll
+    for (int j = 0; j < kReadUnroll; ++j) v[j] = src[min(base + (size_t)j * kReadThreads, n16 - 1)];
+#pragma unroll
+    for (int j = 0; j < kReadUnroll; ++j)
+      if (base + (size_t)j * kReadThreads < n16) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) atomicXor(sink, acc);
+}
+
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int n_cu, hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + (size_t)kReadThreads * kReadUnroll - 1) / ((size_t)kReadThreads * kReadUnroll);
+  if (blocks > (size_t)n_cu) blocks = n_cu;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(kReadThreads), 0, st, (const uint4 *)src, n16,
+                     sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st) {
   const size_t n16 = bytes / 16;
   if (n16 == 0) return hipSuccess;

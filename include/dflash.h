@@ -173,6 +173,16 @@ int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int3
 int dflash_accept_len(const int32_t *draft_ids, const int32_t *target_ids, int32_t batch, int32_t block_size,
                       int32_t *accept_len_out, int32_t *bonus_out, void *stream);
 
+/* Streaming read of `bytes` bytes at `src` (device, 16-byte aligned, bytes a
+ * multiple of 16): every 32-bit word is XOR-folded into *sink (device, one
+ * uint32 the caller zeroes first).  Not a step of the method: it measures the
+ * read bandwidth that bounds the draft step, which [FN] (introduction and
+ * section 1) describes as memory-bound, i.e. timed by moving weights and KV
+ * through memory; a step's bytes/s are reported against it.
+ * Errors: NULL pointers (DFLASH_ERR_NULL), a misaligned `src` or a size that
+ * is not a multiple of 16 (DFLASH_ERR_SHAPE).  bytes == 0 enqueues nothing. */
+int dflash_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *dflash_status_str(int status);
 

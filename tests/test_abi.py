@@ -135,3 +135,12 @@ def test_accept_len_host_validation(lib):
     assert lib.dflash_accept_len(None, FAKE, 4, 16, FAKE, FAKE, None) == -1
     assert lib.dflash_accept_len(FAKE, FAKE, -1, 16, FAKE, FAKE, None) == -2
     assert lib.dflash_accept_len(None, None, 0, 16, None, None, None) == 0
+
+
+def test_stream_read_validation(lib):
+    # host-side checks only: nothing is launched on these paths
+    assert lib.dflash_stream_read(None, 16, FAKE, None) == -1
+    assert lib.dflash_stream_read(FAKE, 16, None, None) == -1
+    assert lib.dflash_stream_read(FAKE, 24, FAKE, None) == -2      # not a multiple of 16
+    assert lib.dflash_stream_read(FAKE + 8, 16, FAKE, None) == -2  # misaligned
+    assert lib.dflash_stream_read(FAKE, 0, FAKE, None) == 0        # empty: no-op

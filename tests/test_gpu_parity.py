@@ -243,3 +243,19 @@ def test_lossless_speculative_decoding_with_gpu_drafter(seed, layer_std):
     assert np.array_equal(s2, g)
     log(f"  taus gpu {taus} oracle {taus2}")
     gd.d.close()
+
+
+# ----------------------------------------------------------------------------
+# streaming-read helper (measures the read ceiling the draft step is reported against)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("n16", [1, 1000, 8192 * 3 + 77])
+def test_stream_read_folds_every_word(n16):
+    log(f"stream_read n16={n16}")
+    from block_diffusion_drafter_gemm_amd import _lib
+    rng = np.random.default_rng(n16)
+    words = rng.integers(0, 2 ** 31 - 1, size=4 * n16, dtype=np.int64).astype(np.int32)
+    x = torch.from_numpy(words).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _lib.dflash_stream_read(x, sink)
+    torch.cuda.synchronize()
+    assert int(sink.cpu().numpy()[0]) == int(np.bitwise_xor.reduce(words))
