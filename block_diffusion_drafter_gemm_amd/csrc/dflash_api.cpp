@@ -95,9 +95,11 @@ InjectLayout inject_layout(const dflash_handle_s *h, int n_new) {
 }
 
 // Fill the launch geometry of ``a`` and launch: the LDS-tiled kernel for many
-// rows (bf16), otherwise the few-rows kernel.
+// rows (bf16), and for 17..64 rows when its 128-row tiles still number at least
+// 64 (wide outputs: LM head, gate/up); otherwise the few-rows kernel.
 int launch(const dflash_handle_s *h, Epilogue epi, GemmArgs &a, int z, hipStream_t st) {
-  if (h->bf16 && a.M > 64 && gemm_tiled_ok(epi, a.N, a.K, a.ffn, a.hd)) {
+  const bool tiled_ok = h->bf16 && gemm_tiled_ok(epi, a.N, a.K, a.ffn, a.hd);
+  if (tiled_ok && (a.M > 64 || (a.M > 16 && gemm_tiled_cols(epi, a.N, a.ffn) * z >= 64))) {
     a.m_groups = 1;
     a.n_groups = gemm_tiled_cols(epi, a.N, a.ffn);
     return launch_gemm_tiled(epi, a, z, st) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;

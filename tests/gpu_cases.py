@@ -49,6 +49,11 @@ MINI = {
     "mini_port": mini("mini_port", 106, dtype="bf16", hidden=256, n_q_heads=2, n_kv_heads=1, head_dim=128,
                       ffn=4352, vocab=1040, n_layers=2, n_feat_layers=17, block_size=8, batch=2,
                       ctx_min=30, ctx_max=200, rope_theta=1e6),
+    # 48 block rows with wide outputs (FFN 4096, vocabulary 66 x 128): gate/up and
+    # the LM head take the many-rows (LDS-tiled) GEMM below 65 rows
+    "mini_wide": mini("mini_wide", 107, dtype="bf16", hidden=256, n_q_heads=2, n_kv_heads=2, head_dim=128,
+                      ffn=4096, vocab=8448, n_layers=2, n_feat_layers=2, block_size=16, batch=3,
+                      ctx_min=20, ctx_max=180, rope_theta=1e6),
     "tiny": S.get_config("tiny"),
 }
 

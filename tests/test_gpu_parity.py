@@ -62,7 +62,8 @@ def test_accept_len(B):
 # A9 LM head + argmax
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("name,rows", [(n, r) for n in ["tiny", "mini_bf16", "mini_f32", "mini_b10"]
-                                       for r in [1, 15, 33, 70]] + [("mini_b8", r) for r in [65, 130, 300]])
+                                       for r in [1, 15, 33, 70]] + [("mini_b8", r) for r in [65, 130, 300]]
+                         + [("mini_wide", r) for r in [20, 47]])
 def test_lmhead_argmax(name, rows):
     cfg = MINI[name]
     log(f"lmhead_argmax {name} rows={rows}")
@@ -161,7 +162,8 @@ def run_draft_case(cfg, seed=0, lens=None, check_seqs=None):
     return hid_h, ids_h
 
 
-@pytest.mark.parametrize("name", ["tiny", "mini_bf16", "mini_b10", "mini_d64", "mini_f32", "mini_b8", "mini_port"])
+@pytest.mark.parametrize("name", ["tiny", "mini_bf16", "mini_b10", "mini_d64", "mini_f32", "mini_b8", "mini_port",
+                                  "mini_wide"])
 def test_draft_block(name):
     log(f"draft_block {name}")
     run_draft_case(MINI[name], seed=0)
