@@ -68,10 +68,12 @@ __device__ void find_seq(const int *ctx_len, int batch, int B, int chunk, int f,
   *first_out = 0;
 }
 
-// TPW: query tiles (16 rows of the G*B block queries) per wave, 1 when G*B <= 64
-// (the smaller register footprint fits twice the workgroups per compute unit)
-template <typename T, int HD, int TPW>
-__global__ __launch_bounds__(256, TPW == 1 ? 4 : 2) void attn_partial_kernel(const AttnArgs a) {
+// NW waves per workgroup, one per 16-row tile of the G*B block queries (4 for
+// G*B <= 64, 8 for G*B <= 128); the first 256 threads stage K and V.  One tile
+// per wave keeps the register footprint small enough for 16 waves per CU.
+template <typename T, int HD, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(const AttnArgs a) {
+  constexpr int NT = NW * 64;
   constexpr int EPV = 16 / (int)sizeof(T);      // elements per 16-byte vector
   constexpr int VPK = HD / EPV;                 // vectors per key row
   constexpr int KSTR = HD + EPV;                // LDS row stride of K (elements)
@@ -105,11 +107,11 @@ __global__ __launch_bounds__(256, TPW == 1 ? 4 : 2) void attn_partial_kernel(con
   const float scale = kLog2e / sqrtf((float)HD);
 
   // query fragments of this wave's tiles (B operand: column = query row)
-  Frag<T> qf[TPW][NU];
-  bool tile_on[TPW];
+  Frag<T> qf[1][NU];
+  bool tile_on[1];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int qt = wave + 4 * t;
+  for (int t = 0; t < 1; ++t) {
+    const int qt = wave;
     tile_on[t] = qt < MTQ;
     const int r = qt * 16 + ln;
     const bool ok = tile_on[t] && r < GB;
@@ -120,10 +122,10 @@ __global__ __launch_bounds__(256, TPW == 1 ? 4 : 2) void attn_partial_kernel(con
       if (ok) qf[t][u].load(qp + 32 * u); else qf[t][u].zero();
     }
   }
-  f32x4 o[TPW][ND];
-  float m_run[TPW], l_run[TPW];
+  f32x4 o[1][ND];
+  float m_run[1], l_run[1];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
+  for (int t = 0; t < 1; ++t) {
     m_run[t] = -1e30f;
     l_run[t] = 0.f;
 #pragma unroll
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(256, TPW == 1 ? 4 : 2) void attn_partial_kernel(con
   // page ids of the item's context keys, read once (a dependent global load per
   // key would serialise every in-flight K/V load behind it)
   const int p0 = kbeg / kPage;
-  for (int i = tid; i <= (min(kend, ctx) - 1) / kPage - p0 && kbeg < ctx; i += 256)
+  for (int i = tid; i <= (min(kend, ctx) - 1) / kPage - p0 && kbeg < ctx; i += NT)
     s_pages[i] = a.block_table[(size_t)s * a.max_pages + p0 + i];
   __syncthreads();
   auto key_ptr = [&](int t, const T *ctxp, const T *blkp) -> const T * {
@@ -150,6 +152,7 @@ __global__ __launch_bounds__(256, TPW == 1 ? 4 : 2) void attn_partial_kernel(con
     return blkp + ((size_t)(s * B + (t - ctx)) * a.nkv + g) * HD;
   };
   auto load_sub = [&](int sub) {
+    if (tid >= 256) return;
     if constexpr (sizeof(T) == 2) {
       if (tid < 128) {
 #pragma unroll
@@ -170,6 +173,7 @@ __global__ __launch_bounds__(256, TPW == 1 ? 4 : 2) void attn_partial_kernel(con
     }
   };
   auto store_sub = [&](int sub) {
+    if (tid >= 256) return;
     if constexpr (sizeof(T) == 2) {
       if (tid < 128) {
 #pragma unroll
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(256, TPW == 1 ? 4 : 2) void attn_partial_kernel(con
       if (sub + kb2 >= kend) break;
       // V^T fragments for all d tiles (A operand: row = d, k = keys)
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
+      for (int t = 0; t < 1; ++t) {
         if (!tile_on[t]) continue;
         f32x4 st[2];
 #pragma unroll
@@ -294,12 +298,12 @@ __global__ __launch_bounds__(256, TPW == 1 ? 4 : 2) void attn_partial_kernel(con
   // partial results: O^T (lane: query row ln, d rows 4*g4..), max, sum
   const int GBP = MTQ * 16;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
+  for (int t = 0; t < 1; ++t) {
     if (!tile_on[t]) continue;
     float l = l_run[t];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    const int r = (wave + 4 * t) * 16 + ln;
+    const int r = wave * 16 + ln;
     if (r >= GB) continue;
     float *po = a.partial + ((size_t)item * GBP + r) * HD;
 #pragma unroll
@@ -383,8 +387,8 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnArgs a) {
 template <typename T, int HD>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   const int GBq = (a.nq / a.nkv) * a.block_size;
-  if (GBq <= 64) hipLaunchKernelGGL((attn_partial_kernel<T, HD, 1>), dim3(a.max_items), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((attn_partial_kernel<T, HD, 2>), dim3(a.max_items), dim3(256), 0, st, a);
+  if (GBq <= 64) hipLaunchKernelGGL((attn_partial_kernel<T, HD, 4>), dim3(a.max_items), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((attn_partial_kernel<T, HD, 8>), dim3(a.max_items), dim3(512), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int GB = (a.nq / a.nkv) * a.block_size;

@@ -54,6 +54,10 @@ MINI = {
     "mini_wide": mini("mini_wide", 107, dtype="bf16", hidden=256, n_q_heads=2, n_kv_heads=2, head_dim=128,
                       ffn=4096, vocab=8448, n_layers=2, n_feat_layers=2, block_size=16, batch=3,
                       ctx_min=20, ctx_max=180, rope_theta=1e6),
+    # 8 query heads per KV head x B 16 = 128 block queries per KV head (8 query tiles)
+    "mini_g8": mini("mini_g8", 108, dtype="bf16", hidden=512, n_q_heads=8, n_kv_heads=1, head_dim=128,
+                    ffn=512, vocab=1040, n_layers=2, n_feat_layers=2, block_size=16, batch=2,
+                    ctx_min=10, ctx_max=260, rope_theta=1e6),
     "tiny": S.get_config("tiny"),
 }
 
