@@ -25,12 +25,12 @@ constexpr int kPage = 16;       // keys per cache page (the only page size accep
 constexpr float kLog2e = 1.4426950408889634f;
 
 int attn_chunk(int batch, int max_ctx, int block_size, int nkv) {
-  // aim for a few items per compute unit; chunk in [64, 1024] keys, multiple of 64
+  // aim for a few items per compute unit; chunk in [64, 512] keys, multiple of 64
   const long keys = (long)batch * (max_ctx + block_size) * nkv;
   long c = keys / 1024;
   c = (c + kSub - 1) / kSub * kSub;
   if (c < kSub) c = kSub;
-  if (c > 1024) c = 1024;
+  if (c > 512) c = 512;
   return (int)c;
 }
 
@@ -319,9 +319,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
 
 // One wave per (sequence, KV head, query row): combine the chunk partials.
 // Lanes fetch the chunks' (max, sum) statistics in parallel; the weighted sum
-// of the partial outputs then runs over chunks with the loads of up to 64
-// chunks in flight at once, in chunk order (deterministic).
-template <typename T, int HD>
+// of the partial outputs then runs over chunks with the loads of DEPTH chunks
+// in flight at once, in chunk order (deterministic).  DEPTH is sized to the
+// most chunks a sequence can have, so short chunk lists do not re-read.
+template <typename T, int HD, int DEPTH>
 __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnArgs a) {
   const int lane = threadIdx.x;
   const int B = a.block_size, G = a.nq / a.nkv, GB = G * B;
@@ -356,21 +357,21 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnArgs a) {
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int c0 = 0; c0 < nch; c0 += 64) {
+  for (int c0 = 0; c0 < nch; c0 += DEPTH) {
     // weight of chunk c0 + lane, broadcast below
     const float wl = c0 + lane < nch ? exp2f(stat(c0 + lane, 0) - M) : 0.f;
-    const int cn = min(64, nch - c0);
-    // all (up to 64) chunks' partial outputs in flight at once; past cn the
-    // last valid chunk is re-read and weighted 0
-    float po[64][PER];
+    const int cn = min(DEPTH, nch - c0);
+    // DEPTH chunks' partial outputs in flight at once; past cn the last valid
+    // chunk is re-read (a cache hit) and weighted 0
+    float po[DEPTH][PER];
 #pragma unroll
-    for (int j = 0; j < 64; ++j) {
+    for (int j = 0; j < DEPTH; ++j) {
       const float *p = a.partial + (((size_t)(base + c0 + min(j, cn - 1)) * a.nkv + g) * GBP + r) * HD;
 #pragma unroll
       for (int e = 0; e < PER; ++e) po[j][e] = p[lane + 64 * e];
     }
 #pragma unroll
-    for (int j = 0; j < 64; ++j) {
+    for (int j = 0; j < DEPTH; ++j) {
       const float w = j < cn ? __shfl(wl, j) : 0.f;
 #pragma unroll
       for (int e = 0; e < PER; ++e) acc[e] += w * po[j][e];
@@ -392,7 +393,11 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int GB = (a.nq / a.nkv) * a.block_size;
-  hipLaunchKernelGGL((attn_merge_kernel<T, HD>), dim3(a.batch * a.nkv * GB), dim3(64), 0, st, a);
+  const int max_chunks = a.max_items / (a.batch * a.nkv);
+  if (max_chunks <= 16)
+    hipLaunchKernelGGL((attn_merge_kernel<T, HD, 16>), dim3(a.batch * a.nkv * GB), dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<T, HD, 64>), dim3(a.batch * a.nkv * GB), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -134,8 +134,21 @@ __device__ __forceinline__ f32x16 mma32(f32x16 acc, const Frag<bf16_t> &a, const
 __device__ __forceinline__ unsigned lds_offset(const void *p) {
   return (unsigned)(size_t)(const __attribute__((address_space(3))) void *)p;
 }
+// M0 carries the LDS base.  An SALU write of M0 needs one wait state before an
+// LDS-DMA load reads it (a hazard the compiler cannot see inside asm), and M0
+// is a reserved register the compiler may hold a value in, so it is saved and
+// restored around the load.
 __device__ __forceinline__ void lds_dma16(const void *gsrc, unsigned lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(gsrc) : "memory", "m0");
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_off), "v"(gsrc)
+      : "memory");
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
