@@ -40,7 +40,7 @@ struct Carve {
 
 // ---- draft_block layout --------------------------------------------------
 struct DraftLayout {
-  size_t X, Y, Q, Kb, Vb, O, Hs, attn_part, attn_stats, total;
+  size_t X, Y, Q, Kb, Vb, O, Hs, attn_part, attn_stats, gemm_part, gemm_part_bytes, total;
   int chunk, max_items;
 };
 
@@ -62,6 +62,10 @@ DraftLayout draft_layout(const dflash_handle_s *h, int batch, int max_ctx) {
   const int GB = (c.n_q_heads / c.n_kv_heads) * B, GBP = (GB + 15) / 16 * 16;
   L.attn_part = cv.take((size_t)L.max_items * GBP * c.head_dim * 4);
   L.attn_stats = cv.take((size_t)L.max_items * GBP * 2 * 4);
+  // split-K partials of the residual projections (O, down) of the many-rows
+  // path: up to 4 fp32 slices of [R, hidden]
+  L.gemm_part_bytes = R > 64 ? (size_t)4 * R * c.hidden * 4 : 0;
+  L.gemm_part = cv.take(L.gemm_part_bytes);
   L.total = cv.off;
   return L;
 }
@@ -94,6 +98,8 @@ InjectLayout inject_layout(const dflash_handle_s *h, int n_new) {
   return L;
 }
 
+int compute_units(dflash_handle_s *h);
+
 // Fill the launch geometry of ``a`` and launch: the LDS-tiled kernel for many
 // rows (bf16), and for 17..64 rows when its 128-row tiles still number at least
 // 64 (wide outputs: LM head, gate/up); otherwise the few-rows kernel.
@@ -102,7 +108,9 @@ int launch(const dflash_handle_s *h, Epilogue epi, GemmArgs &a, int z, hipStream
   if (tiled_ok && (a.M > 64 || (a.M > 16 && gemm_tiled_cols(epi, a.N, a.ffn) * z >= 64))) {
     a.m_groups = 1;
     a.n_groups = gemm_tiled_cols(epi, a.N, a.ffn);
-    return launch_gemm_tiled(epi, a, z, st) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+    return launch_gemm_tiled(epi, a, z, compute_units(const_cast<dflash_handle_s *>(h)), st) == hipSuccess
+               ? DFLASH_OK
+               : DFLASH_ERR_HIP;
   }
   const int MP = gemm_rows_per_group(a.M);
   a.m_groups = (a.M + MP - 1) / MP;
@@ -391,6 +399,8 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     o.K = qd;
     o.X = X;
     o.ldx = c.hidden;
+    o.part = L.gemm_part_bytes ? reinterpret_cast<float *>(w + L.gemm_part) : nullptr;
+    o.part_bytes = L.gemm_part_bytes;
     // one tile per workgroup: activation fragments read straight from L2 beat
     // staging the rows through LDS first
     st = fast ? launch_stream(h, EPI_RESID, AM_GLOBAL, o, 1, s) : launch(h, EPI_RESID, o, 1, s);
@@ -433,6 +443,8 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     dn.K = c.ffn;
     dn.X = X;
     dn.ldx = c.hidden;
+    dn.part = o.part;
+    dn.part_bytes = o.part_bytes;
     st = fast ? launch_stream(h, EPI_RESID, c.ffn <= KR ? AM_COPY : AM_PORTION, dn, 1, s)
               : launch(h, EPI_RESID, dn, 1, s);
     if (st != DFLASH_OK) return st;

@@ -53,6 +53,11 @@ struct GemmArgs {
   const void *embed;
   const int *anchor;
   int mask_id;
+  // split-K of the LDS-tiled GEMM: fp32 partial tiles [split][M][n_groups*128]
+  // (NULL: no split), bytes available there, K elements per split
+  float *part;
+  size_t part_bytes;
+  int kper;
 };
 
 // Launch a skinny GEMM; ``z_slices`` = number of weight slices (layers) in the
@@ -77,7 +82,7 @@ int stream_res_k(bool is_bf16);
 // LDS-tiled GEMM for many rows (bf16, 128 x 128 x 64 tiles).
 bool gemm_tiled_ok(Epilogue epi, int N, int K, int ffn, int hd);
 int gemm_tiled_cols(Epilogue epi, int N, int ffn);
-hipError_t launch_gemm_tiled(Epilogue epi, const GemmArgs &a, int z_slices, hipStream_t st);
+hipError_t launch_gemm_tiled(Epilogue epi, GemmArgs &a, int z_slices, int cu, hipStream_t st);
 
 struct AttnArgs {
   const void *q;          // [R, nq*hd]

@@ -36,6 +36,10 @@ constexpr int kTBN = 128, kTBK = 64;
 constexpr int kTRow = kTBK * 2;                          // bytes per staged row (64 bf16)
 constexpr int kTCStride = kTBN + 4;                      // floats per epilogue row
 constexpr int kTStages = 3;
+#ifndef DF_BIG_MIN_TILES
+#define DF_BIG_MIN_TILES 160
+#endif
+constexpr int kBigMinTiles = DF_BIG_MIN_TILES;   // 256 x 256 tiles from this many tiles on
 
 template <int BM> struct TCfg {
   static constexpr int waves = BM / 64 * 2;
@@ -53,10 +57,10 @@ __device__ __forceinline__ int t_weight_row(const GemmArgs &a, int cb, int c) {
   return cb * kTBN + c;
 }
 
-template <int EPI, int BM>
+// Epilogue of a BM x 128 fp32 tile in LDS (row stride kTCStride), run by NT threads.
+template <int EPI, int BM, int NT>
 __device__ void t_epilogue(const GemmArgs &a, const float *ct, int rb, int cb, int layer) {
   using T = bf16_t;
-  constexpr int NT = TCfg<BM>::threads;
   const int tid = threadIdx.x;
   const int row0 = rb * BM;
   if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_F32 || EPI == EPI_RESID) {
@@ -122,21 +126,24 @@ __device__ void t_epilogue(const GemmArgs &a, const float *ct, int rb, int cb, i
     }
   } else if constexpr (EPI == EPI_ARGMAX) {
     // 2 threads per row, 64 columns each; lowest column on ties
-    const int r = tid >> 1, h = tid & 1, row = row0 + r;
-    float best = -INFINITY;
-    int bc = 0x7fffffff;
-    if (row < a.M) {
-      for (int c = h * 64; c < h * 64 + 64; ++c) {
-        const float v = ct[r * kTCStride + c];
-        if (v > best) { best = v; bc = c; }
+    static_assert(BM % (NT / 2) == 0, "whole passes of NT / 2 rows");
+    for (int r0 = 0; r0 < BM; r0 += NT / 2) {
+      const int r = r0 + (tid >> 1), h = tid & 1, row = row0 + r;
+      float best = -INFINITY;
+      int bc = 0x7fffffff;
+      if (row < a.M) {
+        for (int c = h * 64; c < h * 64 + 64; ++c) {
+          const float v = ct[r * kTCStride + c];
+          if (v > best) { best = v; bc = c; }
+        }
       }
-    }
-    const float ob = __shfl_xor(best, 1);
-    const int oc = __shfl_xor(bc, 1);
-    if (ob > best || (ob == best && oc < bc)) { best = ob; bc = oc; }
-    if (h == 0 && row < a.M) {
-      a.amax_val[(size_t)row * a.n_groups + cb] = best;
-      a.amax_idx[(size_t)row * a.n_groups + cb] = cb * kTBN + bc;
+      const float ob = __shfl_xor(best, 1);
+      const int oc = __shfl_xor(bc, 1);
+      if (ob > best || (ob == best && oc < bc)) { best = ob; bc = oc; }
+      if (h == 0 && row < a.M) {
+        a.amax_val[(size_t)row * a.n_groups + cb] = best;
+        a.amax_idx[(size_t)row * a.n_groups + cb] = cb * kTBN + bc;
+      }
     }
   }
 }
@@ -156,6 +163,7 @@ __global__ __launch_bounds__(TCfg<BM>::threads) void gemm_tiled_kernel(const Gem
   const T *A = (const T *)a.A;
   const T *W = (const T *)a.W[layer];
   const int row0 = rb * BM;
+  const int kz = blockIdx.z, kbase = kz * a.kper;        // split-K: this workgroup's K range
 
   // LDS-direct staging: piece q of a stage covers staged rows 8q .. 8q+7
   // (A rows first, then W rows); this lane fills row 8q + lane/8, slot lane%8
@@ -164,10 +172,10 @@ __global__ __launch_bounds__(TCfg<BM>::threads) void gemm_tiled_kernel(const Gem
   for (int i = 0; i < C::per_wave; ++i) {
     const int q = wave * C::per_wave + i, r = 8 * q + (lane >> 3);
     const int chunk = (lane & 7) ^ ((r >> 1) & 7);
-    src[i] = r < BM ? A + (size_t)min(row0 + r, a.M - 1) * a.lda + chunk * 8
-                    : W + (size_t)t_weight_row<EPI>(a, cb, r - BM) * a.ldw + chunk * 8;
+    src[i] = (r < BM ? A + (size_t)min(row0 + r, a.M - 1) * a.lda
+                     : W + (size_t)t_weight_row<EPI>(a, cb, r - BM) * a.ldw) + kbase + chunk * 8;
   }
-  const int nk = a.K / kTBK;
+  const int nk = a.kper / kTBK;
   // stage kt (clamped to the last k-step: past the end the loads are repeated
   // into a free buffer and never read)
   const unsigned lds0 = lds_offset(lds);
@@ -232,7 +240,217 @@ __global__ __launch_bounds__(TCfg<BM>::threads) void gemm_tiled_kernel(const Gem
       for (int e = 0; e < 16; ++e)
         ct[(wr * 64 + i * 32 + 8 * (e / 4) + 4 * fk + e % 4) * kTCStride + wc * 64 + j * 32 + fr] = acc[i][j][e];
   __syncthreads();
-  t_epilogue<EPI, BM>(a, ct, rb, cb, layer);
+  if (gridDim.z > 1) {
+    // split-K: the raw fp32 tile goes to this split's partial slice
+    const int np = a.n_groups * kTBN;
+    for (int i = tid; i < BM * kTBN / 4; i += C::threads) {
+      const int r = i / (kTBN / 4), c4 = i % (kTBN / 4), row = row0 + r;
+      if (row < a.M)
+        *reinterpret_cast<float4 *>(a.part + ((size_t)kz * a.M + row) * np + cb * kTBN + 4 * c4) =
+            *reinterpret_cast<const float4 *>(ct + r * kTCStride + 4 * c4);
+    }
+    return;
+  }
+  t_epilogue<EPI, BM, C::threads>(a, ct, rb, cb, layer);
+}
+
+// Split-K reduction of a residual projection: X += p_0 + p_1 + ... (summed in
+// split order, so deterministic), streamed as float4 over [M, N].
+template <int S>
+__global__ __launch_bounds__(256) void gemm_splitk_resid_kernel(const GemmArgs a) {
+  const int n4 = a.N / 4;
+  const size_t slice = (size_t)a.M * a.N;
+  const int total = a.M * n4;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
+    const int row = i / n4, c = 4 * (i - row * n4);
+    float4 p[S];
+#pragma unroll
+    for (int z = 0; z < S; ++z) p[z] = *reinterpret_cast<const float4 *>(a.part + z * slice + (size_t)row * a.N + c);
+    float4 *xp = reinterpret_cast<float4 *>(a.X + (size_t)row * a.ldx + c);
+    float4 x = *xp;
+    float4 v = p[0];
+#pragma unroll
+    for (int z = 1; z < S; ++z) {
+      v.x += p[z].x;
+      v.y += p[z].y;
+      v.z += p[z].z;
+      v.w += p[z].w;
+    }
+    x.x += v.x;
+    x.y += v.y;
+    x.z += v.z;
+    x.w += v.w;
+    *xp = x;
+  }
+}
+
+// ---- 256 x 256 tiles, one 128 x 128 quadrant per wave ------------------------
+//
+// Four waves (one per SIMD) each accumulate a 128 x 128 quadrant as 4 x 4
+// tiles of 32x32x16 products (256 fp32 accumulators per lane, held in the
+// accumulation registers).  Per 16-deep k-substep a wave reads 8 fragments
+// (8 KB) from LDS for 16 products, half the LDS reads and half the staged
+// bytes per flop of the 64 x 64-per-wave kernel above.  k-steps of 32 fill
+// 64-byte rows (512 rows = 32 KB per stage) through a ring of five stages
+// (all 160 KB of LDS): three in flight, one being read into registers, one
+// whose fragments are being multiplied.  With one wave per SIMD nothing else
+// covers LDS latency, so each step's fragments are read during the previous
+// step's products (two register sets of 16 fragments).  With 64-byte rows, 4 rows share a 256-byte bank line, so
+// the 16-byte chunk index is XOR-ed with (row / 4) mod 4: the 16 consecutive
+// rows one quarter-wave reads land on 16 distinct bank groups.  The
+// epilogue runs on one 128-column half at a time through the LDS tile.
+constexpr int kBT = 256, kBK = 32, kBRow = kBK * 2, kBStages = 5;
+constexpr int kBStage = 2 * kBT * kBRow;                  // A rows, then W rows
+constexpr int kBPerWave = kBStage / 1024 / 4;             // 1 KB LDS-direct loads per wave per stage
+constexpr int kBLds = kBStages * kBStage > kBT * kTCStride * 4 ? kBStages * kBStage : kBT * kTCStride * 4;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_big_kernel(const GemmArgs a, int n_rb, int n_ct, int per_xcd) {
+  using T = bf16_t;
+  __shared__ __align__(16) unsigned char lds[kBLds];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int layer = blockIdx.y;
+  const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (tile >= n_rb * n_ct) return;
+  const int ct_ = tile / n_rb, rb = tile % n_rb;
+  const int n_cb = a.n_groups;                             // 128-column blocks
+  const T *A = (const T *)a.A;
+  const T *W = (const T *)a.W[layer];
+  const int row0 = rb * kBT;
+
+  // piece q of a stage covers staged rows 16q .. 16q+15; this lane fills row
+  // 16q + lane/4, 16-byte slot lane%4.  A second column block past the end
+  // re-reads the first (its results are never stored).
+  const T *src[kBPerWave];
+#pragma unroll
+  for (int i = 0; i < kBPerWave; ++i) {
+    const int q = wave * kBPerWave + i, r = 16 * q + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((r >> 2) & 3);
+    if (r < kBT) {
+      src[i] = A + (size_t)min(row0 + r, a.M - 1) * a.lda + chunk * 8;
+    } else {
+      const int c = r - kBT;
+      int blk = 2 * ct_ + (c >> 7);
+      if (blk >= n_cb) blk = 2 * ct_;
+      src[i] = W + (size_t)t_weight_row<EPI>(a, blk, c & 127) * a.ldw + chunk * 8;
+    }
+  }
+  const int nk = a.K / kBK;
+  const unsigned lds0 = lds_offset(lds);
+#define DF_BSTAGE(kt)                                                                               \
+  do {                                                                                              \
+    const int k_ = min((kt), nk - 1) * kBK, b_ = (kt) % kBStages;                                   \
+    _Pragma("unroll") for (int i = 0; i < kBPerWave; ++i)                                           \
+      lds_dma16(src[i] + k_, lds0 + b_ * kBStage + (wave * kBPerWave + i) * 1024);                  \
+  } while (0)
+
+  const int wr = wave >> 1, wc = wave & 1;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const int fr = lane & 31, fk = lane >> 5;
+  const int sw = (fr >> 2) & 3;                            // swizzle of every fragment row of this lane
+  // Fragment g of a k-step (g = 4 * substep + i): A rows wr*128 + 32i .. and
+  // W rows wc*128 + 32i .. of the step's buffer.
+  auto read_frag = [&](int kt, int g, Frag<T> (&af)[2][4], Frag<T> (&bf)[2][4]) {
+    const unsigned char *base = lds + (kt % kBStages) * kBStage;
+    const int sub = g >> 2, i = g & 3;
+    const int off = ((2 * sub + fk) ^ sw) << 4;
+    af[sub][i].v = *reinterpret_cast<const uint4 *>(base + (wr * 128 + i * 32 + fr) * kBRow + off);
+    bf[sub][i].v = *reinterpret_cast<const uint4 *>(base + (kBT + wc * 128 + i * 32 + fr) * kBRow + off);
+  };
+  // Step kt: wait for stage kt + 1 (stages kt + 2 and kt + 3 stay in flight),
+  // barrier; then 8 groups of 4 products on the fragments of step kt (read one
+  // step earlier), each followed by one LDS-direct load of stage kt + 4 (into
+  // buffer (kt + 4) % 5, last read at step kt - 1, whose products every wave
+  // issued before this barrier) and two fragment reads of step kt + 1.
+  // Spreading the loads between the products keeps the memory and LDS queues
+  // from holding up the matrix cores; the scheduling barriers pin the order.
+  // lgkmcnt field cleared: the wait also covers this wave's fragment reads of
+  // the previous step (long done), so the compiler adds no wait of its own.
+  constexpr int kLgkm0 = ~(0xF << 8);
+#define DF_BSTEP(kt, FA, FB, GA, GB)                                                                \
+  do {                                                                                              \
+    asm volatile("" ::: "memory");                                                                  \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kBPerWave) & kLgkm0);                                  \
+    __builtin_amdgcn_s_barrier();                                                                   \
+    asm volatile("" ::: "memory");                                                                  \
+    const int kn_ = min((kt) + 4, nk - 1) * kBK, bn_ = ((kt) + 4) % kBStages;                       \
+    _Pragma("unroll") for (int g = 0; g < 8; ++g) {                                                 \
+      const int sub_ = g >> 2, i_ = g & 3;                                                          \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i_][j] = mma32(acc[i_][j], FA[sub_][i_], FB[sub_][j]); \
+      lds_dma16(src[g] + kn_, lds0 + bn_ * kBStage + (wave * kBPerWave + g) * 1024);                \
+      read_frag((kt) + 1, g, GA, GB);                                                               \
+      __builtin_amdgcn_sched_barrier(0);                                                            \
+    }                                                                                               \
+  } while (0)
+  static_assert(kBPerWave == 8, "one LDS-direct load per product group");
+  Frag<T> a0[2][4], b0[2][4], a1[2][4], b1[2][4];
+  DF_BSTAGE(0);
+  DF_BSTAGE(1);
+  DF_BSTAGE(2);
+  DF_BSTAGE(3);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kBPerWave));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int g = 0; g < 8; ++g) read_frag(0, g, a0, b0);
+  // nk is even (K is a multiple of 64)
+  for (int kt = 0; kt < nk; kt += 2) {
+    DF_BSTEP(kt, a0, b0, a1, b1);
+    DF_BSTEP(kt + 1, a1, b1, a0, b0);
+  }
+#undef DF_BSTEP
+#undef DF_BSTAGE
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  float *ctile = reinterpret_cast<float *>(lds);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int blk = 2 * ct_ + h;
+    if (blk >= n_cb) break;
+    if (wc == h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            ctile[(wr * 128 + i * 32 + 8 * (e / 4) + 4 * fk + e % 4) * kTCStride + j * 32 + fr] = acc[i][j][e];
+    }
+    __syncthreads();
+    t_epilogue<EPI, kBT, 256>(a, ctile, rb, blk, layer);
+    __syncthreads();
+  }
+}
+
+template <int EPI>
+static void launch_big_t(const GemmArgs &a, int z_slices, hipStream_t st) {
+  const int n_rb = (a.M + kBT - 1) / kBT, n_ct = (a.n_groups + 1) / 2;
+  const int per_xcd = (n_rb * n_ct + 7) / 8;
+  hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(8 * per_xcd, z_slices), dim3(256), 0, st, a, n_rb, n_ct, per_xcd);
+}
+
+static hipError_t launch_big(Epilogue epi, const GemmArgs &a, int z_slices, hipStream_t st) {
+  switch (epi) {
+    case EPI_STORE: launch_big_t<EPI_STORE>(a, z_slices, st); break;
+    case EPI_STORE_F32: launch_big_t<EPI_STORE_F32>(a, z_slices, st); break;
+    case EPI_RESID: launch_big_t<EPI_RESID>(a, z_slices, st); break;
+    case EPI_SWIGLU: launch_big_t<EPI_SWIGLU>(a, z_slices, st); break;
+    case EPI_QKV: launch_big_t<EPI_QKV>(a, z_slices, st); break;
+    case EPI_INJECT: launch_big_t<EPI_INJECT>(a, z_slices, st); break;
+    case EPI_ARGMAX: launch_big_t<EPI_ARGMAX>(a, z_slices, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 int gemm_tiled_cols(Epilogue epi, int N, int ffn) { return epi == EPI_SWIGLU ? ffn / 64 : N / kTBN; }
@@ -245,11 +463,11 @@ bool gemm_tiled_ok(Epilogue epi, int N, int K, int ffn, int hd) {
 }
 
 template <int BM>
-static hipError_t launch_tiled_bm(Epilogue epi, const GemmArgs &a, int z_slices, hipStream_t st) {
+static hipError_t launch_tiled_bm(Epilogue epi, const GemmArgs &a, int z_slices, int splits, hipStream_t st) {
   const int n_rb = (a.M + BM - 1) / BM;
   const int n_cb = a.n_groups;
   const int per_xcd = (n_rb * n_cb + 7) / 8;
-  dim3 grid(8 * per_xcd, z_slices), block(TCfg<BM>::threads);
+  dim3 grid(8 * per_xcd, z_slices, splits), block(TCfg<BM>::threads);
   switch (epi) {
     case EPI_STORE: hipLaunchKernelGGL((gemm_tiled_kernel<EPI_STORE, BM>), grid, block, 0, st, a, n_rb, n_cb, per_xcd); break;
     case EPI_STORE_F32:
@@ -271,12 +489,37 @@ static hipError_t launch_tiled_bm(Epilogue epi, const GemmArgs &a, int z_slices,
   return hipGetLastError();
 }
 
-// 256-row tiles when they still give a few waves of workgroups per compute
-// unit; 128-row tiles otherwise (more tiles for the narrow projections).
-hipError_t launch_gemm_tiled(Epilogue epi, const GemmArgs &a, int z_slices, hipStream_t st) {
+static void launch_splitk_resid(const GemmArgs &a, int splits, int cu, hipStream_t st) {
+  const long f4 = (long)a.M * (a.N / 4);
+  const int grid = (int)std::min<long>((f4 + 255) / 256, 8L * cu);
+  if (splits == 2) hipLaunchKernelGGL((gemm_splitk_resid_kernel<2>), dim3(grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((gemm_splitk_resid_kernel<4>), dim3(grid), dim3(256), 0, st, a);
+}
+
+// 256 x 256 tiles when they number at least kBigMinTiles; otherwise 256 x 128
+// tiles when those give a few workgroups per compute unit, else 128 x 128.
+// A 128 x 128 launch that leaves compute units idle splits K over 2 or 4
+// workgroups per tile (when a partial buffer is given and each split keeps at
+// least 1024 of K; residual epilogue only): the splits write fp32 partial
+// tiles and a streaming kernel adds their sum to the residual.
+hipError_t launch_gemm_tiled(Epilogue epi, GemmArgs &a, int z_slices, int cu, hipStream_t st) {
+  a.kper = a.K;
+  const long big_tiles = (long)((a.M + kBT - 1) / kBT) * ((a.n_groups + 1) / 2) * z_slices;
+  if (a.M > 128 && big_tiles >= kBigMinTiles) return launch_big(epi, a, z_slices, st);
   const long tiles256 = (long)((a.M + 255) / 256) * a.n_groups * z_slices;
-  if (tiles256 >= 512) return launch_tiled_bm<256>(epi, a, z_slices, st);
-  return launch_tiled_bm<128>(epi, a, z_slices, st);
+  if (tiles256 >= 512) return launch_tiled_bm<256>(epi, a, z_slices, 1, st);
+  const long tiles = (long)((a.M + 127) / 128) * a.n_groups * z_slices;
+  int splits = 1;
+  if (a.part && z_slices == 1 && epi == EPI_RESID) {
+    while (splits < 4 && tiles * splits * 2 <= cu && a.K % (splits * 2 * kTBK) == 0 && a.K / (splits * 2) >= 1024 &&
+           (size_t)splits * 2 * a.M * a.n_groups * kTBN * 4 <= a.part_bytes)
+      splits *= 2;
+  }
+  a.kper = a.K / splits;
+  hipError_t e = launch_tiled_bm<128>(epi, a, z_slices, splits, st);
+  if (e != hipSuccess || splits == 1) return e;
+  launch_splitk_resid(a, splits, cu, st);
+  return hipGetLastError();
 }
 
 }  // namespace dflash

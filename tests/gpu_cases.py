@@ -58,6 +58,17 @@ MINI = {
     "mini_g8": mini("mini_g8", 108, dtype="bf16", hidden=512, n_q_heads=8, n_kv_heads=1, head_dim=128,
                     ffn=512, vocab=1040, n_layers=2, n_feat_layers=2, block_size=16, batch=2,
                     ctx_min=10, ctx_max=260, rope_theta=1e6),
+    # 160 block rows, FFN and vocabulary of 321 128-column blocks each: gate/up and
+    # the LM head take the 256 x 256-tile GEMM, whose last tile has a second
+    # column block past the end, with a ragged row block
+    "mini_big": mini("mini_big", 109, dtype="bf16", hidden=256, n_q_heads=2, n_kv_heads=2, head_dim=128,
+                     ffn=20544, vocab=41088, n_layers=2, n_feat_layers=2, block_size=16, batch=10,
+                     ctx_min=5, ctx_max=150, rope_theta=1e6),
+    # 144 block rows (ragged second 128-row block), FFN 4096: the down projection
+    # has 4 tiles and splits K over 4 workgroups per tile (fp32 partials + reduction)
+    "mini_split": mini("mini_split", 110, dtype="bf16", hidden=256, n_q_heads=2, n_kv_heads=2, head_dim=128,
+                       ffn=4096, vocab=8448, n_layers=2, n_feat_layers=2, block_size=16, batch=9,
+                       ctx_min=3, ctx_max=120, rope_theta=1e6),
     "tiny": S.get_config("tiny"),
 }
 

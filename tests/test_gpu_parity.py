@@ -63,7 +63,7 @@ def test_accept_len(B):
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("name,rows", [(n, r) for n in ["tiny", "mini_bf16", "mini_f32", "mini_b10"]
                                        for r in [1, 15, 33, 70]] + [("mini_b8", r) for r in [65, 130, 300]]
-                         + [("mini_wide", r) for r in [20, 47]])
+                         + [("mini_wide", r) for r in [20, 47]] + [("mini_big", r) for r in [150, 300]])
 def test_lmhead_argmax(name, rows):
     cfg = MINI[name]
     log(f"lmhead_argmax {name} rows={rows}")
@@ -163,7 +163,7 @@ def run_draft_case(cfg, seed=0, lens=None, check_seqs=None):
 
 
 @pytest.mark.parametrize("name", ["tiny", "mini_bf16", "mini_b10", "mini_d64", "mini_f32", "mini_b8", "mini_port",
-                                  "mini_wide", "mini_g8"])
+                                  "mini_wide", "mini_g8", "mini_big", "mini_split"])
 def test_draft_block(name):
     log(f"draft_block {name}")
     run_draft_case(MINI[name], seed=0)
