@@ -290,19 +290,31 @@ __global__ __launch_bounds__(256) void gemm_splitk_resid_kernel(const GemmArgs a
 // tiles of 32x32x16 products (256 fp32 accumulators per lane, held in the
 // accumulation registers).  Per 16-deep k-substep a wave reads 8 fragments
 // (8 KB) from LDS for 16 products, half the LDS reads and half the staged
-// bytes per flop of the 64 x 64-per-wave kernel above.  k-steps of 32 fill
-// 64-byte rows (512 rows = 32 KB per stage) through a ring of five stages
-// (all 160 KB of LDS): three in flight, one being read into registers, one
-// whose fragments are being multiplied.  With one wave per SIMD nothing else
-// covers LDS latency, so each step's fragments are read during the previous
-// step's products (two register sets of 16 fragments).  With 64-byte rows, 4 rows share a 256-byte bank line, so
-// the 16-byte chunk index is XOR-ed with (row / 4) mod 4: the 16 consecutive
-// rows one quarter-wave reads land on 16 distinct bank groups.  The
-// epilogue runs on one 128-column half at a time through the LDS tile.
-constexpr int kBT = 256, kBK = 32, kBRow = kBK * 2, kBStages = 5;
-constexpr int kBStage = 2 * kBT * kBRow;                  // A rows, then W rows
-constexpr int kBPerWave = kBStage / 1024 / 4;             // 1 KB LDS-direct loads per wave per stage
-constexpr int kBLds = kBStages * kBStage > kBT * kTCStride * 4 ? kBStages * kBStage : kBT * kTCStride * 4;
+// bytes per flop of the 64 x 64-per-wave kernel above.  A k-step is 32 deep.
+//
+// Staging (LDS-direct loads, all 160 KB of LDS):
+//  * activations (A, 256 rows, L2-resident): a ring of 4 stages of one k-step,
+//    64-byte rows (16 KB per stage);
+//  * weights (W, 256 rows, streamed from HBM): a ring of 3 stages of two
+//    k-steps, 128-byte rows (32 KB per stage), so that every weight request is
+//    a whole 128-byte line -- 64-byte pieces of an 8 KB-stride matrix stream at
+//    ~3.6 TB/s against ~6 TB/s for whole lines.
+// Each step issues 4 loads of an activation stage 4 steps ahead and 4 loads
+// (half) of a weight stage, so a wave always issues 8 per step and everything
+// a step needs was issued at least 3 steps earlier.  With one wave per SIMD
+// nothing else covers LDS latency, so each step's fragments are read during
+// the previous step's products (two register sets); a buffer is refilled only
+// after the barrier of the step following the one that read its fragments.
+// Bank lines are 256 bytes: 64-byte rows XOR the 16-byte chunk index with
+// (row / 4) mod 4, 128-byte rows with (row / 2) mod 8, so the 16 consecutive
+// rows one quarter-wave reads land on 16 distinct bank groups.  The epilogue
+// runs on one 128-column half at a time through the LDS tile.
+constexpr int kBT = 256, kBK = 32;
+constexpr int kBAStage = kBT * 64, kBAStages = 4;              // activation ring
+constexpr int kBWStage = kBT * 128, kBWStages = 3;             // weight ring (two k-steps per stage)
+constexpr int kBWBase = kBAStages * kBAStage;
+constexpr int kBLdsStaging = kBWBase + kBWStages * kBWStage;   // 160 KB
+constexpr int kBLds = kBLdsStaging > kBT * kTCStride * 4 ? kBLdsStaging : kBT * kTCStride * 4;
 
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_big_kernel(const GemmArgs a, int n_rb, int n_ct, int per_xcd) {
@@ -318,31 +330,37 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const GemmArgs a, int n_r
   const T *W = (const T *)a.W[layer];
   const int row0 = rb * kBT;
 
-  // piece q of a stage covers staged rows 16q .. 16q+15; this lane fills row
-  // 16q + lane/4, 16-byte slot lane%4.  A second column block past the end
-  // re-reads the first (its results are never stored).
-  const T *src[kBPerWave];
+  // Activation piece i of a stage (this wave's 4 of 16): rows 16q .. 16q+15,
+  // q = 4*wave + i; this lane fills row 16q + lane/4, 16-byte slot lane%4.
+  // Weight piece i of half h of a stage (this wave's 4 of 16 per half): rows
+  // 8q .. 8q+7, q = 16h + 4*wave + i; this lane fills row 8q + lane/8, slot
+  // lane%8.  A second column block past the end re-reads the first (its
+  // results are never stored).
+  const T *asrc[4], *wsrc[2][4];
 #pragma unroll
-  for (int i = 0; i < kBPerWave; ++i) {
-    const int q = wave * kBPerWave + i, r = 16 * q + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((r >> 2) & 3);
-    if (r < kBT) {
-      src[i] = A + (size_t)min(row0 + r, a.M - 1) * a.lda + chunk * 8;
-    } else {
-      const int c = r - kBT;
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * (4 * wave + i) + (lane >> 2);
+    asrc[i] = A + (size_t)min(row0 + r, a.M - 1) * a.lda + ((lane & 3) ^ ((r >> 2) & 3)) * 8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = 8 * (16 * h + 4 * wave + i) + (lane >> 3);
       int blk = 2 * ct_ + (c >> 7);
       if (blk >= n_cb) blk = 2 * ct_;
-      src[i] = W + (size_t)t_weight_row<EPI>(a, blk, c & 127) * a.ldw + chunk * 8;
+      wsrc[h][i] = W + (size_t)t_weight_row<EPI>(a, blk, c & 127) * a.ldw + ((lane & 7) ^ ((c >> 1) & 7)) * 8;
     }
   }
-  const int nk = a.K / kBK;
+  const int nk = a.K / kBK, nw = nk / 2;
   const unsigned lds0 = lds_offset(lds);
-#define DF_BSTAGE(kt)                                                                               \
-  do {                                                                                              \
-    const int k_ = min((kt), nk - 1) * kBK, b_ = (kt) % kBStages;                                   \
-    _Pragma("unroll") for (int i = 0; i < kBPerWave; ++i)                                           \
-      lds_dma16(src[i] + k_, lds0 + b_ * kBStage + (wave * kBPerWave + i) * 1024);                  \
-  } while (0)
+  // activation stage s (one k-step) into ring slot s % 4; clamped past the end
+  auto a_load = [&](int s, int i) {
+    const int s_ = min(s, nk - 1);
+    lds_dma16(asrc[i] + s_ * kBK, lds0 + (s % kBAStages) * kBAStage + (4 * wave + i) * 1024);
+  };
+  // half j % 2 of weight stage j / 2 (two k-steps) into ring slot (j / 2) % 3
+  auto w_load = [&](int j, int i) {
+    const int w = j >> 1, h = j & 1, w_ = min(w, nw - 1);
+    lds_dma16(wsrc[h][i] + w_ * 2 * kBK, lds0 + kBWBase + (w % kBWStages) * kBWStage + (16 * h + 4 * wave + i) * 1024);
+  };
 
   const int wr = wave >> 1, wc = wave & 1;
   f32x16 acc[4][4];
@@ -353,49 +371,60 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const GemmArgs a, int n_r
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   const int fr = lane & 31, fk = lane >> 5;
-  const int sw = (fr >> 2) & 3;                            // swizzle of every fragment row of this lane
-  // Fragment g of a k-step (g = 4 * substep + i): A rows wr*128 + 32i .. and
-  // W rows wc*128 + 32i .. of the step's buffer.
+  const int swa = (fr >> 2) & 3, sww = (fr >> 1) & 7;      // swizzles of this lane's fragment rows
+  // Fragment g of step kt (g = 4 * substep + i): A rows wr*128 + 32i .. of
+  // activation slot kt % 4, W rows wc*128 + 32i .. of weight slot (kt/2) % 3,
+  // whose 128-byte rows hold step kt in chunks 4*(kt%2) .. +3.
   auto read_frag = [&](int kt, int g, Frag<T> (&af)[2][4], Frag<T> (&bf)[2][4]) {
-    const unsigned char *base = lds + (kt % kBStages) * kBStage;
-    const int sub = g >> 2, i = g & 3;
-    const int off = ((2 * sub + fk) ^ sw) << 4;
-    af[sub][i].v = *reinterpret_cast<const uint4 *>(base + (wr * 128 + i * 32 + fr) * kBRow + off);
-    bf[sub][i].v = *reinterpret_cast<const uint4 *>(base + (kBT + wc * 128 + i * 32 + fr) * kBRow + off);
+    const int sub = g >> 2, i = g & 3, c = 2 * sub + fk;
+    const unsigned char *ab = lds + (kt % kBAStages) * kBAStage;
+    const unsigned char *wb = lds + kBWBase + ((kt >> 1) % kBWStages) * kBWStage;
+    af[sub][i].v = *reinterpret_cast<const uint4 *>(ab + (wr * 128 + i * 32 + fr) * 64 + ((c ^ swa) << 4));
+    bf[sub][i].v = *reinterpret_cast<const uint4 *>(wb + (wc * 128 + i * 32 + fr) * 128 + (((4 * (kt & 1) + c) ^ sww) << 4));
   };
-  // Step kt: wait for stage kt + 1 (stages kt + 2 and kt + 3 stay in flight),
-  // barrier; then 8 groups of 4 products on the fragments of step kt (read one
-  // step earlier), each followed by one LDS-direct load of stage kt + 4 (into
-  // buffer (kt + 4) % 5, last read at step kt - 1, whose products every wave
-  // issued before this barrier) and two fragment reads of step kt + 1.
-  // Spreading the loads between the products keeps the memory and LDS queues
-  // from holding up the matrix cores; the scheduling barriers pin the order.
-  // lgkmcnt field cleared: the wait also covers this wave's fragment reads of
-  // the previous step (long done), so the compiler adds no wait of its own.
+  // Step kt: wait until only the loads of steps kt-2 and kt-1 are outstanding
+  // (everything step kt+1 needs was issued by step kt-3), barrier; then 8
+  // groups of 4 products on the fragments of step kt (read during step kt-1),
+  // each followed by one load -- activation stage kt+4 into the slot of stage
+  // kt (read during step kt-1), then half kt+5 of the weight ring (its slot
+  // was last read during step kt-1 or kt-2) -- and two fragment reads of step
+  // kt+1.  Spreading the loads between the products keeps the memory and LDS
+  // queues from holding up the matrix cores; the scheduling barriers pin the
+  // order.  lgkmcnt field cleared: the wait also covers this wave's fragment
+  // reads of the previous step (long done), so the compiler adds no wait of
+  // its own.
   constexpr int kLgkm0 = ~(0xF << 8);
 #define DF_BSTEP(kt, FA, FB, GA, GB)                                                                \
   do {                                                                                              \
     asm volatile("" ::: "memory");                                                                  \
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kBPerWave) & kLgkm0);                                  \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(16) & kLgkm0);                                             \
     __builtin_amdgcn_s_barrier();                                                                   \
     asm volatile("" ::: "memory");                                                                  \
-    const int kn_ = min((kt) + 4, nk - 1) * kBK, bn_ = ((kt) + 4) % kBStages;                       \
     _Pragma("unroll") for (int g = 0; g < 8; ++g) {                                                 \
       const int sub_ = g >> 2, i_ = g & 3;                                                          \
       _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i_][j] = mma32(acc[i_][j], FA[sub_][i_], FB[sub_][j]); \
-      lds_dma16(src[g] + kn_, lds0 + bn_ * kBStage + (wave * kBPerWave + g) * 1024);                \
+      if (g < 4) a_load((kt) + 4, g);                                                               \
+      else w_load((kt) + 5, g - 4);                                                                 \
       read_frag((kt) + 1, g, GA, GB);                                                               \
       __builtin_amdgcn_sched_barrier(0);                                                            \
     }                                                                                               \
   } while (0)
-  static_assert(kBPerWave == 8, "one LDS-direct load per product group");
   Frag<T> a0[2][4], b0[2][4], a1[2][4], b1[2][4];
-  DF_BSTAGE(0);
-  DF_BSTAGE(1);
-  DF_BSTAGE(2);
-  DF_BSTAGE(3);
+  // prologue, in the steady state's order: weight half 0, then for p = -4 .. -1
+  // activation stage p+4 and weight half p+5
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w_load(0, i);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a_load(p, i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w_load(p + 1, i);
+  }
+  // step 0's activation stage and both weight halves were issued before the
+  // last three rounds of 8
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kBPerWave));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(24));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 #pragma unroll
@@ -406,7 +435,6 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const GemmArgs a, int n_r
     DF_BSTEP(kt + 1, a1, b1, a0, b0);
   }
 #undef DF_BSTEP
-#undef DF_BSTAGE
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __builtin_amdgcn_s_barrier();
