@@ -24,13 +24,24 @@ constexpr int kSub = 64;        // keys per LDS sub-block
 constexpr int kPage = 16;       // keys per cache page (the only page size accepted)
 constexpr float kLog2e = 1.4426950408889634f;
 
-int attn_chunk(int batch, int max_ctx, int block_size, int nkv) {
+int attn_chunk(int batch, int max_ctx, int block_size, int nq, int nkv, int cu) {
   // aim for a few items per compute unit; chunk in [64, 512] keys, multiple of 64
   const long keys = (long)batch * (max_ctx + block_size) * nkv;
   long c = keys / 1024;
   c = (c + kSub - 1) / kSub * kSub;
   if (c < kSub) c = kSub;
   if (c > 512) c = 512;
+  // Items run in rounds of the resident workgroups (4 per compute unit for up
+  // to 64 block queries per KV head, 2 for up to 128).  When a chunk at most
+  // three times as long puts every item in one round, take the shortest such chunk:
+  // a last round with a few items costs a whole item time (with the declared
+  // maximum context as every sequence's length).
+  const long slots = (long)cu * ((nq / nkv) * block_size <= 64 ? 4 : 2);
+  auto items = [&](long ch) { return (long)batch * ((max_ctx + block_size + ch - 1) / ch) * nkv; };
+  if (items(c) > slots) {
+    for (long c1 = c + kSub; c1 <= 3 * c && c1 <= 1024; c1 += kSub)
+      if (items(c1) <= slots) return (int)c1;
+  }
   return (int)c;
 }
 

@@ -44,7 +44,7 @@ struct DraftLayout {
   int chunk, max_items;
 };
 
-DraftLayout draft_layout(const dflash_handle_s *h, int batch, int max_ctx) {
+DraftLayout draft_layout(const dflash_handle_s *h, int batch, int max_ctx, int cu) {
   const dflash_config &c = h->cfg;
   const int B = c.block_size, R = batch * B;
   const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
@@ -57,7 +57,7 @@ DraftLayout draft_layout(const dflash_handle_s *h, int batch, int max_ctx) {
   L.Vb = cv.take((size_t)R * kvd * h->esz);
   L.O = cv.take((size_t)R * qd * h->esz);
   L.Hs = cv.take((size_t)R * c.ffn * h->esz);
-  L.chunk = attn_chunk(batch, max_ctx, B, c.n_kv_heads);
+  L.chunk = attn_chunk(batch, max_ctx, B, c.n_q_heads, c.n_kv_heads, cu);
   L.max_items = attn_max_items(batch, max_ctx, B, c.n_kv_heads, L.chunk);
   const int GB = (c.n_q_heads / c.n_kv_heads) * B, GBP = (GB + 15) / 16 * 16;
   L.attn_part = cv.take((size_t)L.max_items * GBP * c.head_dim * 4);
@@ -231,7 +231,7 @@ int dflash_destroy(dflash_handle h) {
 int dflash_workspace_size(dflash_handle h, int32_t max_batch, int32_t max_ctx, int32_t max_new, size_t *bytes) {
   if (!h || !bytes) return DFLASH_ERR_NULL;
   if (max_batch < 1 || max_ctx < 0 || max_new < 0) return DFLASH_ERR_SHAPE;
-  size_t need = draft_layout(h, max_batch, max_ctx).total;
+  size_t need = draft_layout(h, max_batch, max_ctx, compute_units(h)).total;
   const size_t lm = lm_layout(h, max_batch * (h->cfg.block_size - 1)).total;
   const size_t inj = inject_layout(h, max_new).total;
   need = need > lm ? need : lm;
@@ -313,7 +313,7 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
   if (!anchor_ids || !hidden_out || !ws) return DFLASH_ERR_NULL;
   const dflash_config &c = h->cfg;
   const int B = c.block_size, batch = kv->batch, R = batch * B;
-  const DraftLayout L = draft_layout(h, batch, kv->max_ctx);
+  const DraftLayout L = draft_layout(h, batch, kv->max_ctx, compute_units(h));
   if (ws_bytes < L.total) return DFLASH_ERR_WORKSPACE;
   char *w = static_cast<char *>(ws);
   hipStream_t s = (hipStream_t)stream;

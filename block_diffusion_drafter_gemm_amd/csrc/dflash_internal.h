@@ -95,7 +95,7 @@ struct AttnArgs {
   int batch, block_size, nq, nkv, hd, max_pages, page_size, chunk, max_items;
 };
 hipError_t launch_attention(bool is_bf16, const AttnArgs &a, hipStream_t st);
-int attn_chunk(int batch, int max_ctx, int block_size, int nkv);
+int attn_chunk(int batch, int max_ctx, int block_size, int nq, int nkv, int cu);
 int attn_max_items(int batch, int max_ctx, int block_size, int nkv, int chunk);
 
 hipError_t launch_embed(bool is_bf16, const void *embed, const int *anchor, int mask_id, int batch, int block_size,
