@@ -251,10 +251,14 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, ln = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int layer = blockIdx.y;
-  if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
-    if (tid < a.hd / 2) inv_freq[tid] = rope_inv_freq(tid, a.hd, a.log2_theta);
-    __syncthreads();
-  }
+  // RoPE inverse frequencies, computed once the first loads are in flight;
+  // the barriers of the staging and of every tile's reduction publish them
+  // before the first epilogue reads them
+  auto init_rope = [&]() {
+    if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
+      if (tid < a.hd / 2) inv_freq[tid] = rope_inv_freq(tid, a.hd, a.log2_theta);
+    }
+  };
   const T *W = (const T *)a.W[layer];
   const int ntiles = a.n_groups;
   const int CPT = a.K / 32;                                    // chunks per tile
@@ -304,19 +308,26 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
 #pragma unroll
       for (int k = 0; k < NV; ++k) cv[k] = src[min(lane + 64 * k, nvec - 1)];
       DF_ISSUE(bufa, 0);
+      init_rope();
+      // every piece of the LDS row is written (zeros past K and for rows >= M):
+      // no branch per piece keeps this once-per-launch code short
       uint4 *dst = reinterpret_cast<uint4 *>(a_lds + r * ASTR);
 #pragma unroll
       for (int k = 0; k < NV; ++k) {
         const int i = lane + 64 * k;
-        if (i < nvec) dst[i] = have_row ? cv[k] : make_uint4(0, 0, 0, 0);
+        dst[i] = have_row && i < nvec ? cv[k] : make_uint4(0, 0, 0, 0);
       }
       lds_barrier();
     } else {
       // lane owns the 4-element groups q4 = lane + 64 k of the row; the gain
-      // is read once per workgroup (one group per thread) and parked in the
-      // reduction buffer, which is unused until the first tile finishes
+      // is read once per workgroup (one group per thread, issued first) and
+      // parked in the reduction buffer, which is unused until the first tile
+      // finishes.  The gain is published before the rows land, so each wave
+      // normalises its row as soon as that row arrives (rows reach a compute
+      // unit one group of four waves after another, not all at once).
       constexpr int PQ = KR / 4 / 64;              // groups per lane at most
       const int nq4 = a.K / 4;
+      const float4 gq = load4((const T *)a.gain, min(tid, nq4 - 1));
       float4 xv[PQ];
       if constexpr (AM == A_EMBED_NORM) {
         const int s = rr / a.block_size, j = rr - s * a.block_size;
@@ -329,45 +340,52 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
 #pragma unroll
         for (int k = 0; k < PQ; ++k) xv[k] = x4[min(lane + 64 * k, nq4 - 1)];
       }
-      const float4 gq = load4((const T *)a.gain, min(tid, nq4 - 1));
       DF_ISSUE(bufa, 0);
+      init_rope();
+      // groups past K hold zeros (row values and gain alike), so the loops
+      // below run branch-free over the whole LDS row: this once-per-launch
+      // code stays short
       float4 *gl = reinterpret_cast<float4 *>(&red[0][0]);
-      if (tid < nq4) gl[tid] = gq;
+      if (tid < KR / 4) gl[tid] = tid < nq4 ? gq : make_float4(0.f, 0.f, 0.f, 0.f);
+      lds_barrier();                               // gain visible
       float ss = 0.f;
 #pragma unroll
       for (int k = 0; k < PQ; ++k) {
-        if (lane + 64 * k < nq4) {
-          ss += xv[k].x * xv[k].x;
-          ss += xv[k].y * xv[k].y;
-          ss += xv[k].z * xv[k].z;
-          ss += xv[k].w * xv[k].w;
-        }
+        if (lane + 64 * k >= nq4) xv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        ss += xv[k].x * xv[k].x;
+        ss += xv[k].y * xv[k].y;
+        ss += xv[k].z * xv[k].z;
+        ss += xv[k].w * xv[k].w;
       }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
       const float rs = 1.0f / sqrtf(ss / (float)a.K + a.eps);
-      const bool write_x = AM == A_EMBED_NORM && have_row && blockIdx.x == 0 && blockIdx.y == 0;
+      const float rsr = have_row ? rs : 0.f;       // rows >= M are stored as zeros
       T *dst = reinterpret_cast<T *>(a_lds + r * ASTR);
-      lds_barrier();                               // gain visible
 #pragma unroll
       for (int k = 0; k < PQ; ++k) {
         const int q4 = lane + 64 * k;
-        if (q4 < nq4) {
-          const float4 gv = gl[q4];
-          float4 o;
-          o.x = xv[k].x * rs * gv.x;
-          o.y = xv[k].y * rs * gv.y;
-          o.z = xv[k].z * rs * gv.z;
-          o.w = xv[k].w * rs * gv.w;
-          if (!have_row) o = make_float4(0.f, 0.f, 0.f, 0.f);
-          store4(dst, q4, o);
-          if (write_x) reinterpret_cast<float4 *>(a.X + (size_t)r * a.ldx)[q4] = xv[k];   // residual stream
+        const float4 gv = gl[q4];
+        float4 o;
+        o.x = xv[k].x * rsr * gv.x;
+        o.y = xv[k].y * rsr * gv.y;
+        o.z = xv[k].z * rsr * gv.z;
+        o.w = xv[k].w * rsr * gv.w;
+        store4(dst, q4, o);
+      }
+      if (AM == A_EMBED_NORM && have_row && blockIdx.x == 0 && blockIdx.y == 0) {
+        // one workgroup starts the residual stream with the embedding rows
+#pragma unroll
+        for (int k = 0; k < PQ; ++k) {
+          const int q4 = lane + 64 * k;
+          if (q4 < nq4) reinterpret_cast<float4 *>(a.X + (size_t)r * a.ldx)[q4] = xv[k];
         }
       }
       lds_barrier();
     }
   } else {
     DF_ISSUE(bufa, 0);
+    init_rope();
   }
 
   float best_v = -INFINITY;
