@@ -127,6 +127,38 @@ def test_inject_context(name, n_new):
     dr.close()
 
 
+@pytest.mark.parametrize("n_new", [16, 40, 100])
+def test_bf16_ties_through_inject(n_new):
+    """fp32 -> bf16 rounding in the GPU epilogues on exact ties and near ties:
+    c = feats . W_fc^T from one-hot fusion weights, read back through identity V
+    projections.  16 rows take the streaming GEMM, 40 the few-rows GEMM, 100 the
+    LDS-tiled GEMM; all must equal torch's CPU conversion (ties to even) bit for
+    bit, as the oracle does."""
+    from tie_cases import tie_case
+    cfg = S.get_config("tiny", dtype="bf16", n_feat_layers=3)
+    log(f"bf16 ties through inject, n_new={n_new}")
+    R = runtime()
+    w, feats, expect, _ = tie_case(cfg, n_new, seed=11)
+    lens = np.array([n_new], dtype=np.int32)
+    lay = S.paged_layout(cfg, lens, headroom=cfg.block_size, seed=11)
+    pos = np.arange(n_new, dtype=np.int32)
+    seq = np.zeros(n_new, dtype=np.int32)
+    dr = R.Drafter(cfg, w, max_batch=1, max_ctx=n_new, max_new=n_new)
+    kv = R.PagedKV(cfg, lay.block_table, lens, lay.n_pages)
+    dr.inject_context(R.to_device(feats), torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), kv)
+    torch.cuda.synchronize()
+    Vg = R.to_host_storage(kv.v)
+    pages = lay.block_table[seq, pos // cfg.page_size]
+    got = Vg[:, pages, pos % cfg.page_size].reshape(cfg.n_layers, n_new, cfg.hidden)
+    _, V_o = D.inject(w, cfg, feats, pos)
+    for l in range(cfg.n_layers):
+        bad = int((got[l] != expect).sum())
+        log(f"  layer {l}: {bad} of {expect.size} elements differ from round-to-nearest-even")
+        assert bad == 0
+        assert np.array_equal(from_storage(got[l]), V_o[l].reshape(n_new, cfg.hidden))
+    dr.close()
+
+
 # ----------------------------------------------------------------------------
 # A3..A8 draft block (+ A9 on its output)
 # ----------------------------------------------------------------------------

@@ -523,3 +523,17 @@ def test_drafter_size_matches_pages():
     layers = cfg.layer_params() - cfg.feat_dim * cfg.hidden - cfg.hidden
     assert 0.5e9 <= layers <= 1.0e9
     assert layers == pytest.approx(964.7e6, rel=1e-3)
+
+
+def test_inject_rounds_exact_ties_to_even():
+    """The oracle's storage rounding of the fused context c (read back through
+    identity V projections) on exact fp32 ties between bf16 neighbours, against
+    torch's CPU conversion: round to nearest, ties to even."""
+    from tie_cases import tie_case
+    cfg = S.get_config("tiny", dtype="bf16", n_feat_layers=3)
+    w, feats, expect, n_ties = tie_case(cfg, 12, seed=7)
+    assert n_ties > 1000
+    _, V = D.inject(w, cfg, feats, np.arange(12))
+    got = bf16_bits(V.reshape(cfg.n_layers, 12, cfg.hidden))
+    for l in range(cfg.n_layers):
+        assert np.array_equal(got[l], expect)
