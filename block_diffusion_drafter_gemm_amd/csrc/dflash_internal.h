@@ -58,6 +58,10 @@ struct GemmArgs {
   float *part;
   size_t part_bytes;
   int kper;
+  // streaming GEMM's A_COPY_ROWS mode (residual projection over more than 16
+  // rows): row_groups slices of the grid, one per 16-row group (grid.y); row0
+  // is the group's first row, set inside the kernel
+  int row_groups, row0;
 };
 
 // Launch a skinny GEMM; ``z_slices`` = number of weight slices (layers) in the
@@ -73,7 +77,8 @@ int gemm_tiles(Epilogue epi, int N, int ffn);
 // Streaming GEMM for M <= 16 rows (persistent, one workgroup per compute unit).
 // amode: 0 = activations read from global memory, 1 = copied into LDS,
 // 2 = RMSNorm of the fp32 residual X into LDS, 3 = embedding gather + RMSNorm,
-// 4 = copied into LDS one K-portion at a time (one tile per workgroup).
+// 4 = copied into LDS one K-portion at a time (one tile per workgroup),
+// 6 = copied into LDS, one grid slice per 16-row group (EPI_RESID only).
 hipError_t launch_gemm_stream(bool is_bf16, Epilogue epi, int amode, const GemmArgs &a, int grid_x, int z_slices,
                               hipStream_t st);
 // Largest K whose 16 activation rows stay resident in LDS.

@@ -27,7 +27,7 @@ constexpr int kSWaves = 16;
 constexpr int kSThreads = kSWaves * 64;
 constexpr int kSResBytes = 128 * 1024;   // LDS budget of the resident activation rows
 
-enum AMode { A_GLOBAL = 0, A_COPY = 1, A_NORM = 2, A_EMBED_NORM = 3 };
+enum AMode { A_GLOBAL = 0, A_COPY = 1, A_NORM = 2, A_EMBED_NORM = 3, A_COPY_ROWS = 6 };
 
 template <typename T>
 __host__ __device__ constexpr int stream_res_k() {
@@ -237,8 +237,28 @@ __device__ __forceinline__ void s_finish_tile(const GemmArgs &a, f32x4 &acc, flo
   s_epilogue<T, EPI>(a, ct, t, layer, best_v, best_i, inv_freq, pre, first);
 }
 
+// A_COPY_ROWS (residual projection only): grid.y is a 16-row group; the
+// activation and residual rows move to the group's first row and M becomes the
+// group's row count (at most 16).  Field by field, so the arguments stay in
+// registers.
+template <typename T>
+__device__ __forceinline__ GemmArgs row_slice(const GemmArgs &a0) {
+  GemmArgs a = a0;
+  const int r0 = 16 * (int)blockIdx.y;
+  a.row0 = r0;
+  a.M = min(16, a0.M - r0);
+  a.A = (const T *)a0.A + (size_t)r0 * a0.lda;
+  a.X = a0.X + (size_t)r0 * a0.ldx;
+  return a;
+}
+
 template <typename T, int EPI, int AM>
-__global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a0) {
+  static_assert(AM != A_COPY_ROWS || EPI == EPI_RESID, "row groups serve the residual projection");
+  // grid.y is the weight slice (layer), or the 16-row group of A_COPY_ROWS
+  constexpr bool ROWS = AM == A_COPY_ROWS;
+  const int layer = ROWS ? 0 : blockIdx.y;
+  const GemmArgs a = ROWS ? row_slice<T>(a0) : a0;
   constexpr bool RES = AM != A_GLOBAL;
   constexpr int KR = stream_res_k<T>();                        // resident k capacity
   constexpr int ASTR = (RES ? KR : 0) * (int)sizeof(T) + 16;   // bytes per resident row
@@ -250,7 +270,6 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   __shared__ double inv_freq[64];   // RoPE inverse frequencies (head_dim <= 128)
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, ln = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int layer = blockIdx.y;
   // RoPE inverse frequencies, computed once the first loads are in flight;
   // the barriers of the staging and of every tile's reduction publish them
   // before the first epilogue reads them
@@ -259,7 +278,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
       if (tid < a.hd / 2) inv_freq[tid] = rope_inv_freq(tid, a.hd, a.log2_theta);
     }
   };
-  const T *W = (const T *)a.W[layer];
+  const T *W = (const T *)a0.W[layer];
   const int ntiles = a.n_groups;
   const int CPT = a.K / 32;                                    // chunks per tile
   const int CPW = (CPT + kSWaves - 1) / kSWaves;               // chunks per wave
@@ -296,7 +315,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
     const int r = wave;
     const bool have_row = r < a.M;
     const int rr = min(r, a.M - 1);
-    if constexpr (AM == A_COPY) {
+    if constexpr (AM == A_COPY || AM == A_COPY_ROWS) {
       // the row goes through registers (NV 16-byte pieces per lane, all
       // issued first, clamped source); the first weight batch is issued
       // before the wait, so it stays in flight while the row is written to LDS
@@ -373,7 +392,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
         o.w = xv[k].w * rsr * gv.w;
         store4(dst, q4, o);
       }
-      if (AM == A_EMBED_NORM && have_row && blockIdx.x == 0 && blockIdx.y == 0) {
+      if (AM == A_EMBED_NORM && have_row && blockIdx.x == 0 && layer == 0) {
         // one workgroup starts the residual stream with the embedding rows
 #pragma unroll
         for (int k = 0; k < PQ; ++k) {
@@ -428,6 +447,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
 // is done.
 template <typename T, int EPI>
 __global__ __launch_bounds__(kSThreads) void gemm_portion_kernel(const GemmArgs a) {
+  const int layer = blockIdx.y;
   constexpr int KR = stream_res_k<T>();
   constexpr int ASTR = KR * (int)sizeof(T) + 16;
   constexpr int U = 8 / (int)(sizeof(T) / 2);
@@ -441,7 +461,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_portion_kernel(const GemmArgs 
   __shared__ double inv_freq[64];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, ln = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int layer = blockIdx.y, t = blockIdx.x;
+  const int t = blockIdx.x;
   if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
     if (tid < a.hd / 2) inv_freq[tid] = rope_inv_freq(tid, a.hd, a.log2_theta);
   }
@@ -533,6 +553,13 @@ static hipError_t launch_s(int am, const GemmArgs &a, dim3 grid, hipStream_t st)
     case A_EMBED_NORM:
       hipLaunchKernelGGL((gemm_stream_kernel<T, EPI, A_EMBED_NORM>), grid, block, 0, st, a);
       break;
+    case A_COPY_ROWS:   // grid.y = 16-row groups
+      if constexpr (EPI == EPI_RESID) {
+        hipLaunchKernelGGL((gemm_stream_kernel<T, EPI, A_COPY_ROWS>), grid, block, 0, st, a);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
     case 4:   // K-portions, one tile per workgroup (grid.x = tiles)
       hipLaunchKernelGGL((gemm_portion_kernel<T, EPI>), dim3(a.n_groups, grid.y), block, 0, st, a);
       break;
