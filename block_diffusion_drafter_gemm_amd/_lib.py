@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(_HERE, "lib", "libdflash.so")
 DFLASH_F32, DFLASH_BF16 = 0, 1
 
 EXPORTS = ("dflash_create", "dflash_destroy", "dflash_workspace_size", "dflash_workspace_init",
-           "dflash_inject_context", "dflash_draft_block", "dflash_lmhead_argmax", "dflash_accept_len",
-           "dflash_stream_read", "dflash_status_str")
+           "dflash_inject_context", "dflash_draft_block", "dflash_target_verify", "dflash_lmhead_argmax",
+           "dflash_accept_len", "dflash_stream_read", "dflash_status_str")
 
 
 class DflashError(RuntimeError):
@@ -70,6 +70,7 @@ def load() -> ctypes.CDLL:
     lib.dflash_workspace_init.argtypes = [vp, vp, sz, vp]
     lib.dflash_inject_context.argtypes = [vp, vp, vp, vp, i32, ctypes.POINTER(DflashKV), vp, sz, vp]
     lib.dflash_draft_block.argtypes = [vp, vp, ctypes.POINTER(DflashKV), vp, vp, sz, vp]
+    lib.dflash_target_verify.argtypes = [vp, vp, ctypes.POINTER(DflashKV), vp, i32, vp, vp, vp, sz, vp]
     lib.dflash_lmhead_argmax.argtypes = [vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.dflash_accept_len.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     lib.dflash_stream_read.argtypes = [vp, sz, vp, vp]
@@ -139,6 +140,15 @@ def dflash_draft_block(h: int, anchor_ids, kv: DflashKV, hidden_out, ws, stream:
                                      current_stream() if stream is None else stream), "dflash_draft_block")
 
 
+def dflash_target_verify(h: int, ids, kv: DflashKV, tap_layers: Sequence[int], taps_out, hidden_out, ws,
+                         stream: Optional[int] = None) -> None:
+    taps = (ctypes.c_int32 * max(1, len(tap_layers)))(*tap_layers)
+    _check(load().dflash_target_verify(h, ptr(ids), ctypes.byref(kv), ctypes.cast(taps, ctypes.c_void_p),
+                                       len(tap_layers), ptr(taps_out), ptr(hidden_out), ptr(ws),
+                                       ws.numel() * ws.element_size(),
+                                       current_stream() if stream is None else stream), "dflash_target_verify")
+
+
 def dflash_lmhead_argmax(h: int, hidden, rows: int, ids_out, max_logit_out, logits_out, ws,
                          stream: Optional[int] = None) -> None:
     _check(load().dflash_lmhead_argmax(h, ptr(hidden), rows, ptr(ids_out), ptr(max_logit_out), ptr(logits_out),
@@ -174,7 +184,8 @@ def make_weights(embed, lm_head, w_fc, final_norm, attn_norm: Sequence, w_qkv: S
         arrays.append(a)
         return ctypes.cast(a, _PP)
 
-    w = DflashWeights(embed.data_ptr(), lm_head.data_ptr(), w_fc.data_ptr(), final_norm.data_ptr(),
+    w = DflashWeights(embed.data_ptr(), lm_head.data_ptr(), None if w_fc is None else w_fc.data_ptr(),
+                      final_norm.data_ptr(),
                       arr(attn_norm), arr(w_qkv), arr(w_o), arr(mlp_norm), arr(w_gate_up), arr(w_down))
     return w, arrays
 

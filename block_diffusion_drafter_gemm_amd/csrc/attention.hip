@@ -120,6 +120,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
   // query fragments of this wave's tiles (B operand: column = query row)
   Frag<T> qf[1][NU];
   bool tile_on[1];
+  int qrow_j[1];   // block position of this lane's query row
 #pragma unroll
   for (int t = 0; t < 1; ++t) {
     const int qt = wave;
@@ -127,6 +128,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
     const int r = qt * 16 + ln;
     const bool ok = tile_on[t] && r < GB;
     const int hh = ok ? r / B : 0, j = ok ? r % B : 0;
+    qrow_j[t] = j;
     const T *qp = Q + ((size_t)(s * B + j) * a.nq + g * G + hh) * HD + 8 * g4;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -259,7 +261,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = sub + kb2 + kt * 16 + 4 * g4 + i;
-            const float sc = key < kend ? f4get(st[kt], i) * scale : -1e30f;
+            // causal (target verify): block row j sees keys up to position ctx + j
+            const bool vis = key < kend && (!a.causal || key <= ctx + qrow_j[t]);
+            const float sc = vis ? f4get(st[kt], i) * scale : -1e30f;
             p[kt * 4 + i] = sc;
             bmax = fmaxf(bmax, sc);
           }

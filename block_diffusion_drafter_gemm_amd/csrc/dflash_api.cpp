@@ -213,7 +213,7 @@ int dflash_create(const dflash_config *cfg, const dflash_weights *w, dflash_hand
   *out = nullptr;
   int st = validate_config(cfg);
   if (st != DFLASH_OK) return st;
-  if (!w->embed || !w->lm_head || !w->w_fc || !w->final_norm || !w->attn_norm || !w->w_qkv || !w->w_o ||
+  if (!w->embed || !w->lm_head || !w->final_norm || !w->attn_norm || !w->w_qkv || !w->w_o ||
       !w->mlp_norm || !w->w_gate_up || !w->w_down)
     return DFLASH_ERR_NULL;
   for (int l = 0; l < cfg->n_layers; ++l)
@@ -271,7 +271,7 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
   int st = validate_kv(h, kv);
   if (st != DFLASH_OK) return st;
   if (n_new == 0) return DFLASH_OK;
-  if (!feats || !seq || !pos || !ws) return DFLASH_ERR_NULL;
+  if (!feats || !seq || !pos || !ws || !h->w_fc) return DFLASH_ERR_NULL;
   const dflash_config &c = h->cfg;
   const InjectLayout L = inject_layout(h, n_new);
   if (ws_bytes < L.total) return DFLASH_ERR_WORKSPACE;
@@ -323,18 +323,23 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
                : launch(h, EPI_INJECT, b, c.n_layers, s);
 }
 
-int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_kv *kv, void *hidden_out, void *ws,
-                       size_t ws_bytes, void *stream) {
-  if (!h) return DFLASH_ERR_NULL;
-  int st = validate_kv(h, kv);
-  if (st != DFLASH_OK) return st;
-  if (!anchor_ids || !hidden_out || !ws) return DFLASH_ERR_NULL;
+// One pass of the handle's decoder over a block of B rows per sequence at
+// positions ctx_len[s] .. ctx_len[s] + B - 1.  Drafter (ids == NULL): rows are
+// the anchor and B - 1 mask tokens, attention is non-causal, the context cache
+// is only read and the final norm covers the mask rows.  Target verify (ids
+// set): rows are the given tokens, attention is causal within the block, every
+// layer's block K/V are appended to the cache, the residual rows after the
+// tapped layers go to taps_out and the final norm covers all B rows.
+static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32_t *ids, const int32_t *tap_layers,
+                         int32_t n_taps, void *taps_out, const dflash_kv *kv, void *hidden_out, void *ws,
+                         size_t ws_bytes, hipStream_t s) {
+  int st = DFLASH_OK;
+  const bool verify = ids != nullptr;
   const dflash_config &c = h->cfg;
   const int B = c.block_size, batch = kv->batch, R = batch * B;
   const DraftLayout L = draft_layout(h, batch, kv->max_ctx, compute_units(h));
   if (ws_bytes < L.total) return DFLASH_ERR_WORKSPACE;
   char *w = static_cast<char *>(ws);
-  hipStream_t s = (hipStream_t)stream;
   const int qd = c.n_q_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
   float *X = reinterpret_cast<float *>(w + L.X);
   const size_t cache_layer = (size_t)kv->n_pages * c.page_size * kvd * h->esz;
@@ -347,7 +352,7 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
   const bool sliced = !fast && R <= 64 && qd <= KR;
 
   if (!fast &&
-      launch_embed(h->bf16, h->embed, anchor_ids, c.mask_token_id, batch, B, c.hidden, X, s) != hipSuccess)
+      launch_embed(h->bf16, h->embed, anchor_ids, c.mask_token_id, ids, batch, B, c.hidden, X, s) != hipSuccess)
     return DFLASH_ERR_HIP;
   for (int l = 0; l < c.n_layers; ++l) {
     // A4: RMSNorm, QKV projection, RoPE; block q/k/v to the workspace
@@ -375,6 +380,7 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
       q.embed = h->embed;
       q.anchor = anchor_ids;
       q.mask_id = c.mask_token_id;
+      q.ids = ids;
       st = launch_stream(h, EPI_QKV, l == 0 ? AM_EMBED_NORM : AM_NORM, q, 1, s);
     } else {
       if (launch_rmsnorm(h->bf16, X, h->attn_norm[l], c.rms_eps, R, c.hidden, B, false, w + L.Y, s) != hipSuccess)
@@ -407,7 +413,14 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     at.page_size = c.page_size;
     at.chunk = L.chunk;
     at.max_items = L.max_items;
+    at.causal = verify ? 1 : 0;
     if (launch_attention(h->bf16, at, s) != hipSuccess) return DFLASH_ERR_HIP;
+    // target verify: the block's K/V join the context cache (the caller keeps
+    // the accepted positions by advancing ctx_len; later blocks overwrite the rest)
+    if (verify && launch_kv_append(h->bf16, w + L.Kb, w + L.Vb, static_cast<char *>(kv->k) + l * cache_layer,
+                                   static_cast<char *>(kv->v) + l * cache_layer, kv->block_table, kv->ctx_len, batch,
+                                   B, kvd, kv->max_pages, c.page_size, s) != hipSuccess)
+      return DFLASH_ERR_HIP;
 
     // A6: O projection + residual
     GemmArgs o;
@@ -472,12 +485,40 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
     st = fast ? launch_stream(h, EPI_RESID, c.ffn <= KR ? AM_COPY : AM_PORTION, dn, 1, s)
               : launch(h, EPI_RESID, dn, 1, s);
     if (st != DFLASH_OK) return st;
+    for (int i = 0; i < n_taps; ++i)   // target hidden-state taps after this layer
+      if (tap_layers[i] == l && launch_tap(h->bf16, X, R, c.hidden, i, n_taps, taps_out, s) != hipSuccess)
+        return DFLASH_ERR_HIP;
   }
-  // A8: final RMSNorm of the mask rows
-  if (launch_rmsnorm(h->bf16, X, h->final_norm, c.rms_eps, batch * (B - 1), c.hidden, B, true, hidden_out, s) !=
+  // A8: final RMSNorm (drafter: the mask rows; target: every row)
+  const int out_rows = verify ? R : batch * (B - 1);
+  if (launch_rmsnorm(h->bf16, X, h->final_norm, c.rms_eps, out_rows, c.hidden, B, !verify, hidden_out, s) !=
       hipSuccess)
     return DFLASH_ERR_HIP;
   return DFLASH_OK;
+}
+
+int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_kv *kv, void *hidden_out, void *ws,
+                       size_t ws_bytes, void *stream) {
+  if (!h) return DFLASH_ERR_NULL;
+  int st = validate_kv(h, kv);
+  if (st != DFLASH_OK) return st;
+  if (!anchor_ids || !hidden_out || !ws) return DFLASH_ERR_NULL;
+  return forward_block(h, anchor_ids, nullptr, nullptr, 0, nullptr, kv, hidden_out, ws, ws_bytes,
+                       (hipStream_t)stream);
+}
+
+int dflash_target_verify(dflash_handle h, const int32_t *ids, const dflash_kv *kv, const int32_t *tap_layers,
+                         int32_t n_taps, void *taps_out, void *hidden_out, void *ws, size_t ws_bytes, void *stream) {
+  if (!h) return DFLASH_ERR_NULL;
+  int st = validate_kv(h, kv);
+  if (st != DFLASH_OK) return st;
+  if (!ids || !hidden_out || !ws) return DFLASH_ERR_NULL;
+  if (n_taps < 0 || n_taps > kMaxLayers) return DFLASH_ERR_SHAPE;
+  if (n_taps > 0 && (!tap_layers || !taps_out)) return DFLASH_ERR_NULL;
+  for (int i = 0; i < n_taps; ++i)
+    if (tap_layers[i] < 0 || tap_layers[i] >= h->cfg.n_layers) return DFLASH_ERR_RANGE;
+  return forward_block(h, nullptr, ids, tap_layers, n_taps, taps_out, kv, hidden_out, ws, ws_bytes,
+                       (hipStream_t)stream);
 }
 
 int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int32_t *ids_out, float *max_logit_out,

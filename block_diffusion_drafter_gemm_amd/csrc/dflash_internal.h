@@ -53,6 +53,7 @@ struct GemmArgs {
   const void *embed;
   const int *anchor;
   int mask_id;
+  const int *ids;         // embedding gather: per-row token ids [M] (NULL: anchor + mask ids)
   // split-K of the LDS-tiled GEMM: fp32 partial tiles [split][M][n_groups*128]
   // (NULL: no split), bytes available there, K elements per split
   float *part;
@@ -98,13 +99,23 @@ struct AttnArgs {
   float *partial;         // [items][GB_pad][hd] + stats
   float *stats;           // [items][GB_pad][2]
   int batch, block_size, nq, nkv, hd, max_pages, page_size, chunk, max_items;
+  int causal;             // block row j sees block keys 0..j only (target verify)
 };
 hipError_t launch_attention(bool is_bf16, const AttnArgs &a, hipStream_t st);
 int attn_chunk(int batch, int max_ctx, int block_size, int nq, int nkv, int cu);
 int attn_max_items(int batch, int max_ctx, int block_size, int nkv, int chunk);
 
-hipError_t launch_embed(bool is_bf16, const void *embed, const int *anchor, int mask_id, int batch, int block_size,
-                        int hidden, float *X, hipStream_t st);
+hipError_t launch_embed(bool is_bf16, const void *embed, const int *anchor, int mask_id, const int *ids, int batch,
+                        int block_size, int hidden, float *X, hipStream_t st);
+// Block K/V rows [batch*B, nkv*hd] of one layer into the paged cache at
+// positions ctx_len[s] + j.
+hipError_t launch_kv_append(bool is_bf16, const void *kb, const void *vb, void *kc, void *vc, const int *block_table,
+                            const int *ctx_len, int batch, int block_size, int kvd, int max_pages, int page_size,
+                            hipStream_t st);
+// Residual rows X [rows, hidden] (fp32) into column block `slot` of
+// taps [rows, n_slots * hidden] (storage type).
+hipError_t launch_tap(bool is_bf16, const float *X, int rows, int hidden, int slot, int n_slots, void *taps,
+                      hipStream_t st);
 hipError_t launch_rmsnorm(bool is_bf16, const float *X, const void *gain, float eps, int rows, int hidden,
                           int block_size, bool skip_anchor, void *Y, hipStream_t st);
 hipError_t launch_argmax_reduce(const float *val, const int *idx, int rows, int n_groups, int *ids_out,

@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
       float4 xv[PQ];
       if constexpr (AM == A_EMBED_NORM) {
         const int s = rr / a.block_size, j = rr - s * a.block_size;
-        const int id = j == 0 ? a.anchor[s] : a.mask_id;
+        const int id = a.ids ? a.ids[rr] : (j == 0 ? a.anchor[s] : a.mask_id);
         const T *erow = (const T *)a.embed + (size_t)id * a.K;
 #pragma unroll
         for (int k = 0; k < PQ; ++k) xv[k] = load4(erow, min(lane + 64 * k, nq4 - 1));

@@ -9,11 +9,11 @@ constexpr int kNormThreads = 512;
 
 // X[s*B + j, :] = E[j == 0 ? anchor[s] : mask] as fp32 (the residual stream).
 template <typename T>
-__global__ __launch_bounds__(256) void embed_kernel(const T *E, const int *anchor, int mask_id, int B, int H,
-                                                    float *X) {
+__global__ __launch_bounds__(256) void embed_kernel(const T *E, const int *anchor, int mask_id, const int *ids,
+                                                    int B, int H, float *X) {
   const int row = blockIdx.x;
   const int s = row / B, j = row % B;
-  const int id = j == 0 ? anchor[s] : mask_id;
+  const int id = ids ? ids[row] : (j == 0 ? anchor[s] : mask_id);
   const T *e = E + (size_t)id * H;
   for (int i = threadIdx.x; i < H; i += blockDim.x) X[(size_t)row * H + i] = Storage<T>::load(e, i);
 }
@@ -118,14 +118,62 @@ __global__ void zero_kernel(uint4 *p, size_t n16) {
     p[i] = make_uint4(0, 0, 0, 0);
 }
 
-hipError_t launch_embed(bool is_bf16, const void *embed, const int *anchor, int mask_id, int batch, int B, int H,
-                        float *X, hipStream_t st) {
+hipError_t launch_embed(bool is_bf16, const void *embed, const int *anchor, int mask_id, const int *ids, int batch,
+                        int B, int H, float *X, hipStream_t st) {
   if (is_bf16)
     hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(batch * B), dim3(256), 0, st, (const bf16_t *)embed, anchor,
-                       mask_id, B, H, X);
+                       mask_id, ids, B, H, X);
   else
     hipLaunchKernelGGL(embed_kernel<float>, dim3(batch * B), dim3(256), 0, st, (const float *)embed, anchor,
-                       mask_id, B, H, X);
+                       mask_id, ids, B, H, X);
+  return hipGetLastError();
+}
+
+// One workgroup per block row: its K and V rows (kvd elements each) go to the
+// paged slot of position ctx_len[s] + j (page from the sequence's table).
+template <typename T>
+__global__ __launch_bounds__(256) void kv_append_kernel(const T *kb, const T *vb, T *kc, T *vc, const int *block_table,
+                                                        const int *ctx_len, int B, int kvd, int max_pages,
+                                                        int page_size) {
+  const int row = blockIdx.x, s = row / B, j = row % B;
+  const int pos = ctx_len[s] + j;
+  const int page = block_table[(size_t)s * max_pages + pos / page_size];
+  const size_t dst = ((size_t)page * page_size + pos % page_size) * kvd;
+  for (int i = threadIdx.x; i < kvd; i += blockDim.x) {
+    kc[dst + i] = kb[(size_t)row * kvd + i];
+    vc[dst + i] = vb[(size_t)row * kvd + i];
+  }
+}
+
+hipError_t launch_kv_append(bool is_bf16, const void *kb, const void *vb, void *kc, void *vc, const int *block_table,
+                            const int *ctx_len, int batch, int B, int kvd, int max_pages, int page_size,
+                            hipStream_t st) {
+  if (is_bf16)
+    hipLaunchKernelGGL(kv_append_kernel<bf16_t>, dim3(batch * B), dim3(256), 0, st, (const bf16_t *)kb,
+                       (const bf16_t *)vb, (bf16_t *)kc, (bf16_t *)vc, block_table, ctx_len, B, kvd, max_pages,
+                       page_size);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<float>, dim3(batch * B), dim3(256), 0, st, (const float *)kb,
+                       (const float *)vb, (float *)kc, (float *)vc, block_table, ctx_len, B, kvd, max_pages,
+                       page_size);
+  return hipGetLastError();
+}
+
+// One workgroup per row: X[row, :] (fp32) rounded to the storage type into
+// taps[row, slot * H .. slot * H + H).
+template <typename T>
+__global__ __launch_bounds__(256) void tap_kernel(const float *X, int H, int slot, int n_slots, T *taps) {
+  const int row = blockIdx.x;
+  T *dst = taps + (size_t)row * n_slots * H + (size_t)slot * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) Storage<T>::store(dst, i, X[(size_t)row * H + i]);
+}
+
+hipError_t launch_tap(bool is_bf16, const float *X, int rows, int H, int slot, int n_slots, void *taps,
+                      hipStream_t st) {
+  if (is_bf16)
+    hipLaunchKernelGGL(tap_kernel<bf16_t>, dim3(rows), dim3(256), 0, st, X, H, slot, n_slots, (bf16_t *)taps);
+  else
+    hipLaunchKernelGGL(tap_kernel<float>, dim3(rows), dim3(256), 0, st, X, H, slot, n_slots, (float *)taps);
   return hipGetLastError();
 }
 

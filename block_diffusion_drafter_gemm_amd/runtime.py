@@ -75,7 +75,7 @@ class Drafter:
         c = L.make_config(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn, cfg.vocab,
                           cfg.n_layers, cfg.n_feat_layers, cfg.block_size, cfg.mask_token_id, cfg.dtype,
                           cfg.rope_theta, cfg.rms_eps, cfg.page_size)
-        ws, self._keep = L.make_weights(self.w["embed"], self.w["lm_head"], self.w["w_fc"], self.w["final_norm"],
+        ws, self._keep = L.make_weights(self.w["embed"], self.w["lm_head"], self.w.get("w_fc"), self.w["final_norm"],
                                         *[self.w[k] for k in _LAYER_KEYS])
         self.handle = L.dflash_create(c, ws)
         self.ws_bytes = L.dflash_workspace_size(self.handle, max_batch, max_ctx, max_new)
@@ -103,6 +103,18 @@ class Drafter:
                                      device=self.device)
         L.dflash_draft_block(self.handle, anchor_ids, kv.struct(), hidden_out, self.ws)
         return hidden_out
+
+    def target_verify(self, ids: torch.Tensor, kv: PagedKV, tap_layers=(), hidden_out=None, taps_out=None):
+        """Causal pass of a target handle over ids [batch, B]; returns
+        (hidden [batch*B, H], taps [batch*B, len(tap_layers)*H] or None)."""
+        R = kv.batch * self.cfg.block_size
+        if hidden_out is None:
+            hidden_out = torch.empty((R, self.cfg.hidden), dtype=storage_dtype(self.cfg), device=self.device)
+        if taps_out is None and len(tap_layers):
+            taps_out = torch.empty((R, len(tap_layers) * self.cfg.hidden), dtype=storage_dtype(self.cfg),
+                                   device=self.device)
+        L.dflash_target_verify(self.handle, ids, kv.struct(), list(tap_layers), taps_out, hidden_out, self.ws)
+        return hidden_out, taps_out
 
     def lmhead_argmax(self, hidden: torch.Tensor, want_max: bool = True, want_logits: bool = False):
         rows = int(hidden.shape[0])

@@ -86,7 +86,8 @@ typedef struct {
 typedef struct {
     const void *embed;              /* [vocab, hidden] */
     const void *lm_head;            /* [vocab, hidden] */
-    const void *w_fc;               /* [hidden, n_feat_layers*hidden] fusion projection */
+    const void *w_fc;               /* [hidden, n_feat_layers*hidden] fusion projection;
+                                       may be NULL for a target handle (no inject) */
     const void *final_norm;         /* [hidden] */
     const void *const *attn_norm;   /* n_layers host-array entries, each [hidden] */
     const void *const *w_qkv;       /* [(nq + 2*nkv)*head_dim, hidden]: q rows, k rows, v rows */
@@ -112,8 +113,9 @@ typedef struct {
                                        sizes launch grids and workspace */
 } dflash_kv;
 
-/* Creates a handle for one drafter.  ``cfg`` and ``w`` are host structs read
- * during the call; the weight memory they point to is borrowed until
+/* Creates a handle for one drafter (or, for dflash_target_verify, one target
+ * decoder of the same layer structure).  ``cfg`` and ``w`` are host structs
+ * read during the call; the weight memory they point to is borrowed until
  * dflash_destroy.  Validates shapes only; launches nothing. */
 int dflash_create(const dflash_config *cfg, const dflash_weights *w, dflash_handle *out);
 
@@ -152,6 +154,28 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
  *              states of mask rows 1..B-1 of every sequence (sequence-major). */
 int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_kv *kv, void *hidden_out,
                        void *ws, size_t ws_bytes, void *stream);
+
+/* Target verify: one causal pass of a target decoder (a handle created from
+ * its config and weights; cfg.block_size = rows per sequence) over the tokens
+ * ids[s][0..B-1] at positions ctx_len[s] .. ctx_len[s]+B-1.  The target checks
+ * the whole drafted block in one forward pass ([FN] §1 and the §2 cycle) and
+ * its hidden states at uniformly spaced layers become the drafter's context
+ * features ([SUM] §2.2; [INS]).  Each row attends to the context and to the
+ * block rows up to itself; every layer's block K/V are written to the cache at
+ * those positions (ctx_len is not changed: the caller advances it by the
+ * accepted length, and a later call overwrites the rest).  The same call with
+ * B = prompt length serves as the prefill.
+ *   ids        [kv->batch, B] int32 token ids
+ *   tap_layers HOST [n_taps] 0-indexed layers (< n_layers), 0 <= n_taps <= 16
+ *   taps_out   [kv->batch * B, n_taps * hidden] storage type: the residual
+ *              stream after layer tap_layers[i] (before the final norm) in
+ *              column block i; may be NULL when n_taps == 0
+ *   hidden_out [kv->batch * B, hidden] storage type: final-norm hidden states
+ *              of every row; dflash_lmhead_argmax turns them into y_1..y_B.
+ * Errors: NULL pointers, n_taps out of range (DFLASH_ERR_SHAPE), a tap layer
+ * out of range (DFLASH_ERR_RANGE), a workspace below dflash_workspace_size. */
+int dflash_target_verify(dflash_handle h, const int32_t *ids, const dflash_kv *kv, const int32_t *tap_layers,
+                         int32_t n_taps, void *taps_out, void *hidden_out, void *ws, size_t ws_bytes, void *stream);
 
 /* A9: shared LM head and greedy argmax ([FN] §3.1; [SUM] §2.3).
  * logits = hidden * lm_head^T in fp32; ids_out[r] = the lowest id among the

@@ -92,8 +92,45 @@ def test_create_rejects_null(lib):
     assert lib.dflash_create(None, None, ctypes.byref(h)) == -1
     cfg = good_config()
     w, keep = fake_weights()
-    w.w_fc = None
+    w.embed = None
     assert lib.dflash_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)) == -1
+
+
+def test_target_handle_without_fusion_weights(lib):
+    # a target decoder has no fusion projection: creation accepts it, inject refuses
+    cfg = good_config()
+    w, keep = fake_weights()
+    w.w_fc = None
+    h = ctypes.c_void_p()
+    assert lib.dflash_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)) == 0 and h.value
+    try:
+        kv = L.DflashKV(FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 64)
+        n1 = L.dflash_workspace_size(h.value, 1, 64, 16)
+        assert lib.dflash_inject_context(h.value, FAKE, FAKE, FAKE, 4, ctypes.byref(kv), FAKE, n1, None) == -1
+    finally:
+        assert lib.dflash_destroy(h.value) == 0
+
+
+def test_target_verify_host_validation(lib):
+    st, h = create(good_config())
+    assert st == 0 and h
+    try:
+        n1 = L.dflash_workspace_size(h, 1, 64, 16)
+        kv = L.DflashKV(FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 64)
+        taps = (ctypes.c_int32 * 2)(0, 1)
+        bad_taps = (ctypes.c_int32 * 2)(0, 2)        # layer 2 of a 2-layer decoder
+        tv = lib.dflash_target_verify
+        assert tv(h, None, ctypes.byref(kv), taps, 2, FAKE, FAKE, FAKE, n1, None) == -1
+        assert tv(h, FAKE, ctypes.byref(kv), taps, 2, None, FAKE, FAKE, n1, None) == -1
+        assert tv(h, FAKE, ctypes.byref(kv), None, 2, FAKE, FAKE, FAKE, n1, None) == -1
+        assert tv(h, FAKE, ctypes.byref(kv), taps, -1, FAKE, FAKE, FAKE, n1, None) == -2
+        assert tv(h, FAKE, ctypes.byref(kv), taps, 17, FAKE, FAKE, FAKE, n1, None) == -2
+        assert tv(h, FAKE, ctypes.byref(kv), bad_taps, 2, FAKE, FAKE, FAKE, n1, None) == -4
+        assert tv(h, FAKE, ctypes.byref(kv), taps, 2, FAKE, FAKE, FAKE, 1024, None) == -5
+        bad = L.DflashKV(FAKE, FAKE, FAKE, FAKE, 0, 8, 8, 64)
+        assert tv(h, FAKE, ctypes.byref(bad), taps, 2, FAKE, FAKE, FAKE, n1, None) == -2
+    finally:
+        assert lib.dflash_destroy(h) == 0
 
 
 def test_workspace_size_and_host_validation(lib):
