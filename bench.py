@@ -35,6 +35,10 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="report eager launches only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--inject", action="store_true", help="also time steady-state inject (B positions)")
+    ap.add_argument("--e2e", type=int, default=0, metavar="LAYERS",
+                    help="also time the target side of the cycle with a LAYERS-layer target of the drafter's "
+                         "layer shape (random weights, shared embedding and LM head): block verify, one-token "
+                         "decode, and the speculative cycle")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -143,6 +147,85 @@ def cpu_baseline(cfg, w, Kp, Vp, lay, lens, anchors, y, min_seconds=10.0, max_st
             "cores": int(cores), "kind": "oracle", "seconds": round(dt, 2), "single_thread": single,
             "sample": f"{steps} draft steps of sequence 0 ({cfg.block_size - 1} drafted tokens each, context "
                       f"{int(lens[0])}) in float64 numpy"}
+
+
+def e2e_cycle(args, cfg, R, dr, lens, b, B, draft_step_ms, inject_ms):
+    """Target side of the speculative cycle on this GPU: a target decoder of the
+    drafter's layer shape with ``args.e2e`` layers (weights N(0, 0.02^2) drawn on
+    the device; embedding and LM head shared with the drafter), its paged cache
+    filled to the same context lengths, feature taps at 5 uniformly spaced
+    layers.  Times one block verify (B rows + LM head argmax over B rows), one
+    plain decode step (a 2-row block, the second row hidden by the causal mask)
+    and the cycle (draft step + verify + inject of B positions); the speedup
+    over plain decoding follows for a mean acceptance length tau as
+    tau * decode / cycle."""
+    import dataclasses
+    import numpy as np
+    import torch
+
+    import dflash_synth as S
+    nL = args.e2e
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+
+    def normal(shape):
+        return (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * 0.02).to(
+            torch.bfloat16).view(torch.int16)
+
+    H, F, d = cfg.hidden, cfg.ffn, cfg.head_dim
+    qkv = (cfg.n_q_heads + 2 * cfg.n_kv_heads) * d
+    ones = torch.ones(H, dtype=torch.bfloat16, device="cuda").view(torch.int16)
+    tw = {"embed": dr.w["embed"], "lm_head": dr.w["lm_head"], "final_norm": ones,
+          "attn_norm": [ones] * nL, "mlp_norm": [ones] * nL,
+          "w_qkv": [normal((qkv, H)) for _ in range(nL)], "w_o": [normal((H, cfg.n_q_heads * d)) for _ in range(nL)],
+          "w_gate_up": [normal((2 * F, H)) for _ in range(nL)], "w_down": [normal((H, F)) for _ in range(nL)]}
+    taps = [int(round(i * (nL - 1) / 4)) for i in range(5)]
+    max_ctx = int(lens.max())
+    tv = {Bt: R.Drafter(dataclasses.replace(cfg, n_layers=nL, block_size=Bt), tw, max_batch=b, max_ctx=max_ctx,
+                        max_new=1) for Bt in (B, 2)}
+    tcfg = dataclasses.replace(cfg, n_layers=nL, block_size=B)
+    lay = S.paged_layout(tcfg, lens, headroom=B, seed=3)
+    shape = (nL, lay.n_pages, cfg.page_size, cfg.n_kv_heads, d)
+    sig = S.kv_sigma(cfg)
+    kc = (torch.randn(shape, generator=gen, device="cuda") * sig).to(torch.bfloat16).view(torch.int16)
+    vc = (torch.randn(shape, generator=gen, device="cuda") * sig).to(torch.bfloat16).view(torch.int16)
+    tkv = R.PagedKV(tcfg, lay.block_table, lens, lay.n_pages)
+    tkv.k, tkv.v = kc, vc
+    out = {}
+    for Bt, name in ((B, "verify"), (2, "decode")):
+        h = tv[Bt]
+        ids = torch.randint(0, cfg.vocab, (b, Bt), generator=gen, device="cuda", dtype=torch.int32)
+        hid = torch.empty((b * Bt, H), dtype=torch.int16, device="cuda")
+        tp = torch.empty((b * Bt, len(taps) * H), dtype=torch.int16, device="cuda")
+
+        def once():
+            h.target_verify(ids, tkv, taps, hidden_out=hid, taps_out=tp)
+            h.lmhead_argmax(hid, want_max=False)
+        for _ in range(3):
+            once()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            once()
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"target_{name}_ms"] = round(e0.elapsed_time(e1) / args.steps, 4)
+    for h in tv.values():
+        h.close()
+    weight_bytes = nL * (qkv * H + H * cfg.n_q_heads * d + 3 * F * H) * 2 + cfg.vocab * H * 2
+    cycle = draft_step_ms + out["target_verify_ms"] + (inject_ms or 0.0)
+    a = 0.7   # the synthetic per-position agreement of the verify targets
+    tau_syn = (1 - a ** B) / (1 - a)
+    out.update({
+        "target": f"{nL} layers of the drafter's shape, hidden {H}, vocab {cfg.vocab}, taps {taps}",
+        "target_weight_bytes": int(weight_bytes),
+        "target_verify_hbm_gbs": round(weight_bytes / (out["target_verify_ms"] / 1e3) / 1e9, 1),
+        "cycle_ms": round(cycle, 4), "inject_in_cycle": inject_ms is not None,
+        "speedup_at_tau": {f"{tau_syn:.2f} (70% agreement, B={B})": round(tau_syn * out["target_decode_ms"] / cycle, 2),
+                           "6.49 (the pages' mean at B=16, context only)":
+                               round(6.49 * out["target_decode_ms"] / cycle, 2)},
+    })
+    return out
 
 
 def main():
@@ -350,6 +433,8 @@ def main():
         out["inject_prefill_ms"] = round(p0.elapsed_time(p1) / 3, 4)
         out["inject_prefill_positions"] = T
         drp.close()
+    if args.e2e > 0:
+        out["e2e"] = e2e_cycle(args, cfg, R, dr, lens, b, B, ms, out.get("inject_steady_ms"))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, w, Kp, Vp, lay, lens, anchors, y)
     dr.close()

@@ -7,7 +7,7 @@
 
 namespace dflash {
 
-constexpr int kMaxLayers = 16;
+constexpr int kMaxLayers = 64;
 
 enum Epilogue {
   EPI_STORE = 0,      // out[row, col] = acc (storage type)

@@ -19,7 +19,10 @@ _LAYER_KEYS = ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down")
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
-    """Host array -> device tensor with the same bytes (bf16 bits travel as int16)."""
+    """Host array -> device tensor with the same bytes (bf16 bits travel as int16);
+    a torch tensor already on the device is kept as it is."""
+    if isinstance(a, torch.Tensor):
+        return a.to(device)
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(device)

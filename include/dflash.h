@@ -61,7 +61,7 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 /* Drafter shape.  Supported: head_dim in {64, 128}; n_q_heads a multiple of
  * n_kv_heads; (n_q_heads / n_kv_heads) * block_size <= 128; 2 <= block_size
  * <= 64; hidden, n_q_heads*head_dim and ffn multiples of 64; hidden <= 16384;
- * vocab a multiple of 16; page_size 16; 1 <= n_layers <= 16.  The mask token is a row of the
+ * vocab a multiple of 16; page_size 16; 1 <= n_layers <= 64.  The mask token is a row of the
  * shared embedding (mask_token_id < vocab). */
 typedef struct {
     int32_t hidden;
@@ -166,7 +166,7 @@ int dflash_draft_block(dflash_handle h, const int32_t *anchor_ids, const dflash_
  * accepted length, and a later call overwrites the rest).  The same call with
  * B = prompt length serves as the prefill.
  *   ids        [kv->batch, B] int32 token ids
- *   tap_layers HOST [n_taps] 0-indexed layers (< n_layers), 0 <= n_taps <= 16
+ *   tap_layers HOST [n_taps] 0-indexed layers (< n_layers), 0 <= n_taps <= 64
  *   taps_out   [kv->batch * B, n_taps * hidden] storage type: the residual
  *              stream after layer tap_layers[i] (before the final norm) in
  *              column block i; may be NULL when n_taps == 0

@@ -73,7 +73,7 @@ def create(cfg):
     (dict(head_dim=96), -2), (dict(n_q_heads=5), -2), (dict(hidden=100), -2), (dict(hidden=16384 + 64), -2),
     (dict(ffn=100), -2),
     (dict(vocab=1000 + 3), -2), (dict(block_size=1), -2), (dict(block_size=65), -2), (dict(n_layers=0), -2),
-    (dict(n_layers=17), -2), (dict(mask_token_id=1024), -4), (dict(dtype="bf16", rope_theta=0.0), -4),
+    (dict(n_layers=65), -2), (dict(mask_token_id=1024), -4), (dict(dtype="bf16", rope_theta=0.0), -4),
     (dict(n_q_heads=32, n_kv_heads=1, block_size=16), -2),
 ])
 def test_create_rejects_bad_config(lib, bad, code):
@@ -124,7 +124,7 @@ def test_target_verify_host_validation(lib):
         assert tv(h, FAKE, ctypes.byref(kv), taps, 2, None, FAKE, FAKE, n1, None) == -1
         assert tv(h, FAKE, ctypes.byref(kv), None, 2, FAKE, FAKE, FAKE, n1, None) == -1
         assert tv(h, FAKE, ctypes.byref(kv), taps, -1, FAKE, FAKE, FAKE, n1, None) == -2
-        assert tv(h, FAKE, ctypes.byref(kv), taps, 17, FAKE, FAKE, FAKE, n1, None) == -2
+        assert tv(h, FAKE, ctypes.byref(kv), taps, 65, FAKE, FAKE, FAKE, n1, None) == -2
         assert tv(h, FAKE, ctypes.byref(kv), bad_taps, 2, FAKE, FAKE, FAKE, n1, None) == -4
         assert tv(h, FAKE, ctypes.byref(kv), taps, 2, FAKE, FAKE, FAKE, 1024, None) == -5
         bad = L.DflashKV(FAKE, FAKE, FAKE, FAKE, 0, 8, 8, 64)
