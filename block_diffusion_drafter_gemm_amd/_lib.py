@@ -33,7 +33,7 @@ class DflashConfig(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("n_layers", ctypes.c_int32), ("n_feat_layers", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("mask_token_id", ctypes.c_int32), ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+                ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("window", ctypes.c_int32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -168,10 +168,10 @@ def dflash_accept_len(draft_ids, target_ids, batch: int, block_size: int, accept
 # ----------------------------------------------------------------------------
 def make_config(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ffn: int, vocab: int, n_layers: int,
                 n_feat_layers: int, block_size: int, mask_token_id: int, dtype: str, rope_theta: float,
-                rms_eps: float, page_size: int = 16) -> DflashConfig:
+                rms_eps: float, page_size: int = 16, window: int = 0) -> DflashConfig:
     return DflashConfig(hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, n_layers, n_feat_layers, block_size,
                         mask_token_id, page_size, DFLASH_BF16 if dtype == "bf16" else DFLASH_F32,
-                        float(rope_theta), float(rms_eps))
+                        float(rope_theta), float(rms_eps), int(window))
 
 
 def make_weights(embed, lm_head, w_fc, final_norm, attn_norm: Sequence, w_qkv: Sequence, w_o: Sequence,

@@ -49,15 +49,20 @@ int attn_max_items(int batch, int max_ctx, int block_size, int nkv, int chunk) {
   return batch * ((max_ctx + block_size + chunk - 1) / chunk) * nkv;
 }
 
+// Context keys a sequence attends to: all ctx of them, or with a sliding
+// window the last `window` (the block keys always).
+__device__ __forceinline__ int attended_ctx(int ctx, int window) { return window > 0 ? min(ctx, window) : ctx; }
+
 // Locate flat chunk index f among the sequences (chunks per sequence =
-// ceil((ctx_len + B) / chunk)).  Executed by one wave; returns seq (-1 when f
-// is beyond the total) and the sequence's first flat chunk index.
-__device__ void find_seq(const int *ctx_len, int batch, int B, int chunk, int f, int *seq_out, int *first_out) {
+// ceil((attended context + B) / chunk)).  Executed by one wave; returns seq
+// (-1 when f is beyond the total) and the sequence's first flat chunk index.
+__device__ void find_seq(const int *ctx_len, int window, int batch, int B, int chunk, int f, int *seq_out,
+                         int *first_out) {
   const int lane = threadIdx.x & 63;
   int base = 0;
   for (int s0 = 0; s0 < batch; s0 += 64) {
     const int s = s0 + lane;
-    const int n = s < batch ? (ctx_len[s] + B + chunk - 1) / chunk : 0;
+    const int n = s < batch ? (attended_ctx(ctx_len[s], window) + B + chunk - 1) / chunk : 0;
     int inc = n;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
   const int f = item / a.nkv, g = item % a.nkv;
   if (wave == 0) {
     int sq, first;
-    find_seq(a.ctx_len, a.batch, a.block_size, a.chunk, f, &sq, &first);
+    find_seq(a.ctx_len, a.window, a.batch, a.block_size, a.chunk, f, &sq, &first);
     if (lane == 0) { s_seq = sq; s_first = first; }
   }
   __syncthreads();
@@ -110,7 +115,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
   const int c = f - s_first;
   const int B = a.block_size, G = a.nq / a.nkv, GB = G * B;
   const int ctx = a.ctx_len[s];
-  const int kbeg = c * a.chunk;
+  // keys k0 .. ctx - 1 of the context (k0 > 0 under a sliding window), then the block
+  const int kbeg = (ctx - attended_ctx(ctx, a.window)) + c * a.chunk;
   const int kend = min(kbeg + a.chunk, ctx + B);
   const int MTQ = (GB + 15) / 16;
   const T *Q = (const T *)a.q;
@@ -349,12 +355,12 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnArgs a) {
   int base = 0;
   for (int s0 = 0; s0 < s; s0 += 64) {
     const int q = s0 + lane;
-    int n = q < s ? (a.ctx_len[q] + B + a.chunk - 1) / a.chunk : 0;
+    int n = q < s ? (attended_ctx(a.ctx_len[q], a.window) + B + a.chunk - 1) / a.chunk : 0;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
     base += n;
   }
-  int nch = (a.ctx_len[s] + B + a.chunk - 1) / a.chunk;
+  int nch = (attended_ctx(a.ctx_len[s], a.window) + B + a.chunk - 1) / a.chunk;
   // chunks past the launched item range were never computed (ctx_len above the
   // declared maximum); never read beyond the partial buffers
   if ((base + nch) * a.nkv > a.max_items) nch = max(0, a.max_items / a.nkv - base);

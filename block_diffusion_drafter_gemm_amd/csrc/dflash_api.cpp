@@ -57,8 +57,10 @@ DraftLayout draft_layout(const dflash_handle_s *h, int batch, int max_ctx, int c
   L.Vb = cv.take((size_t)R * kvd * h->esz);
   L.O = cv.take((size_t)R * qd * h->esz);
   L.Hs = cv.take((size_t)R * c.ffn * h->esz);
-  L.chunk = attn_chunk(batch, max_ctx, B, c.n_q_heads, c.n_kv_heads, cu);
-  L.max_items = attn_max_items(batch, max_ctx, B, c.n_kv_heads, L.chunk);
+  // a sliding window bounds the attended context (and so the chunk items)
+  const int att_ctx = c.window > 0 && c.window < max_ctx ? c.window : max_ctx;
+  L.chunk = attn_chunk(batch, att_ctx, B, c.n_q_heads, c.n_kv_heads, cu);
+  L.max_items = attn_max_items(batch, att_ctx, B, c.n_kv_heads, L.chunk);
   const int GB = (c.n_q_heads / c.n_kv_heads) * B, GBP = (GB + 15) / 16 * 16;
   L.attn_part = cv.take((size_t)L.max_items * GBP * c.head_dim * 4);
   L.attn_stats = cv.take((size_t)L.max_items * GBP * 2 * 4);
@@ -179,6 +181,7 @@ int validate_config(const dflash_config *c) {
   if (c->page_size != 16) return DFLASH_ERR_SHAPE;
   if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return DFLASH_ERR_RANGE;
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return DFLASH_ERR_RANGE;
+  if (c->window < 0) return DFLASH_ERR_RANGE;
   return DFLASH_OK;
 }
 
@@ -414,6 +417,7 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
     at.chunk = L.chunk;
     at.max_items = L.max_items;
     at.causal = verify ? 1 : 0;
+    at.window = c.window;
     if (launch_attention(h->bf16, at, s) != hipSuccess) return DFLASH_ERR_HIP;
     // target verify: the block's K/V join the context cache (the caller keeps
     // the accepted positions by advancing ctx_len; later blocks overwrite the rest)

@@ -100,6 +100,7 @@ struct AttnArgs {
   float *stats;           // [items][GB_pad][2]
   int batch, block_size, nq, nkv, hd, max_pages, page_size, chunk, max_items;
   int causal;             // block row j sees block keys 0..j only (target verify)
+  int window;             // > 0: only the last `window` context keys are attended
 };
 hipError_t launch_attention(bool is_bf16, const AttnArgs &a, hipStream_t st);
 int attn_chunk(int batch, int max_ctx, int block_size, int nq, int nkv, int cu);

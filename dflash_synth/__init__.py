@@ -60,6 +60,7 @@ class Config:
     rms_eps: float = 1e-6
     page_size: int = 16
     match_rate: float = 0.7     # synthetic target agreement per position
+    window: int = 0             # > 0: sliding-window context (last `window` positions)
     # tiny end-to-end target (only the "tiny" configuration)
     target_layers: int = 0
     feat_layer_ids: Tuple[int, ...] = ()

@@ -78,6 +78,9 @@ typedef struct {
     int32_t dtype;           /* dflash_dtype */
     float rope_theta;
     float rms_eps;
+    int32_t window;                 /* 0: attend to the whole context; > 0: a sliding
+                                       window over the last `window` context positions
+                                       (long-context use; the block is always attended) */
 } dflash_config;
 
 /* Device pointers to the drafter's weights (borrowed for the handle's

@@ -145,6 +145,13 @@ def draft_block(w: dict, cfg, anchor: int, K_ctx: np.ndarray, V_ctx: np.ndarray,
     B, H = cfg.block_size, cfg.hidden
     nq, nkv, d, F = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn
     p = K_ctx.shape[1]
+    W = getattr(cfg, "window", 0)
+    if W and p > W:
+        # sliding-window context: only the last W positions are attended; the
+        # block keeps its absolute positions p .. p+B-1 ([PKR] usage notes:
+        # long-context inference with a sliding-window KV cache)
+        K_ctx, V_ctx = K_ctx[:, p - W:], V_ctx[:, p - W:]
+    pc = K_ctx.shape[1]
     ids = np.array([anchor] + [cfg.mask_token_id] * (B - 1), dtype=np.int64)
     pos = np.arange(p, p + B) if positions is None else np.asarray(positions)
     res = (lambda a: a) if dt == "f64" else round_f32   # fp32 residual stream
@@ -161,7 +168,7 @@ def draft_block(w: dict, cfg, anchor: int, K_ctx: np.ndarray, V_ctx: np.ndarray,
         q, k, v = round_storage(q, dt), round_storage(k, dt), round_storage(v, dt)
         Kall = np.concatenate([K_ctx[l], k], axis=0)
         Vall = np.concatenate([V_ctx[l], v], axis=0)
-        O = round_storage(attention(q, Kall, Vall, causal_from=p if causal else None), dt)
+        O = round_storage(attention(q, Kall, Vall, causal_from=pc if causal else None), dt)
         X = res(X + O.reshape(B, nq * d) @ _w(w["w_o"][l]).T)
         Y = round_storage(rms_norm(X, _w(w["mlp_norm"][l]), cfg.rms_eps), dt)
         gu = Y @ _w(w["w_gate_up"][l]).T

@@ -6,6 +6,8 @@ Token ids and accept lengths must match exactly (ids may differ only on an
 oracle near-tie); hidden states, cache entries and logits must be within
 1e-4 (fp32) or 2e-2 (bf16) of the oracle, scaled by max(1, |oracle|).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -199,6 +201,14 @@ def run_draft_case(cfg, seed=0, lens=None, check_seqs=None):
 def test_draft_block(name):
     log(f"draft_block {name}")
     run_draft_case(MINI[name], seed=0)
+
+
+@pytest.mark.parametrize("name,window", [("mini_bf16", 100), ("mini_d64", 50), ("mini_f32", 40)])
+def test_draft_block_sliding_window(name, window):
+    """Sliding-window context (ragged contexts above and below the window;
+    streaming and many-rows paths) against the oracle's windowed pass."""
+    log(f"draft_block {name} window={window}")
+    run_draft_case(dataclasses.replace(MINI[name], window=window), seed=4)
 
 
 def test_draft_block_empty_and_short_context():

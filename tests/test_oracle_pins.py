@@ -326,6 +326,30 @@ def test_context_permutation_invariance_and_causality():
     assert np.max(np.abs(D.draft_block(w2, cfg, anchor, K, V) - Z)) > 1e-6
 
 
+def test_sliding_window_reads_only_the_last_positions():
+    """With a sliding window of W positions the drafter's output does not
+    depend on older context K/V, depends on every position inside the window,
+    and equals the full-context pass when W covers the context (or W = 0)."""
+    cfg = small_cfg("f64", ctx_min=12, ctx_max=12, block_size=4)
+    w, feats, K, V, anchor = small_setup(cfg)
+    p, W = K.shape[1], 5
+    full = D.draft_block(w, cfg, anchor, K, V)
+    for wide in (0, p, p + 3):
+        np.testing.assert_array_equal(D.draft_block(w, dataclasses.replace(cfg, window=wide), anchor, K, V), full)
+    cw = dataclasses.replace(cfg, window=W)
+    Zw = D.draft_block(w, cw, anchor, K, V)
+    assert np.max(np.abs(Zw - full)) > 1e-6
+    rng = np.random.default_rng(11)
+    K2, V2 = K.copy(), V.copy()
+    K2[:, :p - W] = rng.normal(size=K2[:, :p - W].shape)
+    V2[:, :p - W] = rng.normal(size=V2[:, :p - W].shape)
+    np.testing.assert_array_equal(D.draft_block(w, cw, anchor, K2, V2), Zw)
+    for t in (p - W, p - 1):                          # the window's edges
+        K3 = K.copy()
+        K3[:, t] = rng.normal(size=K3[:, t].shape)
+        assert np.max(np.abs(D.draft_block(w, cw, anchor, K3, V) - Zw)) > 1e-9
+
+
 # ----------------------------------------------------------------------------
 # P6: context injection
 # ----------------------------------------------------------------------------
