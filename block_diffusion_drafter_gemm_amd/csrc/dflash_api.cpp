@@ -384,7 +384,14 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
       q.anchor = anchor_ids;
       q.mask_id = c.mask_token_id;
       q.ids = ids;
-      st = launch_stream(h, EPI_QKV, l == 0 ? AM_EMBED_NORM : AM_NORM, q, 1, s);
+      if (verify) {   // the block's k, v go to the cache from the QKV epilogue
+        q.kc_out = static_cast<char *>(kv->k) + l * cache_layer;
+        q.vc_out = static_cast<char *>(kv->v) + l * cache_layer;
+        q.block_table = kv->block_table;
+        q.max_pages = kv->max_pages;
+        q.page_size = c.page_size;
+      }
+      st = launch_stream(h, verify ? EPI_QKV_CACHE : EPI_QKV, l == 0 ? AM_EMBED_NORM : AM_NORM, q, 1, s);
     } else {
       if (launch_rmsnorm(h->bf16, X, h->attn_norm[l], c.rms_eps, R, c.hidden, B, false, w + L.Y, s) != hipSuccess)
         return DFLASH_ERR_HIP;
@@ -421,7 +428,9 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
     if (launch_attention(h->bf16, at, s) != hipSuccess) return DFLASH_ERR_HIP;
     // target verify: the block's K/V join the context cache (the caller keeps
     // the accepted positions by advancing ctx_len; later blocks overwrite the rest)
-    if (verify && launch_kv_append(h->bf16, w + L.Kb, w + L.Vb, static_cast<char *>(kv->k) + l * cache_layer,
+    // (the streaming path's QKV epilogue has already written them)
+    if (verify && !fast &&
+        launch_kv_append(h->bf16, w + L.Kb, w + L.Vb, static_cast<char *>(kv->k) + l * cache_layer,
                                    static_cast<char *>(kv->v) + l * cache_layer, kv->block_table, kv->ctx_len, batch,
                                    B, kvd, kv->max_pages, c.page_size, s) != hipSuccess)
       return DFLASH_ERR_HIP;

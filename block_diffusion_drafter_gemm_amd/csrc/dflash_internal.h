@@ -17,6 +17,8 @@ enum Epilogue {
   EPI_QKV = 4,        // RoPE(q), RoPE(k), v -> block q/k/v buffers
   EPI_INJECT = 5,     // RoPE(k), v -> paged context cache
   EPI_ARGMAX = 6,     // per-row (max, lowest argmax) over the column group
+  EPI_QKV_CACHE = 7,  // EPI_QKV, and the block's k, v also into the paged cache
+                      // (target verify; streaming GEMM only)
 };
 
 struct GemmArgs {
@@ -36,6 +38,7 @@ struct GemmArgs {
   int ldx;
   // EPI_QKV / EPI_INJECT
   void *q_out, *k_out, *v_out;
+  void *kc_out, *vc_out;  // EPI_QKV_CACHE: this layer's paged cache (block k, v at ctx + j)
   const int *ctx_len;
   int block_size, nq, nkv, hd;
   double log2_theta;

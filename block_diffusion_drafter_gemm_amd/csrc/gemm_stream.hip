@@ -29,6 +29,9 @@ constexpr int kSResBytes = 128 * 1024;   // LDS budget of the resident activatio
 
 enum AMode { A_GLOBAL = 0, A_COPY = 1, A_NORM = 2, A_EMBED_NORM = 3, A_COPY_ROWS = 6 };
 
+// the QKV epilogues (with or without the copy into the paged cache)
+constexpr bool qkv_epi(int e) { return e == EPI_QKV || e == EPI_QKV_CACHE; }
+
 template <typename T>
 __host__ __device__ constexpr int stream_res_k() {
   return kSResBytes / (16 * (int)sizeof(T));
@@ -38,7 +41,7 @@ template <int EPI>
 __device__ __forceinline__ int s_weight_row(const GemmArgs &a, int t, int c) {
   if constexpr (EPI == EPI_SWIGLU) {
     return c < 8 ? t * 8 + c : a.ffn + t * 8 + (c - 8);
-  } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
+  } else if constexpr (qkv_epi(EPI) || EPI == EPI_INJECT) {
     const int tph = a.hd / 16;
     const int h = t / tph, j0 = (t - h * tph) * 8;
     return h * a.hd + (c < 8 ? j0 + c : a.hd / 2 + j0 + (c - 8));
@@ -55,16 +58,17 @@ __device__ __forceinline__ int s_weight_row(const GemmArgs &a, int t, int c) {
 struct EpiPre {
   float x;
   int ctx;
+  int page;   // QKV with a cache copy: page of the thread's row position (read after the staging loads)
 };
 
 template <int EPI>
 __device__ __forceinline__ EpiPre s_epi_pre(const GemmArgs &a, int t0) {
-  EpiPre p{0.f, 0};
+  EpiPre p{0.f, 0, 0};
   const int tid = threadIdx.x;
   if constexpr (EPI == EPI_RESID) {
     const int r = min(tid >> 4, a.M - 1), c = tid & 15;
     p.x = a.X[(size_t)r * a.ldx + t0 * 16 + c];
-  } else if constexpr (EPI == EPI_QKV) {
+  } else if constexpr (qkv_epi(EPI)) {
     p.ctx = a.ctx_len[min(tid >> 3, a.M - 1) / a.block_size];
   }
   return p;
@@ -108,12 +112,12 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
         Storage<T>::store((T *)a.out, (size_t)r * a.ldo + t * 8 + c, gt / (1.0f + expf(-gt)) * up);
       }
     }
-  } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
+  } else if constexpr (qkv_epi(EPI) || EPI == EPI_INJECT) {
     if (tid < 128) {
       const int r = tid >> 3, c = tid & 7;
       if (r < a.M) {
         const int hd = a.hd, half = hd / 2;
-        const int nqh = (EPI == EPI_QKV) ? a.nq : 0;  // q heads in the output
+        const int nqh = (qkv_epi(EPI)) ? a.nq : 0;  // q heads in the output
         const int qcols = nqh * hd;
         const int kcols = a.nkv * hd;
         const int h = t / (hd / 16);                  // head of this tile (uniform)
@@ -122,7 +126,7 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
         const float x1 = ct[r * 16 + c], x2 = ct[r * 16 + 8 + c];
         int pos;
         size_t slot = 0;
-        if constexpr (EPI == EPI_QKV) {
+        if constexpr (qkv_epi(EPI)) {
           pos = pre.ctx + r % a.block_size;
         } else {
           pos = a.pos[r];
@@ -145,13 +149,23 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
           off = (size_t)r * qcols + n;
         } else if (h < nqh + a.nkv) {
           dst = (T *)a.k_out;
-          off = (EPI == EPI_QKV ? (size_t)r * kcols : slot) + (n - qcols);
+          off = (qkv_epi(EPI) ? (size_t)r * kcols : slot) + (n - qcols);
         } else {
           dst = (T *)a.v_out;
-          off = (EPI == EPI_QKV ? (size_t)r * kcols : slot) + (n - qcols - kcols);
+          off = (qkv_epi(EPI) ? (size_t)r * kcols : slot) + (n - qcols - kcols);
         }
         Storage<T>::store(dst, off, lo);
         Storage<T>::store(dst, off + half, hi);
+        if constexpr (EPI == EPI_QKV_CACHE) {
+          if (h >= nqh) {   // target verify: the block's k, v also join the cache
+            const int pos = pre.ctx + r % a.block_size;
+            const size_t cs = ((size_t)pre.page * a.page_size + pos % a.page_size) * kcols +
+                              (h < nqh + a.nkv ? n - qcols : n - qcols - kcols);
+            T *cdst = (T *)(h < nqh + a.nkv ? a.kc_out : a.vc_out);
+            Storage<T>::store(cdst, cs, lo);
+            Storage<T>::store(cdst, cs + half, hi);
+          }
+        }
       }
     }
   } else if constexpr (EPI == EPI_ARGMAX) {
@@ -270,12 +284,22 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   __shared__ double inv_freq[64];   // RoPE inverse frequencies (head_dim <= 128)
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, ln = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  EpiPre pre{0.f, 0, 0};   // set below, before the staging loads
   // RoPE inverse frequencies, computed once the first loads are in flight;
   // the barriers of the staging and of every tile's reduction publish them
-  // before the first epilogue reads them
+  // before the first epilogue reads them.  With a cache copy (target verify)
+  // the page of the thread's row position is read here too, behind the
+  // staging and weight loads, so no wait holds them back.
   auto init_rope = [&]() {
-    if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
+    if constexpr (qkv_epi(EPI) || EPI == EPI_INJECT) {
       if (tid < a.hd / 2) inv_freq[tid] = rope_inv_freq(tid, a.hd, a.log2_theta);
+    }
+    if constexpr (EPI == EPI_QKV_CACHE) {
+      {
+        const int r = min(tid >> 3, a.M - 1);
+        pre.page = a.block_table[(size_t)(r / a.block_size) * a.max_pages +
+                                 (pre.ctx + r % a.block_size) / a.page_size];
+      }
     }
   };
   const T *W = (const T *)a0.W[layer];
@@ -299,7 +323,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
     BUF.template issue<EPI>(a, W, arow, tile_of(live_ ? (Q) : 0), live_ ? cbeg + ((Q) % nb) * U : d_, \
                             live_ ? clast : d_);                                               \
   }
-  const EpiPre pre = s_epi_pre<EPI>(a, tile_of(0));
+  pre = s_epi_pre<EPI>(a, tile_of(0));
   const T *A = (const T *)a.A;
   const bool row_ok = ln < a.M;
   const T *arow = RES ? reinterpret_cast<const T *>(a_lds + ln * ASTR) + 8 * g
@@ -462,7 +486,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_portion_kernel(const GemmArgs 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, ln = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = blockIdx.x;
-  if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
+  if constexpr (qkv_epi(EPI) || EPI == EPI_INJECT) {
     if (tid < a.hd / 2) inv_freq[tid] = rope_inv_freq(tid, a.hd, a.log2_theta);
   }
   const T *W = (const T *)a.W[layer];
@@ -576,6 +600,7 @@ static hipError_t launch_st(Epilogue epi, int am, const GemmArgs &a, dim3 grid, 
     case EPI_RESID: return launch_s<T, EPI_RESID>(am, a, grid, st);
     case EPI_SWIGLU: return launch_s<T, EPI_SWIGLU>(am, a, grid, st);
     case EPI_QKV: return launch_s<T, EPI_QKV>(am, a, grid, st);
+    case EPI_QKV_CACHE: return launch_s<T, EPI_QKV_CACHE>(am, a, grid, st);
     case EPI_INJECT: return launch_s<T, EPI_INJECT>(am, a, grid, st);
     case EPI_ARGMAX: return launch_s<T, EPI_ARGMAX>(am, a, grid, st);
     default: return hipErrorInvalidValue;
