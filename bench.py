@@ -67,7 +67,8 @@ def step_flops(cfg, lens):
 
 PROFILE = os.path.join(ROOT, "profiles", "lmhead_argmax_qwen3_8b_b1.md")
 KERNEL_SOURCES = ["block_diffusion_drafter_gemm_amd/csrc/gemm_stream.hip",
-                  "block_diffusion_drafter_gemm_amd/csrc/dflash_device.h"]
+                  "block_diffusion_drafter_gemm_amd/csrc/dflash_device.h",
+                  "block_diffusion_drafter_gemm_amd/csrc/dflash_internal.h"]
 
 
 def read_stream_gbs(torch, nbytes=1 << 30, reps=10):
