@@ -19,7 +19,7 @@ DFLASH_F32, DFLASH_BF16 = 0, 1
 
 EXPORTS = ("dflash_create", "dflash_destroy", "dflash_workspace_size", "dflash_workspace_init",
            "dflash_inject_context", "dflash_draft_block", "dflash_target_verify", "dflash_lmhead_argmax",
-           "dflash_accept_len", "dflash_stream_read", "dflash_status_str")
+           "dflash_accept_len", "dflash_accept_len_ragged", "dflash_stream_read", "dflash_status_str")
 
 
 class DflashError(RuntimeError):
@@ -48,7 +48,7 @@ class DflashWeights(ctypes.Structure):
 class DflashKV(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("ctx_len", ctypes.c_void_p), ("batch", ctypes.c_int32), ("max_pages", ctypes.c_int32),
-                ("n_pages", ctypes.c_int32), ("max_ctx", ctypes.c_int32)]
+                ("n_pages", ctypes.c_int32), ("max_ctx", ctypes.c_int32), ("block_len", ctypes.c_void_p)]
 
 
 _lib = None
@@ -73,6 +73,7 @@ def load() -> ctypes.CDLL:
     lib.dflash_target_verify.argtypes = [vp, vp, ctypes.POINTER(DflashKV), vp, i32, vp, vp, vp, sz, vp]
     lib.dflash_lmhead_argmax.argtypes = [vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.dflash_accept_len.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    lib.dflash_accept_len_ragged.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
     lib.dflash_stream_read.argtypes = [vp, sz, vp, vp]
     lib.dflash_status_str.argtypes = [ctypes.c_int]
     lib.dflash_status_str.restype = ctypes.c_char_p
@@ -163,6 +164,14 @@ def dflash_accept_len(draft_ids, target_ids, batch: int, block_size: int, accept
            "dflash_accept_len")
 
 
+def dflash_accept_len_ragged(draft_ids, target_ids, batch: int, block_size: int, block_len, accept_len_out,
+                             bonus_out, stream: Optional[int] = None) -> None:
+    _check(load().dflash_accept_len_ragged(ptr(draft_ids), ptr(target_ids), batch, block_size, ptr(block_len),
+                                           ptr(accept_len_out), ptr(bonus_out),
+                                           current_stream() if stream is None else stream),
+           "dflash_accept_len_ragged")
+
+
 # ----------------------------------------------------------------------------
 # struct helpers
 # ----------------------------------------------------------------------------
@@ -190,9 +199,10 @@ def make_weights(embed, lm_head, w_fc, final_norm, attn_norm: Sequence, w_qkv: S
     return w, arrays
 
 
-def make_kv(k, v, block_table, ctx_len, batch: int, max_pages: int, n_pages: int, max_ctx: int) -> DflashKV:
+def make_kv(k, v, block_table, ctx_len, batch: int, max_pages: int, n_pages: int, max_ctx: int,
+            block_len=None) -> DflashKV:
     return DflashKV(k.data_ptr(), v.data_ptr(), block_table.data_ptr(), ctx_len.data_ptr(), batch, max_pages,
-                    n_pages, max_ctx)
+                    n_pages, max_ctx, ptr(block_len))
 
 
 def dflash_stream_read(src, sink, stream: Optional[int] = None) -> None:

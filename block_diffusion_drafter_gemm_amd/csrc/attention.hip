@@ -115,6 +115,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
   const int c = f - s_first;
   const int B = a.block_size, G = a.nq / a.nkv, GB = G * B;
   const int ctx = a.ctx_len[s];
+  // block keys this sequence attends to (a per-sequence block size)
+  const int bs = a.block_len ? min(max(a.block_len[s], 1), a.block_size) : a.block_size;
   // keys k0 .. ctx - 1 of the context (k0 > 0 under a sliding window), then the block
   const int kbeg = (ctx - attended_ctx(ctx, a.window)) + c * a.chunk;
   const int kend = min(kbeg + a.chunk, ctx + B);
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
           for (int i = 0; i < 4; ++i) {
             const int key = sub + kb2 + kt * 16 + 4 * g4 + i;
             // causal (target verify): block row j sees keys up to position ctx + j
-            const bool vis = key < kend && (!a.causal || key <= ctx + qrow_j[t]);
+            const bool vis = key < kend && (!a.causal || key <= ctx + qrow_j[t]) && (key < ctx || key - ctx < bs);
             const float sc = vis ? f4get(st[kt], i) * scale : -1e30f;
             p[kt * 4 + i] = sc;
             bmax = fmaxf(bmax, sc);

@@ -425,6 +425,7 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
     at.max_items = L.max_items;
     at.causal = verify ? 1 : 0;
     at.window = c.window;
+    at.block_len = kv->block_len;
     if (launch_attention(h->bf16, at, s) != hipSuccess) return DFLASH_ERR_HIP;
     // target verify: the block's K/V join the context cache (the caller keeps
     // the accepted positions by advancing ctx_len; later blocks overwrite the rest)
@@ -581,8 +582,20 @@ int dflash_accept_len(const int32_t *draft_ids, const int32_t *target_ids, int32
   if (block_size < 2 || block_size > 64) return DFLASH_ERR_SHAPE;
   if (batch == 0) return DFLASH_OK;
   if (!draft_ids || !target_ids || !accept_len_out || !bonus_out) return DFLASH_ERR_NULL;
-  return launch_accept(draft_ids, target_ids, batch, block_size, accept_len_out, bonus_out, (hipStream_t)stream) ==
-                 hipSuccess
+  return launch_accept(draft_ids, target_ids, batch, block_size, nullptr, accept_len_out, bonus_out,
+                       (hipStream_t)stream) == hipSuccess
+             ? DFLASH_OK
+             : DFLASH_ERR_HIP;
+}
+
+int dflash_accept_len_ragged(const int32_t *draft_ids, const int32_t *target_ids, int32_t batch, int32_t block_size,
+                             const int32_t *block_len, int32_t *accept_len_out, int32_t *bonus_out, void *stream) {
+  if (batch < 0) return DFLASH_ERR_SHAPE;
+  if (block_size < 2 || block_size > 64) return DFLASH_ERR_SHAPE;
+  if (batch == 0) return DFLASH_OK;
+  if (!draft_ids || !target_ids || !accept_len_out || !bonus_out) return DFLASH_ERR_NULL;
+  return launch_accept(draft_ids, target_ids, batch, block_size, block_len, accept_len_out, bonus_out,
+                       (hipStream_t)stream) == hipSuccess
              ? DFLASH_OK
              : DFLASH_ERR_HIP;
 }

@@ -104,6 +104,7 @@ struct AttnArgs {
   int batch, block_size, nq, nkv, hd, max_pages, page_size, chunk, max_items;
   int causal;             // block row j sees block keys 0..j only (target verify)
   int window;             // > 0: only the last `window` context keys are attended
+  const int *block_len;   // [batch] or NULL: block keys j >= block_len[s] are not attended
 };
 hipError_t launch_attention(bool is_bf16, const AttnArgs &a, hipStream_t st);
 int attn_chunk(int batch, int max_ctx, int block_size, int nq, int nkv, int cu);
@@ -124,8 +125,8 @@ hipError_t launch_rmsnorm(bool is_bf16, const float *X, const void *gain, float 
                           int block_size, bool skip_anchor, void *Y, hipStream_t st);
 hipError_t launch_argmax_reduce(const float *val, const int *idx, int rows, int n_groups, int *ids_out,
                                 float *max_out, hipStream_t st);
-hipError_t launch_accept(const int *draft, const int *target, int batch, int block_size, int *tau, int *bonus,
-                         hipStream_t st);
+hipError_t launch_accept(const int *draft, const int *target, int batch, int block_size, const int *block_len,
+                         int *tau, int *bonus, hipStream_t st);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
 hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int n_cu, hipStream_t st);
 

@@ -101,12 +101,13 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float *val, co
 }
 
 // One wave per sequence: tau = 1 + (leading matches of draft vs target), bonus = target[tau-1].
-__global__ __launch_bounds__(64) void accept_kernel(const int *draft, const int *target, int B, int *tau,
-                                                    int *bonus) {
+__global__ __launch_bounds__(64) void accept_kernel(const int *draft, const int *target, int B,
+                                                    const int *block_len, int *tau, int *bonus) {
   const int s = blockIdx.x, lane = threadIdx.x;
-  const bool miss = lane < B - 1 && draft[(size_t)s * (B - 1) + lane] != target[(size_t)s * B + lane];
+  const int bs = block_len ? min(max(block_len[s], 1), B) : B;   // this sequence's block size
+  const bool miss = lane < bs - 1 && draft[(size_t)s * (B - 1) + lane] != target[(size_t)s * B + lane];
   const unsigned long long m = __ballot(miss);
-  const int k = m ? __ffsll((long long)m) - 1 : B - 1;
+  const int k = m ? __ffsll((long long)m) - 1 : bs - 1;
   if (lane == 0) {
     tau[s] = k + 1;
     bonus[s] = target[(size_t)s * B + k];
@@ -201,9 +202,9 @@ hipError_t launch_argmax_reduce(const float *val, const int *idx, int rows, int 
   return hipGetLastError();
 }
 
-hipError_t launch_accept(const int *draft, const int *target, int batch, int B, int *tau, int *bonus,
-                         hipStream_t st) {
-  hipLaunchKernelGGL(accept_kernel, dim3(batch), dim3(64), 0, st, draft, target, B, tau, bonus);
+hipError_t launch_accept(const int *draft, const int *target, int batch, int B, const int *block_len, int *tau,
+                         int *bonus, hipStream_t st) {
+  hipLaunchKernelGGL(accept_kernel, dim3(batch), dim3(64), 0, st, draft, target, B, block_len, tau, bonus);
   return hipGetLastError();
 }
 

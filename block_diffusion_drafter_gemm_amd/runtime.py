@@ -56,6 +56,11 @@ class PagedKV:
         self.batch, self.max_pages = int(block_table.shape[0]), int(block_table.shape[1])
         self.n_pages = int(n_pages)
         self.max_ctx = int(max_ctx if max_ctx is not None else int(np.max(ctx_len)))
+        self.block_len = None   # optional device [batch] int32: per-sequence block sizes
+
+    def set_block_len(self, block_len: Optional[np.ndarray]) -> None:
+        self.block_len = None if block_len is None else torch.from_numpy(
+            np.ascontiguousarray(block_len, dtype=np.int32)).to(self.ctx_len.device)
 
     def set_ctx_len(self, ctx_len: np.ndarray, max_ctx: Optional[int] = None) -> None:
         self.ctx_len.copy_(torch.from_numpy(np.ascontiguousarray(ctx_len, dtype=np.int32)))
@@ -63,7 +68,7 @@ class PagedKV:
 
     def struct(self) -> L.DflashKV:
         return L.make_kv(self.k, self.v, self.block_table, self.ctx_len, self.batch, self.max_pages,
-                         self.n_pages, self.max_ctx)
+                         self.n_pages, self.max_ctx, self.block_len)
 
 
 class Drafter:
@@ -126,6 +131,15 @@ class Drafter:
         lg = torch.empty((rows, self.cfg.vocab), dtype=torch.float32, device=self.device) if want_logits else None
         L.dflash_lmhead_argmax(self.handle, hidden, rows, ids, mx, lg, self.ws)
         return ids, mx, lg
+
+    @staticmethod
+    def accept_len_ragged(draft_ids: torch.Tensor, target_ids: torch.Tensor, block_size: int,
+                          block_len: Optional[torch.Tensor]):
+        b = int(draft_ids.shape[0])
+        tau = torch.empty(b, dtype=torch.int32, device=draft_ids.device)
+        bonus = torch.empty(b, dtype=torch.int32, device=draft_ids.device)
+        L.dflash_accept_len_ragged(draft_ids, target_ids, b, block_size, block_len, tau, bonus)
+        return tau, bonus
 
     @staticmethod
     def accept_len(draft_ids: torch.Tensor, target_ids: torch.Tensor, block_size: int):

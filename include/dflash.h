@@ -114,6 +114,11 @@ typedef struct {
     int32_t n_pages;
     int32_t max_ctx;                /* HOST value: upper bound of every ctx_len[s];
                                        sizes launch grids and workspace */
+    const int32_t *block_len;       /* device [batch] or NULL: per-sequence block size
+                                       B_s (values clamped to 1..B); block rows j >= B_s
+                                       are left out of every row's attention, so rows
+                                       < B_s equal a pass with block size B_s and rows
+                                       >= B_s carry no meaning */
 } dflash_kv;
 
 /* Creates a handle for one drafter (or, for dflash_target_verify, one target
@@ -199,6 +204,16 @@ int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int3
  * Needs no handle; 2 <= block_size <= 64. */
 int dflash_accept_len(const int32_t *draft_ids, const int32_t *target_ids, int32_t batch, int32_t block_size,
                       int32_t *accept_len_out, int32_t *bonus_out, void *stream);
+
+/* A10 with a block size per sequence (dynamic block size at inference: the
+ * drafter trained with B drafts B_s - 1 <= B - 1 tokens, [FN] §8 and [PKR]
+ * usage notes): as dflash_accept_len over the first B_s - 1 drafts and B_s
+ * target tokens of each sequence, so accept_len_out <= B_s.
+ *   block_len [batch] int32 device, B_s clamped to 1..block_size; NULL means
+ *             block_size for every sequence.  Layouts as dflash_accept_len. */
+int dflash_accept_len_ragged(const int32_t *draft_ids, const int32_t *target_ids, int32_t batch,
+                             int32_t block_size, const int32_t *block_len, int32_t *accept_len_out,
+                             int32_t *bonus_out, void *stream);
 
 /* Streaming read of `bytes` bytes at `src` (device, 16-byte aligned, bytes a
  * multiple of 16): every 32-bit word is XOR-folded into *sink (device, one

@@ -174,6 +174,16 @@ def test_accept_len_host_validation(lib):
     assert lib.dflash_accept_len(None, None, 0, 16, None, None, None) == 0
 
 
+def test_accept_len_ragged_host_validation(lib):
+    f = lib.dflash_accept_len_ragged
+    assert f(FAKE, FAKE, 4, 1, FAKE, FAKE, FAKE, None) == -2
+    assert f(FAKE, FAKE, 4, 65, None, FAKE, FAKE, None) == -2
+    assert f(None, FAKE, 4, 16, FAKE, FAKE, FAKE, None) == -1
+    assert f(FAKE, FAKE, 4, 16, FAKE, None, FAKE, None) == -1
+    assert f(FAKE, FAKE, -1, 16, FAKE, FAKE, FAKE, None) == -2
+    assert f(None, None, 0, 16, None, None, None, None) == 0
+
+
 def test_stream_read_validation(lib):
     # host-side checks only: nothing is launched on these paths
     assert lib.dflash_stream_read(None, 16, FAKE, None) == -1

@@ -211,6 +211,58 @@ def test_draft_block_sliding_window(name, window):
     run_draft_case(dataclasses.replace(MINI[name], window=window), seed=4)
 
 
+@pytest.mark.parametrize("name,blens", [("mini_bf16", [16, 5, 9]), ("mini_d64", [4, 2]), ("mini_f32", [3, 8]),
+                                        ("mini_b8", [16, 1, 7, 12, 2, 16, 9, 4])])
+def test_draft_block_per_sequence_block_sizes(name, blens):
+    """Dynamic block size: sequence s drafts B_s - 1 tokens; its rows 1..B_s-1
+    must equal the oracle's pass with block size B_s (block rows >= B_s are
+    left out of attention), on the streaming and many-rows paths."""
+    cfg = MINI[name]
+    log(f"draft_block {name} block sizes {blens}")
+    R = runtime()
+    w = S.drafter_weights(cfg, seed=6, random_gain=True)
+    lens = S.ctx_lens(cfg, seed=6)
+    batch = len(lens)
+    assert batch == len(blens)
+    lay = S.paged_layout(cfg, lens, headroom=cfg.block_size, seed=6)
+    Kp, Vp = S.ctx_kv_cache(cfg, lay, seed=6)
+    anchors = S.anchor_ids(cfg, seed=6, batch=batch)
+    dr = R.Drafter(cfg, w, max_batch=batch, max_ctx=int(lens.max()), max_new=1)
+    kv = R.PagedKV(cfg, lay.block_table, lens, lay.n_pages, k=Kp, v=Vp)
+    kv.set_block_len(np.array(blens))
+    hid = dr.draft_block(torch.from_numpy(anchors).cuda(), kv)
+    torch.cuda.synchronize()
+    hid_h = from_storage(R.to_host_storage(hid)).reshape(batch, cfg.block_size - 1, cfg.hidden)
+    for s, bs in enumerate(blens):
+        if bs < 2:                                               # nothing drafted
+            continue
+        Z = oracle_draft(dataclasses.replace(cfg, block_size=bs), w, anchors[s], Kp, Vp, lay.block_table, s,
+                         int(lens[s]))
+        assert_close(hid_h[s, :bs - 1], Z, tol_of(cfg), f"{name} seq {s} (B_s {bs}) hidden")
+    dr.close()
+
+
+@pytest.mark.parametrize("B", [2, 10, 16, 64])
+def test_accept_len_per_sequence_block_sizes(B):
+    R = runtime()
+    rng = np.random.default_rng(B)
+    batch = 300
+    d = rng.integers(0, 50, size=(batch, B - 1)).astype(np.int32)
+    y = np.where(rng.random((batch, B)) < 0.8, np.pad(d, ((0, 0), (0, 1))), rng.integers(0, 50, (batch, B)))
+    y = y.astype(np.int32)
+    bl = rng.integers(0, B + 3, size=batch).astype(np.int32)         # includes values clamped to 1..B
+    tau, bonus = R.Drafter.accept_len_ragged(torch.from_numpy(d).cuda(), torch.from_numpy(y).cuda(), B,
+                                             torch.from_numpy(bl).cuda())
+    tau, bonus = tau.cpu().numpy(), bonus.cpu().numpy()
+    for s in range(batch):
+        bs = min(max(int(bl[s]), 1), B)
+        t_o, b_o = D.accept_len(d[s, :bs - 1], y[s, :bs])
+        assert (tau[s], bonus[s]) == (t_o, b_o), (s, bs)
+    t0, b0 = R.Drafter.accept_len_ragged(torch.from_numpy(d).cuda(), torch.from_numpy(y).cuda(), B, None)
+    t1, b1 = R.Drafter.accept_len(torch.from_numpy(d).cuda(), torch.from_numpy(y).cuda(), B)
+    assert torch.equal(t0, t1) and torch.equal(b0, b1)
+
+
 def test_draft_block_empty_and_short_context():
     cfg = MINI["mini_bf16"]
     log("draft_block ctx 0/1/16")
