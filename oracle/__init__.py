@@ -28,7 +28,8 @@ Sources, cited by page title and section:
 
 Modules: ``numerics`` (storage rounding), ``drafter`` (inject, draft block,
 LM head, accept length), ``target`` (tiny target, greedy and speculative
-decoding).
+decoding), ``sampling`` (Philox4x32-10 draws, Gumbel-max sampling and the
+speculative-sampling accept rule at temperature > 0).
 """
 from .numerics import round_bf16, round_f32, round_storage, bf16_bits, from_storage  # noqa: F401
-from . import drafter, target  # noqa: F401
+from . import drafter, sampling, target  # noqa: F401
