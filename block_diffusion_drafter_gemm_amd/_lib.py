@@ -19,7 +19,8 @@ DFLASH_F32, DFLASH_BF16 = 0, 1
 
 EXPORTS = ("dflash_create", "dflash_destroy", "dflash_workspace_size", "dflash_workspace_init",
            "dflash_inject_context", "dflash_draft_block", "dflash_target_verify", "dflash_lmhead_argmax",
-           "dflash_accept_len", "dflash_accept_len_ragged", "dflash_stream_read", "dflash_status_str")
+           "dflash_accept_len", "dflash_accept_len_ragged", "dflash_sample_workspace_size", "dflash_sample",
+           "dflash_accept_sample", "dflash_stream_read", "dflash_status_str")
 
 
 class DflashError(RuntimeError):
@@ -74,6 +75,11 @@ def load() -> ctypes.CDLL:
     lib.dflash_lmhead_argmax.argtypes = [vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.dflash_accept_len.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     lib.dflash_accept_len_ragged.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
+    u32, u64, f32 = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float
+    lib.dflash_sample_workspace_size.argtypes = [i32, i32, ctypes.POINTER(sz)]
+    lib.dflash_sample.argtypes = [vp, i32, i32, f32, u64, u32, u32, vp, vp, vp, sz, vp]
+    lib.dflash_accept_sample.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, f32, u64, u32, vp, vp, vp, sz,
+                                         vp]
     lib.dflash_stream_read.argtypes = [vp, sz, vp, vp]
     lib.dflash_status_str.argtypes = [ctypes.c_int]
     lib.dflash_status_str.restype = ctypes.c_char_p
@@ -170,6 +176,29 @@ def dflash_accept_len_ragged(draft_ids, target_ids, batch: int, block_size: int,
                                            ptr(accept_len_out), ptr(bonus_out),
                                            current_stream() if stream is None else stream),
            "dflash_accept_len_ragged")
+
+
+def dflash_sample_workspace_size(rows: int, vocab: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().dflash_sample_workspace_size(rows, vocab, ctypes.byref(n)), "dflash_sample_workspace_size")
+    return n.value
+
+
+def dflash_sample(logits, rows: int, vocab: int, temperature: float, seed: int, offset: int, tag: int, ids_out,
+                  lse_out, ws, stream: Optional[int] = None) -> None:
+    _check(load().dflash_sample(ptr(logits), rows, vocab, temperature, seed, offset, tag, ptr(ids_out),
+                                ptr(lse_out), ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                current_stream() if stream is None else stream), "dflash_sample")
+
+
+def dflash_accept_sample(draft_logits, draft_lse, draft_ids, target_logits, target_lse, target_ids, batch: int,
+                         block_size: int, block_len, vocab: int, temperature: float, seed: int, offset: int,
+                         accept_len_out, bonus_out, ws, stream: Optional[int] = None) -> None:
+    _check(load().dflash_accept_sample(ptr(draft_logits), ptr(draft_lse), ptr(draft_ids), ptr(target_logits),
+                                       ptr(target_lse), ptr(target_ids), batch, block_size, ptr(block_len), vocab,
+                                       temperature, seed, offset, ptr(accept_len_out), ptr(bonus_out), ptr(ws),
+                                       0 if ws is None else ws.numel() * ws.element_size(),
+                                       current_stream() if stream is None else stream), "dflash_accept_sample")
 
 
 # ----------------------------------------------------------------------------

@@ -18,7 +18,7 @@ OUT_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(OUT_DIR, "libdflash.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 
-SOURCES = ["dflash_api.cpp", "gemm.hip", "gemm_stream.hip", "gemm_tiled.hip", "attention.hip", "small_kernels.hip"]
+SOURCES = ["dflash_api.cpp", "gemm.hip", "gemm_stream.hip", "gemm_tiled.hip", "attention.hip", "small_kernels.hip", "sampling.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          # keep hipcc from forming packed fp32 instructions

@@ -1,6 +1,7 @@
 // C ABI of libdflash: argument validation, workspace layout and the launch
 // sequence of each entry point.  All compute happens in the HIP kernels; this
 // file only plans and enqueues.
+#include <cmath>
 #include <math.h>
 #include <string.h>
 
@@ -540,7 +541,7 @@ int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int3
   if (!h) return DFLASH_ERR_NULL;
   if (rows < 0) return DFLASH_ERR_SHAPE;
   if (rows == 0) return DFLASH_OK;
-  if (!hidden || !ids_out || !ws) return DFLASH_ERR_NULL;
+  if (!hidden || !ws || (!ids_out && !logits_out)) return DFLASH_ERR_NULL;
   const dflash_config &c = h->cfg;
   const LmLayout L = lm_layout(h, rows);
   if (ws_bytes < L.total) return DFLASH_ERR_WORKSPACE;
@@ -561,7 +562,13 @@ int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int3
   a.amax_idx = reinterpret_cast<int *>(w + L.idx);
   const int am = c.hidden <= KR ? AM_COPY : AM_GLOBAL;
   int parts = 0;
-  int st = small ? launch_stream(h, EPI_ARGMAX, am, a, 1, s, &parts) : launch(h, EPI_ARGMAX, a, 1, s);
+  int st = DFLASH_OK;
+  if (!ids_out) {   // logits only
+    a.out = logits_out;
+    a.ldo = c.vocab;
+    return small ? launch_stream(h, EPI_STORE_F32, am, a, 1, s) : launch(h, EPI_STORE_F32, a, 1, s);
+  }
+  st = small ? launch_stream(h, EPI_ARGMAX, am, a, 1, s, &parts) : launch(h, EPI_ARGMAX, a, 1, s);
   if (st != DFLASH_OK) return st;
   if (!small) parts = a.n_groups;
   if (launch_argmax_reduce(a.amax_val, a.amax_idx, rows, parts, ids_out, max_logit_out, s) != hipSuccess)
@@ -596,6 +603,49 @@ int dflash_accept_len_ragged(const int32_t *draft_ids, const int32_t *target_ids
   if (!draft_ids || !target_ids || !accept_len_out || !bonus_out) return DFLASH_ERR_NULL;
   return launch_accept(draft_ids, target_ids, batch, block_size, block_len, accept_len_out, bonus_out,
                        (hipStream_t)stream) == hipSuccess
+             ? DFLASH_OK
+             : DFLASH_ERR_HIP;
+}
+
+int dflash_sample_workspace_size(int32_t rows, int32_t vocab, size_t *bytes) {
+  if (!bytes) return DFLASH_ERR_NULL;
+  if (rows < 0 || vocab < 1) return DFLASH_ERR_SHAPE;
+  *bytes = sample_ws_bytes(rows, vocab);
+  return DFLASH_OK;
+}
+
+static bool temperature_ok(float t) { return std::isfinite(t) && t > 0.f && std::isfinite(1.f / t); }
+
+int dflash_sample(const float *logits, int32_t rows, int32_t vocab, float temperature, uint64_t seed,
+                  uint32_t offset, uint32_t tag, int32_t *ids_out, float *lse_out, void *ws, size_t ws_bytes,
+                  void *stream) {
+  if (rows < 0 || vocab < 1) return DFLASH_ERR_SHAPE;
+  if (!temperature_ok(temperature) || tag >= 0xFFFFFFFEu) return DFLASH_ERR_RANGE;
+  if (rows == 0) return DFLASH_OK;
+  if (!logits || !ids_out || !ws) return DFLASH_ERR_NULL;
+  if (ws_bytes < sample_ws_bytes(rows, vocab)) return DFLASH_ERR_WORKSPACE;
+  return launch_sample(logits, rows, vocab, 1.f / temperature, seed, offset, tag, ids_out, lse_out, ws,
+                       (hipStream_t)stream) == hipSuccess
+             ? DFLASH_OK
+             : DFLASH_ERR_HIP;
+}
+
+int dflash_accept_sample(const float *draft_logits, const float *draft_lse, const int32_t *draft_ids,
+                         const float *target_logits, const float *target_lse, const int32_t *target_ids,
+                         int32_t batch, int32_t block_size, const int32_t *block_len, int32_t vocab,
+                         float temperature, uint64_t seed, uint32_t offset, int32_t *accept_len_out,
+                         int32_t *bonus_out, void *ws, size_t ws_bytes, void *stream) {
+  if (batch < 0 || vocab < 1) return DFLASH_ERR_SHAPE;
+  if (block_size < 2 || block_size > 64) return DFLASH_ERR_SHAPE;
+  if (!temperature_ok(temperature)) return DFLASH_ERR_RANGE;
+  if (batch == 0) return DFLASH_OK;
+  if (!draft_logits || !draft_lse || !draft_ids || !target_logits || !target_lse || !target_ids ||
+      !accept_len_out || !bonus_out || !ws)
+    return DFLASH_ERR_NULL;
+  if (ws_bytes < sample_ws_bytes(batch, vocab)) return DFLASH_ERR_WORKSPACE;
+  return launch_accept_sample(draft_logits, draft_lse, draft_ids, target_logits, target_lse, target_ids, batch,
+                              block_size, block_len, vocab, 1.f / temperature, seed, offset, accept_len_out,
+                              bonus_out, ws, (hipStream_t)stream) == hipSuccess
              ? DFLASH_OK
              : DFLASH_ERR_HIP;
 }

@@ -127,6 +127,16 @@ hipError_t launch_argmax_reduce(const float *val, const int *idx, int rows, int 
                                 float *max_out, hipStream_t st);
 hipError_t launch_accept(const int *draft, const int *target, int batch, int block_size, const int *block_len,
                          int *tau, int *bonus, hipStream_t st);
+
+// temperature sampling (sampling.hip): 4096-column chunks per workgroup
+constexpr int kSampleCols = 4096;
+size_t sample_ws_bytes(int rows, int vocab);
+hipError_t launch_sample(const float *logits, int rows, int vocab, float inv_t, uint64_t seed, uint32_t offset,
+                         uint32_t tag, int *ids_out, float *lse_out, void *ws, hipStream_t st);
+hipError_t launch_accept_sample(const float *dz, const float *dlse, const int *dids, const float *tz,
+                                const float *tlse, const int *tids, int batch, int B, const int *block_len,
+                                int vocab, float inv_t, uint64_t seed, uint32_t offset, int *tau, int *bonus,
+                                void *ws, hipStream_t st);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
 hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, int n_cu, hipStream_t st);
 

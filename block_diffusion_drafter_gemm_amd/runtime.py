@@ -132,6 +132,40 @@ class Drafter:
         L.dflash_lmhead_argmax(self.handle, hidden, rows, ids, mx, lg, self.ws)
         return ids, mx, lg
 
+    def lmhead_logits(self, hidden: torch.Tensor) -> torch.Tensor:
+        """fp32 logits [rows, vocab] only (the input of temperature sampling)."""
+        rows = int(hidden.shape[0])
+        lg = torch.empty((rows, self.cfg.vocab), dtype=torch.float32, device=self.device)
+        L.dflash_lmhead_argmax(self.handle, hidden, rows, None, None, lg, self.ws)
+        return lg
+
+    @staticmethod
+    def sample(logits: torch.Tensor, temperature: float, seed: int, offset: int, tag: int, ws=None):
+        """One draw per row from softmax(logits / T); returns (ids, lse)."""
+        rows, vocab = int(logits.shape[0]), int(logits.shape[1])
+        ids = torch.empty(rows, dtype=torch.int32, device=logits.device)
+        lse = torch.empty(rows, dtype=torch.float32, device=logits.device)
+        if ws is None:
+            ws = torch.empty(max(1, L.dflash_sample_workspace_size(rows, vocab)), dtype=torch.uint8,
+                             device=logits.device)
+        L.dflash_sample(logits, rows, vocab, temperature, seed, offset, tag, ids, lse, ws)
+        return ids, lse
+
+    @staticmethod
+    def accept_sample(draft_logits, draft_lse, draft_ids, target_logits, target_lse, target_ids, block_size: int,
+                      temperature: float, seed: int, offset: int, block_len=None, ws=None):
+        """Speculative-sampling accept / resample; returns (tau, bonus)."""
+        b = int(draft_ids.shape[0])
+        vocab = int(target_logits.shape[-1])
+        tau = torch.empty(b, dtype=torch.int32, device=draft_ids.device)
+        bonus = torch.empty(b, dtype=torch.int32, device=draft_ids.device)
+        if ws is None:
+            ws = torch.empty(max(1, L.dflash_sample_workspace_size(b, vocab)), dtype=torch.uint8,
+                             device=draft_ids.device)
+        L.dflash_accept_sample(draft_logits, draft_lse, draft_ids, target_logits, target_lse, target_ids, b,
+                               block_size, block_len, vocab, temperature, seed, offset, tau, bonus, ws)
+        return tau, bonus
+
     @staticmethod
     def accept_len_ragged(draft_ids: torch.Tensor, target_ids: torch.Tensor, block_size: int,
                           block_len: Optional[torch.Tensor]):

@@ -115,7 +115,9 @@ typedef struct {
     int32_t max_ctx;                /* HOST value: upper bound of every ctx_len[s];
                                        sizes launch grids and workspace */
     const int32_t *block_len;       /* device [batch] or NULL: per-sequence block size
-                                       B_s (values clamped to 1..B); block rows j >= B_s
+                                       B_s ([SUM] §3 item 4, §4: a drafter trained with
+                                       B runs smaller blocks; values clamped to 1..B);
+                                       block rows j >= B_s
                                        are left out of every row's attention, so rows
                                        < B_s equal a pass with block size B_s and rows
                                        >= B_s carry no meaning */
@@ -189,9 +191,10 @@ int dflash_target_verify(dflash_handle h, const int32_t *ids, const dflash_kv *k
  * logits = hidden * lm_head^T in fp32; ids_out[r] = the lowest id among the
  * maxima of row r.
  *   hidden        [rows, hidden] storage type
- *   ids_out       [rows] int32
+ *   ids_out       [rows] int32; may be NULL when logits_out is given (logits only,
+ *                 the input of temperature sampling; max_logit_out is then unused)
  *   max_logit_out [rows] fp32, may be NULL
- *   logits_out    [rows, vocab] fp32, may be NULL (materialises the logits; testing aid) */
+ *   logits_out    [rows, vocab] fp32, may be NULL */
 int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int32_t *ids_out,
                          float *max_logit_out, float *logits_out, void *ws, size_t ws_bytes, void *stream);
 
@@ -206,14 +209,65 @@ int dflash_accept_len(const int32_t *draft_ids, const int32_t *target_ids, int32
                       int32_t *accept_len_out, int32_t *bonus_out, void *stream);
 
 /* A10 with a block size per sequence (dynamic block size at inference: the
- * drafter trained with B drafts B_s - 1 <= B - 1 tokens, [FN] §8 and [PKR]
- * usage notes): as dflash_accept_len over the first B_s - 1 drafts and B_s
+ * drafter trained with B drafts B_s - 1 <= B - 1 tokens, [SUM] §3 item 4 and
+ * §4 block-size ablation): as dflash_accept_len over the first B_s - 1 drafts and B_s
  * target tokens of each sequence, so accept_len_out <= B_s.
  *   block_len [batch] int32 device, B_s clamped to 1..block_size; NULL means
  *             block_size for every sequence.  Layouts as dflash_accept_len. */
 int dflash_accept_len_ragged(const int32_t *draft_ids, const int32_t *target_ids, int32_t batch,
                              int32_t block_size, const int32_t *block_len, int32_t *accept_len_out,
                              int32_t *bonus_out, void *stream);
+
+/* Verification at temperature T > 0 ([FN] §1: drafts that pass are kept and
+ * the first failing position is drawn again from the target's distribution, so
+ * the output has the target's own distribution).  The rule is the published
+ * speculative-sampling one: with p_i = softmax(target logits / T) and
+ * q_i = softmax(drafter logits / T) for position p+i, draft d_i (drawn from
+ * q_i) is kept while u_i * q_i(d_i) < p_i(d_i), u_i uniform on (0, 1); the first
+ * rejected position takes a draw from max(0, p_i - q_i) (normalised), and when
+ * every draft is kept the next token is the target's draw from p_B.
+ *
+ * Random numbers: Philox4x32-10 (Salmon et al., SC 2011) keyed by `seed`,
+ * counter (column / 4, row, offset, tag), word column mod 4, u = (w >> 9 + 1/2)
+ * * 2^-23.  A categorical draw is the Gumbel-max rule argmax_v(log weight_v -
+ * log(-log u_v)), lowest id on ties.  The same (seed, offset, tag, row) gives
+ * the same draw; advance `offset` between cycles.
+ *
+ * Logits are fp32 row-major [rows, vocab] (dflash_lmhead_argmax with
+ * ids_out == NULL writes them) and must be finite.  Temperature must be finite
+ * and > 0 (greedy verify is dflash_accept_len).  Workspace: at least
+ * dflash_sample_workspace_size(rows, vocab) bytes (rows = batch for
+ * dflash_accept_sample), device memory owned by the caller. */
+int dflash_sample_workspace_size(int32_t rows, int32_t vocab, size_t *bytes);
+
+/* One draw per row from softmax(logits[r] / T), with counter row r and the
+ * caller's `tag` (tags 0xFFFFFFFE and 0xFFFFFFFF are dflash_accept_sample's:
+ * DFLASH_ERR_RANGE).  ids_out [rows] int32; lse_out [rows] fp32 (may be NULL):
+ * the natural log of sum_v exp(logits[r][v] / T).  Drafts are drawn with it
+ * from the drafter's logits, and the target's rows give p_B's draw and the
+ * target lse dflash_accept_sample needs. */
+int dflash_sample(const float *logits, int32_t rows, int32_t vocab, float temperature, uint64_t seed,
+                  uint32_t offset, uint32_t tag, int32_t *ids_out, float *lse_out, void *ws, size_t ws_bytes,
+                  void *stream);
+
+/* The accept / resample rule above for each sequence s (counter row s):
+ *   draft_logits [batch * (B-1), vocab] fp32: the drafter's rows for p+1..p+B-1
+ *   draft_lse    [batch * (B-1)] fp32 and draft_ids [batch, B-1] int32: from
+ *                dflash_sample over draft_logits (an id outside the vocabulary
+ *                is rejected)
+ *   target_logits [batch * B, vocab] fp32: verify rows 0..B-1 (positions p+1..p+B)
+ *   target_lse    [batch * B] fp32 and target_ids [batch, B] int32: from
+ *                dflash_sample over target_logits
+ *   block_len    [batch] int32 or NULL: per-sequence block size B_s (clamped to 1..B)
+ *   accept_len_out [batch]: tau in [1, B_s]; bonus_out [batch]: the token at
+ *                position p + tau.  If fp32 rounding leaves no positive
+ *                residual at a rejected position, the target's draw there is
+ *                taken.  2 <= block_size <= 64. */
+int dflash_accept_sample(const float *draft_logits, const float *draft_lse, const int32_t *draft_ids,
+                         const float *target_logits, const float *target_lse, const int32_t *target_ids,
+                         int32_t batch, int32_t block_size, const int32_t *block_len, int32_t vocab,
+                         float temperature, uint64_t seed, uint32_t offset, int32_t *accept_len_out,
+                         int32_t *bonus_out, void *ws, size_t ws_bytes, void *stream);
 
 /* Streaming read of `bytes` bytes at `src` (device, 16-byte aligned, bytes a
  * multiple of 16): every 32-bit word is XOR-folded into *sink (device, one

@@ -184,6 +184,43 @@ def test_accept_len_ragged_host_validation(lib):
     assert f(None, None, 0, 16, None, None, None, None) == 0
 
 
+def test_sample_host_validation(lib):
+    import ctypes
+    n = ctypes.c_size_t(0)
+    assert lib.dflash_sample_workspace_size(3, 4097, ctypes.byref(n)) == 0 and n.value == 3 * 2 * 16
+    assert lib.dflash_sample_workspace_size(-1, 10, ctypes.byref(n)) == -2
+    assert lib.dflash_sample_workspace_size(1, 0, ctypes.byref(n)) == -2
+    assert lib.dflash_sample_workspace_size(1, 10, None) == -1
+    f = lib.dflash_sample
+    for T in (0.0, -1.0, float("nan"), float("inf"), 1e-45):
+        assert f(FAKE, 4, 10, T, 1, 0, 0, FAKE, None, FAKE, 1 << 20, None) == -4, T
+    assert f(FAKE, 4, 10, 1.0, 1, 0, 0xFFFFFFFE, FAKE, None, FAKE, 1 << 20, None) == -4
+    assert f(FAKE, 4, 10, 1.0, 1, 0, 0xFFFFFFFF, FAKE, None, FAKE, 1 << 20, None) == -4
+    assert f(FAKE, -1, 10, 1.0, 1, 0, 0, FAKE, None, FAKE, 1 << 20, None) == -2
+    assert f(FAKE, 4, 0, 1.0, 1, 0, 0, FAKE, None, FAKE, 1 << 20, None) == -2
+    assert f(None, 0, 10, 1.0, 1, 0, 0, None, None, None, 0, None) == 0
+    assert f(None, 4, 10, 1.0, 1, 0, 0, FAKE, None, FAKE, 1 << 20, None) == -1
+    assert f(FAKE, 4, 10, 1.0, 1, 0, 0, None, None, FAKE, 1 << 20, None) == -1
+    assert f(FAKE, 4, 10, 1.0, 1, 0, 0, FAKE, None, FAKE, 4 * 16 - 1, None) == -5
+
+
+def test_accept_sample_host_validation(lib):
+    f = lib.dflash_accept_sample
+    args = lambda **k: [k.get("dz", FAKE), FAKE, FAKE, FAKE, FAKE, FAKE, k.get("batch", 4), k.get("B", 16), None,
+                        k.get("V", 100), k.get("T", 1.0), 9, 0, FAKE, k.get("bonus", FAKE), FAKE,
+                        k.get("ws", 1 << 20), None]
+    assert f(*args(B=1)) == -2
+    assert f(*args(B=65)) == -2
+    assert f(*args(batch=-1)) == -2
+    assert f(*args(V=0)) == -2
+    assert f(*args(T=0.0)) == -4
+    assert f(*args(T=float("nan"))) == -4
+    assert f(*args(dz=None)) == -1
+    assert f(*args(bonus=None)) == -1
+    assert f(*args(ws=4 * 16 - 1)) == -5
+    assert f(*args(batch=0, dz=None)) == 0
+
+
 def test_stream_read_validation(lib):
     # host-side checks only: nothing is launched on these paths
     assert lib.dflash_stream_read(None, 16, FAKE, None) == -1
