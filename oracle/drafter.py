@@ -250,3 +250,6 @@ class OracleDrafter:
         Z = draft_block(self.w, self.cfg, anchor, self.K, self.V)
         ids, _, _ = lm_argmax(self.w["lm_head"], Z)
         return ids
+
+    def draft_logits(self, anchor: int) -> np.ndarray:
+        return lm_logits(self.w["lm_head"], draft_block(self.w, self.cfg, anchor, self.K, self.V))

@@ -30,9 +30,11 @@ id on ties.
 """
 from __future__ import annotations
 
-from typing import Tuple
+from typing import List, Sequence, Tuple
 
 import numpy as np
+
+from .numerics import round_storage
 
 M0, M1 = 0xD2511F53, 0xCD9E8D57          # Philox4x32 multipliers
 W0, W1 = 0x9E3779B9, 0xBB67AE85          # Weyl key increments
@@ -41,6 +43,8 @@ MASK32 = 0xFFFFFFFF
 # tags the accept rule draws with (the caller's sampling uses other tags)
 TAG_ACCEPT = 0xFFFFFFFE
 TAG_RESIDUAL = 0xFFFFFFFF
+# tags of the speculative loop below: drafts, the target's rows, the prefill's token
+TAG_DRAFT, TAG_TARGET, TAG_PREFILL = 0, 1, 2
 
 
 def philox4x32_10(ctr: np.ndarray, key: Tuple[int, int]) -> np.ndarray:
@@ -137,3 +141,40 @@ def accept_sample(draft_logits: np.ndarray, draft_ids, target_logits: np.ndarray
         if not u[i] < p / q:
             return i + 1, residual_sample(target_logits[i], draft_logits[i], T, seed, offset, s)
     return bm1 + 1, int(target_last_id)
+
+
+def spec_sample(target, drafter, prompt: Sequence[int], n_new: int, T: float, seed: int,
+                feat_dtype: str) -> Tuple[np.ndarray, List[int]]:
+    """Speculative sampling with a block drafter at temperature T ([FN] §1, §2).
+
+    As the greedy loop (``target.spec_decode``), with draws in place of
+    argmaxes: the prefill's token is drawn from its last row (tag TAG_PREFILL,
+    offset 0, row 0); in cycle c (offset c) the drafts are drawn from the
+    drafter's rows (tag TAG_DRAFT, row i), the target's rows are drawn (tag
+    TAG_TARGET, row i; the last one is the token taken when every draft is
+    kept), and ``accept_sample`` (sequence row 0) decides.  ``drafter``
+    provides ``inject(feats, pos)`` and ``draft_logits(anchor) -> [B-1, V]``.
+    """
+    B = target.cfg.block_size
+    target.reset()
+    P = len(prompt)
+    logits, taps = target.run(prompt, 0)
+    drafter.inject(round_storage(taps, feat_dtype), np.arange(P))
+    out = [sample_row(logits[-1], T, seed, TAG_PREFILL, 0, 0)]
+    taus: List[int] = []
+    p, c = P, 0
+    while len(out) < n_new:
+        anchor = out[-1]
+        zd = drafter.draft_logits(anchor)
+        d, _ = sample_rows(zd, T, seed, TAG_DRAFT, c)
+        zt, taps = target.run([anchor] + [int(t) for t in d], p)
+        y, _ = sample_rows(zt, T, seed, TAG_TARGET, c)
+        tau, bonus = accept_sample(zd, d, zt, int(y[B - 1]), T, seed, c, 0)
+        taus.append(tau)
+        out.extend(int(t) for t in d[:tau - 1])
+        out.append(bonus)
+        target.truncate(p + tau)
+        drafter.inject(round_storage(taps[:tau], feat_dtype), np.arange(p, p + tau))
+        p += tau
+        c += 1
+    return np.array(out[:n_new], dtype=np.int32), taus

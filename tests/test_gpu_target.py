@@ -15,6 +15,8 @@ import torch
 
 import dflash_synth as S
 from gpu_cases import MINI, assert_close, check_ids, log
+from oracle import drafter as D
+from oracle import sampling as P
 from oracle import target as T
 
 pytestmark = pytest.mark.gpu
@@ -60,6 +62,14 @@ class GpuTarget:
         hid, taps = d.target_verify(ids, self.kv, self.taps)
         _, _, lg = d.lmhead_argmax(hid, want_max=False, want_logits=True)
         return lg.cpu().numpy(), self.R.to_host_storage(taps)
+
+    def run_logits(self, tokens, pos):
+        """As run, with the logits left on the device (logits-only LM head)."""
+        assert pos == self.ctx
+        d = self.h[len(tokens)]
+        ids = torch.tensor([list(tokens)], dtype=torch.int32, device="cuda")
+        hid, taps = d.target_verify(ids, self.kv, self.taps)
+        return d.lmhead_logits(hid), self.R.to_host_storage(taps)
 
     def commit(self, n):
         self.ctx += n
@@ -143,6 +153,10 @@ class GpuDrafter:
         hid = self.d.draft_block(torch.tensor([anchor], dtype=torch.int32, device="cuda"), self.kv)
         ids, _, _ = self.d.lmhead_argmax(hid, want_max=False)
         return ids.cpu().numpy()
+
+    def draft_logits(self, anchor):
+        hid = self.d.draft_block(torch.tensor([anchor], dtype=torch.int32, device="cuda"), self.kv)
+        return self.d.lmhead_logits(hid)
 
 
 def gpu_greedy(cfg, tw, prompt, n_new):
@@ -232,3 +246,57 @@ def test_speculative_commits_accepted_drafts_on_gpu(kind):
     log(f"  {kind}: taus {taus}")
     assert np.array_equal(spec, greedy[:n])
     assert all(t == (B if kind == "perfect" else 2) for t in taus)
+
+
+def gpu_spec_sample(cfg, tw, dw, prompt, n_new, temp, seed):
+    """Speculative sampling at temperature ``temp``, everything on the GPU: the
+    loop and counter conventions of the oracle's ``spec_sample``."""
+    R = runtime()
+    B, Pl = cfg.block_size, len(prompt)
+    cap = Pl + n_new + 2 * B
+    g = GpuTarget(cfg, tw, cap, (Pl, B))
+    dr = GpuDrafter(cfg, dw, cap)
+    lg, taps = g.run_logits(prompt, 0)
+    g.commit(Pl)
+    dr.inject(taps, np.arange(Pl))
+    first, _ = R.Drafter.sample(lg[-1:].contiguous(), temp, seed, 0, P.TAG_PREFILL)
+    out = [int(first.cpu()[0])]
+    taus = []
+    p, c = Pl, 0
+    while len(out) < n_new:
+        anchor = out[-1]
+        zd = dr.draft_logits(anchor)
+        d, dlse = R.Drafter.sample(zd, temp, seed, c, P.TAG_DRAFT)
+        dh = [int(t) for t in d.cpu().numpy()]
+        zt, taps = g.run_logits([anchor] + dh, p)
+        y, tlse = R.Drafter.sample(zt, temp, seed, c, P.TAG_TARGET)
+        tau, bonus = R.Drafter.accept_sample(zd, dlse, d.view(1, B - 1), zt, tlse, y.view(1, B), B, temp, seed, c)
+        tau, bonus = int(tau.cpu()[0]), int(bonus.cpu()[0])
+        taus.append(tau)
+        out.extend(dh[:tau - 1])
+        out.append(bonus)
+        g.commit(tau)
+        dr.inject(taps[:tau], np.arange(p, p + tau))
+        p += tau
+        c += 1
+    g.close()
+    dr.d.close()
+    return np.array(out[:n_new], dtype=np.int32), taus
+
+
+@pytest.mark.parametrize("seed,temp", [(0, 1.0), (1, 0.7), (2, 1.3)])
+def test_speculative_sampling_on_gpu_matches_oracle(seed, temp):
+    """Temperature > 0: drafter, target, draws and the accept / resample rule on
+    the GPU reproduce the oracle's speculative sampling token for token (same
+    Philox streams; fp32 tiny configuration)."""
+    cfg = MINI["tiny"]
+    log(f"speculative sampling seed={seed} T={temp}")
+    tw = S.target_weights(cfg, seed, layer_std=0.05)
+    dw = S.drafter_weights(cfg, seed)
+    prompt = S.prompt_ids(cfg, seed)
+    got, taus = gpu_spec_sample(cfg, tw, dw, prompt, cfg.new_tokens, temp, seed + 100)
+    want, taus_o = P.spec_sample(T.TinyTarget(tw, cfg), D.OracleDrafter(dw, cfg), prompt, cfg.new_tokens, temp,
+                                 seed + 100, cfg.dtype)
+    log(f"  taus gpu {taus} oracle {taus_o}")
+    assert np.array_equal(got, want)
+    assert taus == taus_o
