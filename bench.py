@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="report eager launches only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--inject", action="store_true", help="also time steady-state inject (B positions)")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="> 0: draws drafts at this temperature (logits-only LM head + dflash_sample) and "
+                         "verifies with dflash_accept_sample against synthetic target logits")
     ap.add_argument("--e2e", type=int, default=0, metavar="LAYERS",
                     help="also time the target side of the cycle with a LAYERS-layer target of the drafter's "
                          "layer shape (random weights, shared embedding and LM head): block verify, one-token "
@@ -281,6 +284,28 @@ def main():
         assert lib.dflash_accept_len(ids.data_ptr(), y_dev.data_ptr(), b, B, tau.data_ptr(), bonus.data_ptr(),
                                      st) == 0
 
+    temp = args.temperature
+    if temp > 0:
+        # drafts drawn from softmax(logits / T); the verifier's logits are a
+        # synthetic stand-in (the drafter's logits plus noise), their draws and
+        # lse taken once outside the timed region
+        dz = torch.empty((rows, cfg.vocab), dtype=torch.float32, device="cuda")
+        dlse = torch.empty(rows, dtype=torch.float32, device="cuda")
+        sws = torch.empty(L.dflash_sample_workspace_size(max(rows, b * B), cfg.vocab), dtype=torch.uint8,
+                          device="cuda")
+        seed = 2024
+
+        def lmhead():
+            assert lib.dflash_lmhead_argmax(h, hid.data_ptr(), rows, None, None, dz.data_ptr(), ws.data_ptr(), wsb,
+                                            st) == 0
+            assert lib.dflash_sample(dz.data_ptr(), rows, cfg.vocab, temp, seed, 0, 0, ids.data_ptr(),
+                                     dlse.data_ptr(), sws.data_ptr(), sws.numel(), st) == 0
+
+        def accept():
+            assert lib.dflash_accept_sample(dz.data_ptr(), dlse.data_ptr(), ids.data_ptr(), tz.data_ptr(),
+                                            tlse.data_ptr(), tids.data_ptr(), b, B, None, cfg.vocab, temp, seed, 0,
+                                            tau.data_ptr(), bonus.data_ptr(), sws.data_ptr(), sws.numel(), st) == 0
+
     # synthetic target ids (70% agreement) from the first step's drafts
     draft()
     lmhead()
@@ -288,6 +313,14 @@ def main():
     d0 = ids.cpu().numpy().reshape(b, B - 1)
     y = S.target_ids_for(cfg, d0, seed=0)
     y_dev = torch.from_numpy(y).cuda()
+    if temp > 0:
+        tz = torch.empty((b, B, cfg.vocab), dtype=torch.float32, device="cuda")
+        tz[:, :B - 1] = dz.view(b, B - 1, -1)
+        tz[:, B - 1] = dz.view(b, B - 1, -1)[:, -1]
+        tz = (tz + 0.5 * torch.randn(tz.shape, generator=torch.Generator("cuda").manual_seed(0), device="cuda"))
+        tz = tz.view(b * B, -1).contiguous()
+        tids, tlse = R.Drafter.sample(tz, temp, seed, 0, 1)
+        torch.cuda.synchronize()
 
     def step():
         draft()
@@ -359,6 +392,8 @@ def main():
     total_b = layers_b + lm_b + kv_b + emb_b
     gemm_f, lm_f, attn_f = step_flops(cfg, lens)
     lm_s = float(np.mean(lm_ms)) / 1e3
+    if temp > 0:   # logits written and read back by the draw
+        lm_b += 2 * b * (B - 1) * cfg.vocab * 4
     # the LM head is HBM-bound while its flops per weight byte (= rows) stay
     # below the ridge peak_flops / peak_bandwidth (~312), MFMA-bound above
     lm_rows = b * (B - 1)
@@ -386,7 +421,7 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, N(0,sigma) context K/V, uniform anchor ids)",
         "config": {"workload": f"{cfg.name} drafter step: batch {b}, context {int(lens.max())}, B={B}, "
                                f"{cfg.n_layers} layers, hidden {cfg.hidden}, vocab {cfg.vocab}",
-                   "batch": b, "block_size": B, "ctx_len": int(lens.max()),
+                   "batch": b, "block_size": B, "ctx_len": int(lens.max()), "temperature": temp,
                    "launch": "hipgraph" if graph_ms is not None else "eager"},
         "step": {"eager_ms": round(eager_ms, 4), "graph_ms": None if graph_ms is None else round(graph_ms, 4),
                  "draft_block_ms": round(float(np.mean(draft_ms)), 4),
@@ -398,8 +433,9 @@ def main():
                  "read_stream_gbs": round(stream_gbs, 1),
                  "hbm_frac_of_read_stream": round(total_b / (ms / 1e3) / 1e9 / stream_gbs, 4),
                  "mfma_frac_step": round((gemm_f + lm_f) / (ms / 1e3) / MFMA_PEAK_FLOPS, 4)},
-        "roofline": {"kernel": "lmhead_argmax (vocabulary GEMM with argmax epilogue + argmax reduce)", **roof,
-                     "traffic": recorded_traffic() if args.config == "qwen3_8b" else None,
+        "roofline": {"kernel": "lmhead_argmax (vocabulary GEMM with argmax epilogue + argmax reduce)" if temp <= 0
+                     else "lmhead logits (vocabulary GEMM, fp32 store) + dflash_sample", **roof,
+                     "traffic": recorded_traffic() if args.config == "qwen3_8b" and temp <= 0 else None,
                      "bytes_per_launch": int(lm_b), "avg_launch_us": round(lm_s * 1e6, 2)},
     }
     if args.inject:

@@ -115,11 +115,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
   const int c = f - s_first;
   const int B = a.block_size, G = a.nq / a.nkv, GB = G * B;
   const int ctx = a.ctx_len[s];
-  // block keys this sequence attends to (a per-sequence block size)
+  // block keys this sequence attends to (a per-sequence block size): the
+  // attended keys stay one contiguous range, so a smaller block only ends it
+  // earlier (a chunk past the end is empty and its partial carries no weight)
   const int bs = a.block_len ? min(max(a.block_len[s], 1), a.block_size) : a.block_size;
   // keys k0 .. ctx - 1 of the context (k0 > 0 under a sliding window), then the block
   const int kbeg = (ctx - attended_ctx(ctx, a.window)) + c * a.chunk;
-  const int kend = min(kbeg + a.chunk, ctx + B);
+  const int kend = min(kbeg + a.chunk, ctx + bs);
   const int MTQ = (GB + 15) / 16;
   const T *Q = (const T *)a.q;
   const T *Kc = (const T *)a.kc, *Vc = (const T *)a.vc, *Kb = (const T *)a.kb, *Vb = (const T *)a.vb;
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
           for (int i = 0; i < 4; ++i) {
             const int key = sub + kb2 + kt * 16 + 4 * g4 + i;
             // causal (target verify): block row j sees keys up to position ctx + j
-            const bool vis = key < kend && (!a.causal || key <= ctx + qrow_j[t]) && (key < ctx || key - ctx < bs);
+            const bool vis = key < kend && (!a.causal || key <= ctx + qrow_j[t]);
             const float sc = vis ? f4get(st[kt], i) * scale : -1e30f;
             p[kt * 4 + i] = sc;
             bmax = fmaxf(bmax, sc);
