@@ -128,8 +128,8 @@ hipError_t launch_argmax_reduce(const float *val, const int *idx, int rows, int 
 hipError_t launch_accept(const int *draft, const int *target, int batch, int block_size, const int *block_len,
                          int *tau, int *bonus, hipStream_t st);
 
-// temperature sampling (sampling.hip): 4096-column chunks per workgroup
-constexpr int kSampleCols = 4096;
+// temperature sampling (sampling.hip): 1024-column chunks per workgroup
+constexpr int kSampleCols = 1024;
 size_t sample_ws_bytes(int rows, int vocab);
 hipError_t launch_sample(const float *logits, int rows, int vocab, float inv_t, uint64_t seed, uint32_t offset,
                          uint32_t tag, int *ids_out, float *lse_out, void *ws, hipStream_t st);

@@ -9,9 +9,10 @@
 // is word c mod 4, turned into u = (floor(w / 2^9) + 1/2) * 2^-23 in (0, 1).
 // One Philox call serves four consecutive columns of one thread.
 //
-// Vocabulary passes are split into 4096-column chunks, one 256-thread
-// workgroup each (16 columns per thread), with a per-row merge afterwards; the
-// logits are read once per pass (fp32, [rows, V] row-major).
+// Vocabulary passes are split into 1024-column chunks, one 256-thread
+// workgroup each (4 columns and one Philox call per thread), with a per-row
+// merge afterwards; the logits are read once per pass (fp32, [rows, V]
+// row-major).
 #include <climits>
 
 #include "dflash_device.h"
@@ -43,7 +44,22 @@ __device__ __forceinline__ float word_of(const uint4 &w, int j) {
   return ((float)(x >> 9) + 0.5f) * 0x1p-23f;    // exact in fp32, in (0, 1)
 }
 
-__device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
+// hardware log2 / exp2 based (a few ulp; the draws' near-ties are at 1e-4)
+__device__ __forceinline__ float gumbel(float u) { return -__logf(-__logf(u)); }
+
+// 4 logits of one thread from column c0 (one 16-byte load when the row is
+// 16-byte aligned)
+__device__ __forceinline__ float4 load4_cols(const float *z, int c0, int vocab) {
+  if ((vocab & 3) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0) return *reinterpret_cast<const float4 *>(z + c0);
+  float4 v;
+  v.x = z[c0];
+  v.y = c0 + 1 < vocab ? z[c0 + 1] : 0.f;
+  v.z = c0 + 2 < vocab ? z[c0 + 2] : 0.f;
+  v.w = c0 + 3 < vocab ? z[c0 + 3] : 0.f;
+  return v;
+}
+
+__device__ __forceinline__ float f4at(const float4 &v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
 
 // (key, lowest index) and (max, sum of exp(x - max)) of one thread or group
 struct Part {
@@ -99,26 +115,24 @@ __global__ __launch_bounds__(256) void sample_partial_kernel(const float *logits
   const int r = blockIdx.x, ch = blockIdx.y;
   const float *z = logits + (size_t)r * vocab;
   Part p = empty_part();
+  const int c0 = ch * kSampleCols + (int)threadIdx.x * 4;
+  if (c0 < vocab) {
+    const float4 zv = load4_cols(z, c0, vocab);
+    const uint4 w = philox4x32_10(make_uint4((uint32_t)c0 >> 2, (uint32_t)r, offset, tag), k0, k1);
 #pragma unroll
-  for (int g = 0; g < kSampleCols / (4 * 256); ++g) {
-    const int c0 = ch * kSampleCols + (g * 256 + (int)threadIdx.x) * 4;   // increasing per thread
-    if (c0 < vocab) {
-      const uint4 w = philox4x32_10(make_uint4((uint32_t)c0 >> 2, (uint32_t)r, offset, tag), k0, k1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (c0 + j < vocab) {
-          const float x = z[c0 + j] * inv_t;
-          const float key = x + gumbel(word_of(w, j));
-          if (key > p.key) {
-            p.key = key;
-            p.idx = c0 + j;
-          }
-          if (x > p.m) {
-            p.s = p.s * expf(p.m - x) + 1.f;
-            p.m = x;
-          } else {
-            p.s += expf(x - p.m);
-          }
+    for (int j = 0; j < 4; ++j) {
+      if (c0 + j < vocab) {
+        const float x = f4at(zv, j) * inv_t;
+        const float key = x + gumbel(word_of(w, j));
+        if (key > p.key) {       // increasing column: strict keeps the lowest id
+          p.key = key;
+          p.idx = c0 + j;
+        }
+        if (x > p.m) {
+          p.s = p.s * __expf(p.m - x) + 1.f;
+          p.m = x;
+        } else {
+          p.s += __expf(x - p.m);
         }
       }
     }
@@ -194,22 +208,19 @@ __global__ __launch_bounds__(256) void accept_partial_kernel(const AcceptArgs a,
   const float *zd = a.dz + dr * a.vocab, *zt = a.tz + tr * a.vocab;
   const float ld = a.dlse[dr], lt = a.tlse[tr];
   Part p = empty_part();
+  const int c0 = ch * kSampleCols + (int)threadIdx.x * 4;
+  if (c0 < a.vocab) {
+    const float4 tv = load4_cols(zt, c0, a.vocab), dv = load4_cols(zd, c0, a.vocab);
+    const uint4 w = philox4x32_10(make_uint4((uint32_t)c0 >> 2, (uint32_t)s, a.offset, kTagResidual), a.k0, a.k1);
 #pragma unroll
-  for (int g = 0; g < kSampleCols / (4 * 256); ++g) {
-    const int c0 = ch * kSampleCols + (g * 256 + (int)threadIdx.x) * 4;
-    if (c0 < a.vocab) {
-      const uint4 w = philox4x32_10(make_uint4((uint32_t)c0 >> 2, (uint32_t)s, a.offset, kTagResidual), a.k0, a.k1);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = c0 + j;
-        if (c < a.vocab) {
-          const float res = expf(zt[c] * a.inv_t - lt) - expf(zd[c] * a.inv_t - ld);
-          if (res > 0.f) {
-            const float key = logf(res) + gumbel(word_of(w, j));
-            if (key > p.key) {
-              p.key = key;
-              p.idx = c;
-            }
+    for (int j = 0; j < 4; ++j) {
+      if (c0 + j < a.vocab) {
+        const float res = __expf(f4at(tv, j) * a.inv_t - lt) - __expf(f4at(dv, j) * a.inv_t - ld);
+        if (res > 0.f) {
+          const float key = __logf(res) + gumbel(word_of(w, j));
+          if (key > p.key) {
+            p.key = key;
+            p.idx = c0 + j;
           }
         }
       }

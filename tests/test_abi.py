@@ -187,7 +187,7 @@ def test_accept_len_ragged_host_validation(lib):
 def test_sample_host_validation(lib):
     import ctypes
     n = ctypes.c_size_t(0)
-    assert lib.dflash_sample_workspace_size(3, 4097, ctypes.byref(n)) == 0 and n.value == 3 * 2 * 16
+    assert lib.dflash_sample_workspace_size(3, 4097, ctypes.byref(n)) == 0 and n.value == 3 * 5 * 16
     assert lib.dflash_sample_workspace_size(-1, 10, ctypes.byref(n)) == -2
     assert lib.dflash_sample_workspace_size(1, 0, ctypes.byref(n)) == -2
     assert lib.dflash_sample_workspace_size(1, 10, None) == -1
