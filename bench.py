@@ -469,6 +469,10 @@ def main():
         torch.cuda.synchronize()
         out["inject_prefill_ms"] = round(p0.elapsed_time(p1) / 3, 4)
         out["inject_prefill_positions"] = T
+        # fusion projection (L*H -> H) and every layer's K and V projection per position
+        inj_f = 2.0 * T * cfg.hidden * (cfg.feat_dim + cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim)
+        out["inject_prefill_tflops"] = round(inj_f / (out["inject_prefill_ms"] / 1e3) / 1e12, 1)
+        out["inject_prefill_mfma_frac"] = round(inj_f / (out["inject_prefill_ms"] / 1e3) / MFMA_PEAK_FLOPS, 4)
         drp.close()
     if args.e2e > 0:
         out["e2e"] = e2e_cycle(args, cfg, R, dr, lens, b, B, ms, out.get("inject_steady_ms"))
