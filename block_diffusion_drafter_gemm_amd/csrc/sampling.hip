@@ -9,10 +9,12 @@
 // is word c mod 4, turned into u = (floor(w / 2^9) + 1/2) * 2^-23 in (0, 1).
 // One Philox call serves four consecutive columns of one thread.
 //
-// Vocabulary passes are split into 1024-column chunks, one 256-thread
-// workgroup each (4 columns and one Philox call per thread), with a per-row
-// merge afterwards; the logits are read once per pass (fp32, [rows, V]
-// row-major).
+// Vocabulary passes are split into 1024-column chunks (4 columns, one 16-byte
+// load and one Philox call per thread of a 256-thread workgroup); a workgroup
+// takes 1 to 8 consecutive chunks of one row so that many rows do not launch
+// tens of thousands of tiny workgroups.  A per-row merge follows; the logits
+// are read once per pass (fp32, [rows, V] row-major).
+#include <algorithm>
 #include <climits>
 
 #include "dflash_device.h"
@@ -32,9 +34,9 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
-    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    // one 32 x 32 -> 64-bit product each (high and low words)
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x, p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
   }
   return c;
 }
@@ -44,8 +46,14 @@ __device__ __forceinline__ float word_of(const uint4 &w, int j) {
   return ((float)(x >> 9) + 0.5f) * 0x1p-23f;    // exact in fp32, in (0, 1)
 }
 
-// hardware log2 / exp2 based (a few ulp; the draws' near-ties are at 1e-4)
-__device__ __forceinline__ float gumbel(float u) { return -__logf(-__logf(u)); }
+// Keys and log-sum-exp terms are kept in base 2 (the hardware's log2 / exp2;
+// a few ulp, against near-ties at 1e-4): with y = z * log2(e) / T, the
+// Gumbel-max key (z/T + g) * log2(e) is y - log2(-log2 u) up to a constant
+// shared by all columns, and lse = ln 2 * (max y + log2 sum 2^(y - max y)).
+constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float gumbel2(float u) { return -log2_hw(-log2_hw(u)); }
 
 // 4 logits of one thread from column c0 (one 16-byte load when the row is
 // 16-byte aligned)
@@ -61,7 +69,7 @@ __device__ __forceinline__ float4 load4_cols(const float *z, int c0, int vocab) 
 
 __device__ __forceinline__ float f4at(const float4 &v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
 
-// (key, lowest index) and (max, sum of exp(x - max)) of one thread or group
+// (key, lowest index) and (max, sum of 2^(y - max)) of one thread or group
 struct Part {
   float key;
   int idx;
@@ -76,7 +84,7 @@ __device__ __forceinline__ void merge(Part &a, const Part &b) {
   }
   const float m = fmaxf(a.m, b.m);
   if (m != -INFINITY) {
-    a.s = a.s * expf(a.m - m) + b.s * expf(b.m - m);
+    a.s = a.s * exp2f(a.m - m) + b.s * exp2f(b.m - m);
     a.m = m;
   }
 }
@@ -108,37 +116,51 @@ __device__ __forceinline__ Part block_merge(Part p) {
 
 __device__ __forceinline__ Part empty_part() { return Part{-INFINITY, INT_MAX, -INFINITY, 0.f}; }
 
-// Chunk `ch` of row r: Gumbel-max key z/T + g and the log-sum-exp terms.
-__global__ __launch_bounds__(256) void sample_partial_kernel(const float *logits, int vocab, float inv_t,
+// Chunks g*per .. g*per + per - 1 of row r: Gumbel-max key z/T + g and the
+// log-sum-exp terms.  All of a thread's loads are issued before the first
+// Philox call; a thread's columns increase, so a strict comparison keeps the
+// lowest id.
+constexpr int kSamplePer = 8;   // most chunks per workgroup
+
+__global__ __launch_bounds__(256) void sample_partial_kernel(const float *logits, int vocab, float scale,
                                                              uint32_t k0, uint32_t k1, uint32_t offset,
-                                                             uint32_t tag, Part *part) {
-  const int r = blockIdx.x, ch = blockIdx.y;
+                                                             uint32_t tag, int per, Part *part) {
+  const int r = blockIdx.x, g = blockIdx.y;
   const float *z = logits + (size_t)r * vocab;
-  Part p = empty_part();
-  const int c0 = ch * kSampleCols + (int)threadIdx.x * 4;
-  if (c0 < vocab) {
-    const float4 zv = load4_cols(z, c0, vocab);
-    const uint4 w = philox4x32_10(make_uint4((uint32_t)c0 >> 2, (uint32_t)r, offset, tag), k0, k1);
+  float4 zv[kSamplePer];
+  float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (c0 + j < vocab) {
-        const float x = f4at(zv, j) * inv_t;
-        const float key = x + gumbel(word_of(w, j));
-        if (key > p.key) {       // increasing column: strict keeps the lowest id
-          p.key = key;
-          p.idx = c0 + j;
-        }
-        if (x > p.m) {
-          p.s = p.s * __expf(p.m - x) + 1.f;
-          p.m = x;
-        } else {
-          p.s += __expf(x - p.m);
+  for (int it = 0; it < kSamplePer; ++it) {
+    const int c0 = (g * per + it) * kSampleCols + (int)threadIdx.x * 4;
+    if (it < per && c0 < vocab) {
+      zv[it] = load4_cols(z, c0, vocab);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (c0 + j < vocab) m = fmaxf(m, f4at(zv[it], j) * scale);
+    }
+  }
+  Part p = empty_part();
+  p.m = m;
+#pragma unroll
+  for (int it = 0; it < kSamplePer; ++it) {
+    const int c0 = (g * per + it) * kSampleCols + (int)threadIdx.x * 4;
+    if (it < per && c0 < vocab) {
+      const uint4 w = philox4x32_10(make_uint4((uint32_t)c0 >> 2, (uint32_t)r, offset, tag), k0, k1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (c0 + j < vocab) {
+          const float y = f4at(zv[it], j) * scale;
+          p.s += exp2_hw(y - m);
+          const float key = y + gumbel2(word_of(w, j));
+          const bool better = key > p.key;     // increasing column: keeps the lowest id
+          p.key = better ? key : p.key;
+          p.idx = better ? c0 + j : p.idx;
         }
       }
     }
   }
   p = block_merge(p);
-  if (threadIdx.x == 0) part[(size_t)r * gridDim.y + ch] = p;
+  if (threadIdx.x == 0) part[(size_t)r * gridDim.y + g] = p;
 }
 
 // One wave per row: merge the chunk partials into the drawn id and the lse.
@@ -150,7 +172,7 @@ __global__ __launch_bounds__(64) void sample_reduce_kernel(const Part *part, int
   p = wave_merge(p);
   if (threadIdx.x == 0) {
     ids_out[r] = p.idx;
-    if (lse_out) lse_out[r] = p.m + logf(p.s);
+    if (lse_out) lse_out[r] = kLn2 * (p.m + log2f(p.s));
   }
 }
 
@@ -215,14 +237,12 @@ __global__ __launch_bounds__(256) void accept_partial_kernel(const AcceptArgs a,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       if (c0 + j < a.vocab) {
-        const float res = __expf(f4at(tv, j) * a.inv_t - lt) - __expf(f4at(dv, j) * a.inv_t - ld);
-        if (res > 0.f) {
-          const float key = __logf(res) + gumbel(word_of(w, j));
-          if (key > p.key) {
-            p.key = key;
-            p.idx = c0 + j;
-          }
-        }
+        // p - q, with lse in natural-log units
+        const float res = exp2_hw((f4at(tv, j) * a.inv_t - lt) * kLog2e) - exp2_hw((f4at(dv, j) * a.inv_t - ld) * kLog2e);
+        const float key = res > 0.f ? log2_hw(res) + gumbel2(word_of(w, j)) : -INFINITY;
+        const bool better = key > p.key;
+        p.key = better ? key : p.key;
+        p.idx = better ? c0 + j : p.idx;
       }
     }
   }
@@ -262,10 +282,14 @@ size_t sample_ws_bytes(int rows, int vocab) {
 hipError_t launch_sample(const float *logits, int rows, int vocab, float inv_t, uint64_t seed, uint32_t offset,
                          uint32_t tag, int *ids_out, float *lse_out, void *ws, hipStream_t st) {
   const int nch = (vocab + kSampleCols - 1) / kSampleCols;
+  // about 2048 workgroups or more: several chunks per workgroup once rows x
+  // chunks exceed that (many rows), one otherwise
+  const int per = std::max(1, std::min(kSamplePer, (int)((long)rows * nch / 2048)));
+  const int groups = (nch + per - 1) / per;
   Part *part = static_cast<Part *>(ws);
-  hipLaunchKernelGGL(sample_partial_kernel, dim3(rows, nch), dim3(256), 0, st, logits, vocab, inv_t,
-                     (uint32_t)seed, (uint32_t)(seed >> 32), offset, tag, part);
-  hipLaunchKernelGGL(sample_reduce_kernel, dim3(rows), dim3(64), 0, st, part, nch, ids_out, lse_out);
+  hipLaunchKernelGGL(sample_partial_kernel, dim3(rows, groups), dim3(256), 0, st, logits, vocab, inv_t * kLog2e,
+                     (uint32_t)seed, (uint32_t)(seed >> 32), offset, tag, per, part);
+  hipLaunchKernelGGL(sample_reduce_kernel, dim3(rows), dim3(64), 0, st, part, groups, ids_out, lse_out);
   return hipGetLastError();
 }
 

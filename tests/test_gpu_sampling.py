@@ -46,7 +46,7 @@ def check_draw(got, want, keys, what):
 
 
 @pytest.mark.parametrize("rows,vocab,T", [(7, 1, 1.0), (5, 5, 0.6), (9, 4097, 1.0), (3, 12345, 0.35),
-                                          (40, 151936, 1.0)])
+                                          (40, 151936, 1.0), (300, 60001, 0.9)])
 def test_sample_matches_oracle(rows, vocab, T):
     log(f"sample rows={rows} vocab={vocab} T={T}")
     rng = np.random.default_rng(vocab + rows)
