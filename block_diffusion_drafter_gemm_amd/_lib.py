@@ -34,7 +34,8 @@ class DflashConfig(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("n_layers", ctypes.c_int32), ("n_feat_layers", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("mask_token_id", ctypes.c_int32), ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("window", ctypes.c_int32)]
+                ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("window", ctypes.c_int32),
+                ("ctx_norm", ctypes.c_int32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -43,7 +44,7 @@ _PP = ctypes.POINTER(ctypes.c_void_p)
 class DflashWeights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("lm_head", ctypes.c_void_p), ("w_fc", ctypes.c_void_p),
                 ("final_norm", ctypes.c_void_p), ("attn_norm", _PP), ("w_qkv", _PP), ("w_o", _PP),
-                ("mlp_norm", _PP), ("w_gate_up", _PP), ("w_down", _PP)]
+                ("mlp_norm", _PP), ("w_gate_up", _PP), ("w_down", _PP), ("ctx_norm", ctypes.c_void_p)]
 
 
 class DflashKV(ctypes.Structure):
@@ -206,14 +207,14 @@ def dflash_accept_sample(draft_logits, draft_lse, draft_ids, target_logits, targ
 # ----------------------------------------------------------------------------
 def make_config(hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int, ffn: int, vocab: int, n_layers: int,
                 n_feat_layers: int, block_size: int, mask_token_id: int, dtype: str, rope_theta: float,
-                rms_eps: float, page_size: int = 16, window: int = 0) -> DflashConfig:
+                rms_eps: float, page_size: int = 16, window: int = 0, ctx_norm: int = 0) -> DflashConfig:
     return DflashConfig(hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, n_layers, n_feat_layers, block_size,
                         mask_token_id, page_size, DFLASH_BF16 if dtype == "bf16" else DFLASH_F32,
-                        float(rope_theta), float(rms_eps), int(window))
+                        float(rope_theta), float(rms_eps), int(window), int(ctx_norm))
 
 
 def make_weights(embed, lm_head, w_fc, final_norm, attn_norm: Sequence, w_qkv: Sequence, w_o: Sequence,
-                 mlp_norm: Sequence, w_gate_up: Sequence, w_down: Sequence):
+                 mlp_norm: Sequence, w_gate_up: Sequence, w_down: Sequence, ctx_norm=None):
     """Returns (DflashWeights, keepalive) - keep the second object alive while the struct is used."""
     arrays = []
 
@@ -224,7 +225,8 @@ def make_weights(embed, lm_head, w_fc, final_norm, attn_norm: Sequence, w_qkv: S
 
     w = DflashWeights(embed.data_ptr(), lm_head.data_ptr(), None if w_fc is None else w_fc.data_ptr(),
                       final_norm.data_ptr(),
-                      arr(attn_norm), arr(w_qkv), arr(w_o), arr(mlp_norm), arr(w_gate_up), arr(w_down))
+                      arr(attn_norm), arr(w_qkv), arr(w_o), arr(mlp_norm), arr(w_gate_up), arr(w_down),
+                      ptr(ctx_norm))
     return w, arrays
 
 

@@ -15,7 +15,7 @@ using namespace dflash;
 
 struct dflash_handle_s {
   dflash_config cfg;
-  const void *embed, *lm_head, *w_fc, *final_norm;
+  const void *embed, *lm_head, *w_fc, *final_norm, *ctx_norm;
   const void *attn_norm[kMaxLayers], *w_qkv[kMaxLayers], *w_o[kMaxLayers];
   const void *mlp_norm[kMaxLayers], *w_gate_up[kMaxLayers], *w_down[kMaxLayers];
   bool bf16;
@@ -89,7 +89,7 @@ LmLayout lm_layout(const dflash_handle_s *h, int rows) {
 }
 
 struct InjectLayout {
-  size_t c, total;
+  size_t c, cf, total;
 };
 
 InjectLayout inject_layout(const dflash_handle_s *h, int n_new) {
@@ -97,6 +97,7 @@ InjectLayout inject_layout(const dflash_handle_s *h, int n_new) {
   InjectLayout L;
   Carve cv;
   L.c = cv.take((size_t)n_new * c.hidden * h->esz);
+  L.cf = c.ctx_norm ? cv.take((size_t)n_new * c.hidden * 4) : 0;   // fp32 projection before the norm
   L.total = cv.off;
   return L;
 }
@@ -183,6 +184,7 @@ int validate_config(const dflash_config *c) {
   if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return DFLASH_ERR_RANGE;
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return DFLASH_ERR_RANGE;
   if (c->window < 0) return DFLASH_ERR_RANGE;
+  if (c->ctx_norm != 0 && c->ctx_norm != 1) return DFLASH_ERR_RANGE;
   return DFLASH_OK;
 }
 
@@ -223,6 +225,7 @@ int dflash_create(const dflash_config *cfg, const dflash_weights *w, dflash_hand
   for (int l = 0; l < cfg->n_layers; ++l)
     if (!w->attn_norm[l] || !w->w_qkv[l] || !w->w_o[l] || !w->mlp_norm[l] || !w->w_gate_up[l] || !w->w_down[l])
       return DFLASH_ERR_NULL;
+  if (cfg->ctx_norm && !w->ctx_norm) return DFLASH_ERR_NULL;
   dflash_handle_s *h = new (std::nothrow) dflash_handle_s();
   if (!h) return DFLASH_ERR_RANGE;
   h->cfg = *cfg;
@@ -230,6 +233,7 @@ int dflash_create(const dflash_config *cfg, const dflash_weights *w, dflash_hand
   h->lm_head = w->lm_head;
   h->w_fc = w->w_fc;
   h->final_norm = w->final_norm;
+  h->ctx_norm = cfg->ctx_norm ? w->ctx_norm : nullptr;
   for (int l = 0; l < cfg->n_layers; ++l) {
     h->attn_norm[l] = w->attn_norm[l];
     h->w_qkv[l] = w->w_qkv[l];
@@ -285,7 +289,7 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
   const int KR = stream_res_k(h->bf16);
   const bool small = n_new <= 16;
 
-  // A1: c = feats * W_fc^T
+  // A1: c = feats * W_fc^T (then RMSNorm(c) when the handle has ctx_norm)
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.A = feats;
@@ -295,10 +299,14 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
   a.M = n_new;
   a.N = c.hidden;
   a.K = c.n_feat_layers * c.hidden;
-  a.out = w + L.c;
+  a.out = w + (c.ctx_norm ? L.cf : L.c);
   a.ldo = c.hidden;
-  st = small ? launch_stream(h, EPI_STORE, a.K <= KR ? AM_COPY : AM_PORTION, a, 1, s) : launch(h, EPI_STORE, a, 1, s);
+  const Epilogue fe = c.ctx_norm ? EPI_STORE_F32 : EPI_STORE;
+  st = small ? launch_stream(h, fe, a.K <= KR ? AM_COPY : AM_PORTION, a, 1, s) : launch(h, fe, a, 1, s);
   if (st != DFLASH_OK) return st;
+  if (c.ctx_norm && launch_rmsnorm(h->bf16, reinterpret_cast<const float *>(w + L.cf), h->ctx_norm, c.rms_eps,
+                                   n_new, c.hidden, 1, false, w + L.c, s) != hipSuccess)
+    return DFLASH_ERR_HIP;
 
   // A2: every layer's K and V projections of c, RoPE on K, paged write
   GemmArgs b;

@@ -82,9 +82,10 @@ class Drafter:
                   for k, v in weights.items()}
         c = L.make_config(cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn, cfg.vocab,
                           cfg.n_layers, cfg.n_feat_layers, cfg.block_size, cfg.mask_token_id, cfg.dtype,
-                          cfg.rope_theta, cfg.rms_eps, cfg.page_size, getattr(cfg, "window", 0))
+                          cfg.rope_theta, cfg.rms_eps, cfg.page_size, getattr(cfg, "window", 0),
+                          getattr(cfg, "ctx_norm", 0))
         ws, self._keep = L.make_weights(self.w["embed"], self.w["lm_head"], self.w.get("w_fc"), self.w["final_norm"],
-                                        *[self.w[k] for k in _LAYER_KEYS])
+                                        *[self.w[k] for k in _LAYER_KEYS], ctx_norm=self.w.get("ctx_norm"))
         self.handle = L.dflash_create(c, ws)
         self.ws_bytes = L.dflash_workspace_size(self.handle, max_batch, max_ctx, max_new)
         self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=device)

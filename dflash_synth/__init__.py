@@ -61,6 +61,7 @@ class Config:
     page_size: int = 16
     match_rate: float = 0.7     # synthetic target agreement per position
     window: int = 0             # > 0: sliding-window context (last `window` positions)
+    ctx_norm: int = 0           # 1: RMSNorm after the fusion projection (gain "ctx_norm")
     # tiny end-to-end target (only the "tiny" configuration)
     target_layers: int = 0
     feat_layer_ids: Tuple[int, ...] = ()
@@ -221,6 +222,8 @@ def drafter_weights(cfg: Config, seed: int = 0, random_gain: bool = False,
         w["lm_head"] = normal_matrix(cfg, TAG_LM_HEAD, (cfg.vocab, H), std, seed)
     w["w_fc"] = normal_matrix(cfg, TAG_W_FC, (H, cfg.feat_dim), std, seed)
     w["final_norm"] = _gain(cfg, 3, H, seed, random_gain)
+    if cfg.ctx_norm:
+        w["ctx_norm"] = _gain(cfg, 4, H, seed, random_gain)
     for key in ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate_up", "w_down"):
         w[key] = []
     for l in range(cfg.n_layers):

@@ -81,6 +81,9 @@ typedef struct {
     int32_t window;                 /* 0: attend to the whole context; > 0: a sliding
                                        window over the last `window` context positions
                                        (long-context use; the block is always attended) */
+    int32_t ctx_norm;               /* 0: c = W_fc f; 1: c = RMSNorm(W_fc f) with gain
+                                       dflash_weights::ctx_norm (an option: the pages name
+                                       only a lightweight projection, [INS]; [SUM] §2.2) */
 } dflash_config;
 
 /* Device pointers to the drafter's weights (borrowed for the handle's
@@ -98,6 +101,8 @@ typedef struct {
     const void *const *mlp_norm;    /* [hidden] */
     const void *const *w_gate_up;   /* [2*ffn, hidden]: gate rows first, then up rows */
     const void *const *w_down;      /* [hidden, ffn] */
+    const void *ctx_norm;           /* [hidden] gain of the optional RMSNorm after the fusion
+                                       projection; required when config.ctx_norm == 1 */
 } dflash_weights;
 
 /* Paged drafter context cache (injected K/V, [FN] §2 "KV injection").

@@ -92,10 +92,15 @@ def fuse_context(w: dict, cfg, feats: np.ndarray) -> np.ndarray:
 
     The hidden states of several uniformly spaced target layers are
     concatenated and fused by a lightweight projection ([INS]; [SUM] §2.2).
-    Returns c ``[n, H]`` rounded to the storage type.
+    Returns c ``[n, H]`` rounded to the storage type.  With ``cfg.ctx_norm``
+    the projection is followed by an RMSNorm with gain ``w["ctx_norm"]``
+    (an option; the pages name only the projection), rounded once after it.
     """
     f = _w(feats)
-    return round_storage(f @ _w(w["w_fc"]).T, cfg.dtype)
+    c = f @ _w(w["w_fc"]).T
+    if getattr(cfg, "ctx_norm", 0):
+        c = rms_norm(c, _w(w["ctx_norm"]), cfg.rms_eps)
+    return round_storage(c, cfg.dtype)
 
 
 def inject(w: dict, cfg, feats: np.ndarray, pos: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:

@@ -74,7 +74,8 @@ def create(cfg):
     (dict(ffn=100), -2),
     (dict(vocab=1000 + 3), -2), (dict(block_size=1), -2), (dict(block_size=65), -2), (dict(n_layers=0), -2),
     (dict(n_layers=65), -2), (dict(mask_token_id=1024), -4), (dict(dtype="bf16", rope_theta=0.0), -4),
-    (dict(n_q_heads=32, n_kv_heads=1, block_size=16), -2), (dict(window=-1), -4),
+    (dict(n_q_heads=32, n_kv_heads=1, block_size=16), -2), (dict(window=-1), -4), (dict(ctx_norm=2), -4),
+    (dict(ctx_norm=1), -1),   # the RMSNorm gain is missing
 ])
 def test_create_rejects_bad_config(lib, bad, code):
     st, h = create(good_config(**bad))

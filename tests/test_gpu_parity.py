@@ -97,10 +97,22 @@ def test_lmhead_argmax(name, rows):
 @pytest.mark.parametrize("name,n_new", [(n, k) for n in ["tiny", "mini_bf16", "mini_d64", "mini_f32"]
                                         for k in [1, 16, 90]] + [("mini_bf16", 200), ("mini_d64", 300), ("mini_port", 5), ("mini_port", 16)])
 def test_inject_context(name, n_new):
-    cfg = MINI[name]
-    log(f"inject {name} n_new={n_new}")
+    run_inject_case(MINI[name], n_new)
+
+
+@pytest.mark.parametrize("name,n_new", [("mini_bf16", 5), ("mini_bf16", 300), ("mini_f32", 16), ("mini_f32", 90),
+                                        ("mini_port", 40)])
+def test_inject_context_with_ctx_norm(name, n_new):
+    """The optional RMSNorm after the fusion projection (random gain), on the
+    streaming (<= 16 rows), few-rows and LDS-tiled paths."""
+    run_inject_case(dataclasses.replace(MINI[name], ctx_norm=1), n_new, random_gain=True)
+
+
+def run_inject_case(cfg, n_new, random_gain=False):
+    name = cfg.name
+    log(f"inject {name} n_new={n_new} ctx_norm={cfg.ctx_norm}")
     R = runtime()
-    w = S.drafter_weights(cfg, seed=2)
+    w = S.drafter_weights(cfg, seed=2, random_gain=random_gain)
     batch = 3
     lens = np.array([n_new, n_new + 7, 3], dtype=np.int32)
     lay = S.paged_layout(cfg, lens, headroom=cfg.block_size, seed=2)

@@ -561,3 +561,22 @@ def test_inject_rounds_exact_ties_to_even():
     got = bf16_bits(V.reshape(cfg.n_layers, 12, cfg.hidden))
     for l in range(cfg.n_layers):
         assert np.array_equal(got[l], expect)
+
+
+def test_ctx_norm_rows_have_unit_rms_and_scale_invariance():
+    """The optional RMSNorm after the fusion projection: with gain 1 every row of
+    c has root mean square 1 (to eps and fp32 rounding), scaling the features
+    changes nothing, and a gain scales each column; off, c is the plain product."""
+    import dataclasses as dc
+    cfg = dc.replace(S.get_config("tiny"), ctx_norm=1, rms_eps=0.0)
+    w = S.drafter_weights(cfg, seed=1)
+    f = S.features(cfg, 7, seed=2)
+    c = D.fuse_context(w, cfg, f)
+    assert np.allclose(np.sqrt((c ** 2).mean(axis=1)), 1.0, atol=1e-6)
+    f64 = from_storage(f)
+    assert np.allclose(D.fuse_context(w, cfg, f64 * 7.0), c, atol=1e-6)
+    g = np.linspace(0.5, 2.0, cfg.hidden).astype(np.float32)
+    w2 = dict(w, ctx_norm=g)
+    assert np.allclose(D.fuse_context(w2, cfg, f), c * g, atol=1e-5)
+    off = D.fuse_context(w, dc.replace(cfg, ctx_norm=0), f)
+    assert np.allclose(off, f64 @ from_storage(w["w_fc"]).T, atol=1e-6)
