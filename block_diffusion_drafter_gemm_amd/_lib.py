@@ -20,7 +20,7 @@ DFLASH_F32, DFLASH_BF16 = 0, 1
 EXPORTS = ("dflash_create", "dflash_destroy", "dflash_workspace_size", "dflash_workspace_init",
            "dflash_inject_context", "dflash_draft_block", "dflash_target_verify", "dflash_lmhead_argmax",
            "dflash_accept_len", "dflash_accept_len_ragged", "dflash_sample_workspace_size", "dflash_sample",
-           "dflash_accept_sample", "dflash_stream_read", "dflash_status_str")
+           "dflash_accept_sample", "dflash_check_inputs", "dflash_stream_read", "dflash_status_str")
 
 
 class DflashError(RuntimeError):
@@ -81,6 +81,7 @@ def load() -> ctypes.CDLL:
     lib.dflash_sample.argtypes = [vp, i32, i32, f32, u64, u32, u32, vp, vp, vp, sz, vp]
     lib.dflash_accept_sample.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, f32, u64, u32, vp, vp, vp, sz,
                                          vp]
+    lib.dflash_check_inputs.argtypes = [vp, ctypes.POINTER(DflashKV), vp, vp, i32, vp, vp, i32, vp, vp]
     lib.dflash_stream_read.argtypes = [vp, sz, vp, vp]
     lib.dflash_status_str.argtypes = [ctypes.c_int]
     lib.dflash_status_str.restype = ctypes.c_char_p
@@ -177,6 +178,13 @@ def dflash_accept_len_ragged(draft_ids, target_ids, batch: int, block_size: int,
                                            ptr(accept_len_out), ptr(bonus_out),
                                            current_stream() if stream is None else stream),
            "dflash_accept_len_ragged")
+
+
+def dflash_check_inputs(h: int, kv, anchor_ids, ids, seq, pos, err_out, stream: Optional[int] = None) -> None:
+    _check(load().dflash_check_inputs(h, ctypes.byref(kv), ptr(anchor_ids), ptr(ids),
+                                      0 if ids is None else ids.numel(), ptr(seq), ptr(pos),
+                                      0 if seq is None else seq.numel(), ptr(err_out),
+                                      current_stream() if stream is None else stream), "dflash_check_inputs")
 
 
 def dflash_sample_workspace_size(rows: int, vocab: int) -> int:

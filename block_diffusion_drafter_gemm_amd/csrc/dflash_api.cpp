@@ -615,6 +615,33 @@ int dflash_accept_len_ragged(const int32_t *draft_ids, const int32_t *target_ids
              : DFLASH_ERR_HIP;
 }
 
+int dflash_check_inputs(dflash_handle h, const dflash_kv *kv, const int32_t *anchor_ids, const int32_t *ids,
+                        int32_t n_ids, const int32_t *seq, const int32_t *pos, int32_t n_new, int32_t *err_out,
+                        void *stream) {
+  if (!h || !err_out) return DFLASH_ERR_NULL;
+  int st = validate_kv(h, kv);
+  if (st != DFLASH_OK) return st;
+  if (n_ids < 0 || n_new < 0) return DFLASH_ERR_SHAPE;
+  if ((n_ids > 0 && !ids) || (n_new > 0 && (!seq || !pos))) return DFLASH_ERR_NULL;
+  CheckArgs a;
+  a.ctx_len = kv->ctx_len;
+  a.block_table = kv->block_table;
+  a.anchor = anchor_ids;
+  a.ids = ids;
+  a.seq = seq;
+  a.pos = pos;
+  a.batch = kv->batch;
+  a.max_pages = kv->max_pages;
+  a.n_pages = kv->n_pages;
+  a.max_ctx = kv->max_ctx;
+  a.page_size = h->cfg.page_size;
+  a.block_size = h->cfg.block_size;
+  a.vocab = h->cfg.vocab;
+  a.n_ids = n_ids;
+  a.n_new = n_new;
+  return launch_check_inputs(a, err_out, (hipStream_t)stream) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
 int dflash_sample_workspace_size(int32_t rows, int32_t vocab, size_t *bytes) {
   if (!bytes) return DFLASH_ERR_NULL;
   if (rows < 0 || vocab < 1) return DFLASH_ERR_SHAPE;

@@ -128,6 +128,14 @@ hipError_t launch_argmax_reduce(const float *val, const int *idx, int rows, int 
 hipError_t launch_accept(const int *draft, const int *target, int batch, int block_size, const int *block_len,
                          int *tau, int *bonus, hipStream_t st);
 
+// range check of device-resident indices (small_kernels.hip); bits as DFLASH_BAD_*
+constexpr int kBadCtxLen = 1, kBadCtxPage = 2, kBadBlockPage = 4, kBadTokenId = 8, kBadInjectSlot = 16;
+struct CheckArgs {
+  const int *ctx_len, *block_table, *anchor, *ids, *seq, *pos;
+  int batch, max_pages, n_pages, max_ctx, page_size, block_size, vocab, n_ids, n_new;
+};
+hipError_t launch_check_inputs(const CheckArgs &a, int *err, hipStream_t st);
+
 // temperature sampling (sampling.hip): 1024-column chunks per workgroup
 constexpr int kSampleCols = 1024;
 size_t sample_ws_bytes(int rows, int vocab);

@@ -1,5 +1,7 @@
 // Row-wise kernels of the draft step: block embedding, RMSNorm, the second
 // level of the vocabulary argmax, greedy accept length and a zero fill.
+#include <algorithm>
+
 #include "dflash_device.h"
 #include "dflash_internal.h"
 
@@ -178,6 +180,44 @@ hipError_t launch_tap(bool is_bf16, const float *X, int rows, int H, int slot, i
   return hipGetLastError();
 }
 
+// Range check of device-resident indices (the compute kernels trust them).
+// Blocks 0 .. batch-1: sequence s's context length, its block size and the page
+// table entries its context and block cover; the remaining blocks: token ids
+// and inject (seq, pos) pairs.  Every read is bounded by the sizes the host
+// passes, whatever the values read; findings are OR-ed into *err.
+__global__ __launch_bounds__(256) void check_inputs_kernel(CheckArgs a, int *err) {
+  int bad = 0;
+  const int s = blockIdx.x;
+  if (s < a.batch) {
+    const int ctx = a.ctx_len[s];
+    if (ctx < 0 || ctx > a.max_ctx) bad |= kBadCtxLen;
+    const long cap = (long)a.max_pages * a.page_size;
+    if ((long)max(ctx, 0) + a.block_size > cap) bad |= kBadBlockPage;
+    const long ctx_pages = ((long)max(ctx, 0) + a.page_size - 1) / a.page_size;
+    const long all_pages = ((long)max(ctx, 0) + a.block_size + a.page_size - 1) / a.page_size;
+    const int n_ctx = (int)min(ctx_pages, (long)a.max_pages), n_all = (int)min(all_pages, (long)a.max_pages);
+    for (int i = threadIdx.x; i < n_all; i += blockDim.x) {
+      const int pg = a.block_table[(size_t)s * a.max_pages + i];
+      if (pg < 0 || pg >= a.n_pages) bad |= i < n_ctx ? kBadCtxPage : kBadBlockPage;
+    }
+    if (threadIdx.x == 0 && a.anchor && (a.anchor[s] < 0 || a.anchor[s] >= a.vocab)) bad |= kBadTokenId;
+  } else {
+    const int t0 = (s - a.batch) * blockDim.x + threadIdx.x, stride = (gridDim.x - a.batch) * blockDim.x;
+    for (int t = t0; t < a.n_ids; t += stride)
+      if (a.ids[t] < 0 || a.ids[t] >= a.vocab) bad |= kBadTokenId;
+    for (int t = t0; t < a.n_new; t += stride) {
+      const int q = a.seq[t], p = a.pos[t];
+      if (q < 0 || q >= a.batch || p < 0 || (long)p >= (long)a.max_pages * a.page_size) {
+        bad |= kBadInjectSlot;
+      } else {
+        const int pg = a.block_table[(size_t)q * a.max_pages + p / a.page_size];
+        if (pg < 0 || pg >= a.n_pages) bad |= kBadInjectSlot;
+      }
+    }
+  }
+  if (bad) atomicOr(err, bad);
+}
+
 template <typename T>
 static hipError_t launch_rmsnorm_t(const float *X, const T *gain, float eps, int rows, int H, int B, bool skip_anchor,
                                    T *Y, hipStream_t st) {
@@ -245,6 +285,12 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t st) {
   size_t blocks = (n16 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (uint4 *)p, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_inputs(const CheckArgs &a, int *err, hipStream_t st) {
+  const int extra = (a.n_ids > 0 || a.n_new > 0) ? std::min(64, (std::max(a.n_ids, a.n_new) + 255) / 256) : 0;
+  hipLaunchKernelGGL(check_inputs_kernel, dim3(a.batch + extra), dim3(256), 0, st, a, err);
   return hipGetLastError();
 }
 

@@ -133,6 +133,12 @@ class Drafter:
         L.dflash_lmhead_argmax(self.handle, hidden, rows, ids, mx, lg, self.ws)
         return ids, mx, lg
 
+    def check_inputs(self, kv: "PagedKV", anchor_ids=None, ids=None, seq=None, pos=None) -> int:
+        """Range check of the device-resident indices; returns the DFLASH_BAD_* bits."""
+        err = torch.zeros(1, dtype=torch.int32, device=self.device)
+        L.dflash_check_inputs(self.handle, kv.struct(), anchor_ids, ids, seq, pos, err)
+        return int(err.cpu()[0])
+
     def lmhead_logits(self, hidden: torch.Tensor) -> torch.Tensor:
         """fp32 logits [rows, vocab] only (the input of temperature sampling)."""
         rows = int(hidden.shape[0])

@@ -223,6 +223,36 @@ int dflash_accept_len_ragged(const int32_t *draft_ids, const int32_t *target_ids
                              int32_t block_size, const int32_t *block_len, int32_t *accept_len_out,
                              int32_t *bonus_out, void *stream);
 
+/* Range check of the device-resident indices the hot calls trust (they do not
+ * test them: an id >= vocab or a page >= n_pages there is undefined).  Enqueues
+ * one small kernel on `stream` that ORs into *err_out (device int32, zeroed by
+ * the caller) these bits:
+ *   DFLASH_BAD_CTX_LEN    ctx_len[s] outside [0, kv->max_ctx]
+ *   DFLASH_BAD_CTX_PAGE   a block_table entry covering context positions
+ *                         0 .. ctx_len[s]-1 outside [0, n_pages)
+ *   DFLASH_BAD_BLOCK_PAGE ctx_len[s] + block_size > max_pages * page_size, or an
+ *                         entry covering the block positions outside [0, n_pages)
+ *                         (only dflash_target_verify writes there)
+ *   DFLASH_BAD_TOKEN_ID   anchor_ids[s] (kv->batch entries) or ids[t] (n_ids
+ *                         entries) outside [0, vocab)
+ *   DFLASH_BAD_INJECT_SLOT an inject (seq[t], pos[t]) pair (n_new entries) with
+ *                         seq outside [0, batch), pos outside [0, max_pages *
+ *                         page_size) or its page entry outside [0, n_pages).
+ * anchor_ids, ids and seq/pos may be NULL (not checked) when their count is 0
+ * (anchor_ids: NULL skips them).  Every read is bounded by the host-side sizes,
+ * so any index values are safe to check.  Host errors: NULL handle, kv or
+ * err_out, invalid kv sizes, negative counts. */
+enum {
+    DFLASH_BAD_CTX_LEN = 1,
+    DFLASH_BAD_CTX_PAGE = 2,
+    DFLASH_BAD_BLOCK_PAGE = 4,
+    DFLASH_BAD_TOKEN_ID = 8,
+    DFLASH_BAD_INJECT_SLOT = 16
+};
+int dflash_check_inputs(dflash_handle h, const dflash_kv *kv, const int32_t *anchor_ids, const int32_t *ids,
+                        int32_t n_ids, const int32_t *seq, const int32_t *pos, int32_t n_new, int32_t *err_out,
+                        void *stream);
+
 /* Verification at temperature T > 0 ([FN] §1: drafts that pass are kept and
  * the first failing position is drawn again from the target's distribution, so
  * the output has the target's own distribution).  The rule is the published

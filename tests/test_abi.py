@@ -134,6 +134,25 @@ def test_target_verify_host_validation(lib):
         assert lib.dflash_destroy(h) == 0
 
 
+def test_check_inputs_host_validation(lib):
+    st, h = create(good_config())
+    assert st == 0 and h
+    try:
+        kv = L.DflashKV(FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 64)
+        f = lib.dflash_check_inputs
+        assert f(None, ctypes.byref(kv), None, None, 0, None, None, 0, FAKE, None) == -1
+        assert f(h, None, None, None, 0, None, None, 0, FAKE, None) == -1
+        assert f(h, ctypes.byref(kv), None, None, 0, None, None, 0, None, None) == -1
+        assert f(h, ctypes.byref(kv), None, None, -1, None, None, 0, FAKE, None) == -2
+        assert f(h, ctypes.byref(kv), None, None, 0, None, None, -1, FAKE, None) == -2
+        assert f(h, ctypes.byref(kv), None, None, 3, None, None, 0, FAKE, None) == -1
+        assert f(h, ctypes.byref(kv), None, None, 0, FAKE, None, 2, FAKE, None) == -1
+        bad = L.DflashKV(FAKE, FAKE, FAKE, FAKE, 0, 8, 8, 64)
+        assert f(h, ctypes.byref(bad), None, None, 0, None, None, 0, FAKE, None) == -2
+    finally:
+        assert lib.dflash_destroy(h) == 0
+
+
 def test_workspace_size_and_host_validation(lib):
     st, h = create(good_config())
     assert st == 0 and h

@@ -275,6 +275,46 @@ def test_accept_len_per_sequence_block_sizes(B):
     assert torch.equal(t0, t1) and torch.equal(b0, b1)
 
 
+def test_check_inputs_flags_each_bad_index():
+    """dflash_check_inputs on valid indices reports 0, and each kind of bad
+    device index sets its own bit (the bad values go to the check kernel only)."""
+    cfg = MINI["mini_bf16"]
+    R = runtime()
+    w = S.drafter_weights(cfg, seed=8)
+    lens = np.array([5, 300, 17], dtype=np.int32)
+    B, ps = cfg.block_size, cfg.page_size
+    lay = S.paged_layout(cfg, lens, headroom=B, seed=8)
+    dr = R.Drafter(cfg, w, max_batch=3, max_ctx=int(lens.max()), max_new=4)
+    anchors = torch.from_numpy(S.anchor_ids(cfg, seed=8, batch=3)).cuda()
+    ids = torch.randint(0, cfg.vocab, (40,), dtype=torch.int32, device="cuda")
+    seq = torch.tensor([0, 1, 2, 1], dtype=torch.int32, device="cuda")
+    pos = torch.tensor([0, 299, 20, 310], dtype=torch.int32, device="cuda")
+
+    def run(table=None, ctx=None, anc=anchors, tok=ids, sq=seq, ps_=pos):
+        kv = R.PagedKV(cfg, lay.block_table if table is None else table, lens if ctx is None else ctx, lay.n_pages,
+                       max_ctx=int(lens.max()))
+        return dr.check_inputs(kv, anchor_ids=anc, ids=tok, seq=sq, pos=ps_)
+
+    assert run() == 0
+    assert run(anc=None, tok=None, sq=None, ps_=None) == 0
+    assert run(ctx=np.array([5, 301, 17], dtype=np.int32)) & 1           # above max_ctx
+    assert run(ctx=np.array([-1, 300, 17], dtype=np.int32)) == 1
+    t = lay.block_table.copy(); t[1, 3] = lay.n_pages                    # a context page of seq 1
+    assert run(table=t) == 2
+    t = lay.block_table.copy(); t[2, (17 + B - 1) // ps] = -1            # a page only the block covers
+    assert run(table=t) == 4
+    bad_anc = anchors.clone(); bad_anc[2] = cfg.vocab
+    assert run(anc=bad_anc) == 8
+    bad_ids = ids.clone(); bad_ids[39] = -5
+    assert run(tok=bad_ids) == 8
+    assert run(sq=torch.tensor([0, 3, 2, 1], dtype=torch.int32, device="cuda")) == 16
+    big = lay.block_table.shape[1] * ps
+    assert run(ps_=torch.tensor([0, big, 20, 1], dtype=torch.int32, device="cuda")) == 16
+    t = lay.block_table.copy(); t[1, 310 // ps] = lay.n_pages + 7        # the page an inject slot lands in
+    assert run(table=t) & 16
+    dr.close()
+
+
 def test_draft_block_empty_and_short_context():
     cfg = MINI["mini_bf16"]
     log("draft_block ctx 0/1/16")
