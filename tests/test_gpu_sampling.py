@@ -46,7 +46,7 @@ def check_draw(got, want, keys, what):
 
 
 @pytest.mark.parametrize("rows,vocab,T", [(7, 1, 1.0), (5, 5, 0.6), (9, 4097, 1.0), (3, 12345, 0.35),
-                                          (40, 151936, 1.0), (300, 60001, 0.9)])
+                                          (40, 151936, 1.0), (300, 60001, 0.9), (9, 4097, 0.05)])
 def test_sample_matches_oracle(rows, vocab, T):
     log(f"sample rows={rows} vocab={vocab} T={T}")
     rng = np.random.default_rng(vocab + rows)
@@ -77,7 +77,8 @@ def make_block_logits(rng, batch, B, V, agree):
 
 
 @pytest.mark.parametrize("batch,B,V,T,agree", [(40, 4, 3000, 1.0, 0.9), (24, 16, 5000, 0.7, 0.97),
-                                               (16, 16, 40000, 1.0, 0.99), (8, 2, 300, 1.5, 0.5)])
+                                               (16, 16, 40000, 1.0, 0.99), (8, 2, 300, 1.5, 0.5),
+                                               (20, 8, 2001, 0.2, 0.995)])
 def test_accept_sample_matches_oracle(batch, B, V, T, agree):
     log(f"accept_sample batch={batch} B={B} V={V} T={T}")
     R = runtime()
@@ -138,3 +139,23 @@ def test_accept_sample_block_len_and_zero_batch():
     z = torch.zeros(0, dtype=torch.int32, device="cuda")
     t0, b0 = R.Drafter.accept_sample(dz[:0], dlse[:0], z.view(0, B - 1), tz[:0], tlse[:0], z, B, T, seed, offset)
     assert t0.numel() == 0 and b0.numel() == 0
+
+
+def test_accept_sample_rejects_ids_outside_the_vocabulary():
+    """A draft id outside [0, V) is rejected at its position; the next token is
+    then the residual draw there (compared with the oracle's residual draw)."""
+    R = runtime()
+    rng = np.random.default_rng(21)
+    batch, B, V, T = 6, 5, 900, 1.0
+    zd, zt, d = make_block_logits(rng, batch, B, V, 0.9)
+    d[:, 0] = np.array([-1, V, V + 5, -7, 2 ** 30, -(2 ** 31)], dtype=np.int32)
+    seed, offset = 99, 4
+    dz, tz = torch.from_numpy(zd).cuda(), torch.from_numpy(zt).cuda()
+    _, dlse = R.Drafter.sample(dz, T, seed, offset, 0)
+    tids, tlse = R.Drafter.sample(tz, T, seed, offset, 1)
+    tau, bonus = R.Drafter.accept_sample(dz, dlse, torch.from_numpy(d).cuda(), tz, tlse, tids, B, T, seed, offset)
+    tau, bonus = tau.cpu().numpy(), bonus.cpu().numpy()
+    assert np.all(tau == 1)
+    zd3, zt3 = zd.reshape(batch, B - 1, V), zt.reshape(batch, B, V)
+    for s in range(batch):
+        assert bonus[s] == P.residual_sample(zt3[s, 0], zd3[s, 0], T, seed, offset, s), s
