@@ -11,6 +11,14 @@
  *        summary of arXiv 2602.06036), sections 2.2 and 2.3.
  *  [PKR] "DFlash 소개" (discuss.pytorch.kr), ``spec_generate`` example.
  *
+ * Entry points: handle and workspace (dflash_create, dflash_destroy,
+ * dflash_workspace_size, dflash_workspace_init); the drafter step
+ * (dflash_inject_context, dflash_draft_block, dflash_lmhead_argmax,
+ * dflash_accept_len); the rest of the speculative cycle (dflash_target_verify,
+ * dflash_accept_len_ragged, dflash_sample_workspace_size, dflash_sample,
+ * dflash_accept_sample); dflash_check_inputs, dflash_stream_read and
+ * dflash_status_str.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every pointer argument is a DEVICE pointer unless stated otherwise; the
@@ -25,7 +33,8 @@
  *    before anything is enqueued; a failed validation enqueues nothing.
  *    Device faults surface as HIP errors at the caller's next synchronisation.
  *    Out-of-range device data (ids >= vocab, page ids >= n_pages) is the
- *    caller's responsibility and is not checked on the device.
+ *    caller's responsibility: the compute calls do not check it;
+ *    dflash_check_inputs reports it when the caller enqueues that check.
  *  - A handle is not thread-safe; concurrent streams need separate
  *    workspaces.  Two calls that share a workspace must be ordered on one
  *    stream.
