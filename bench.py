@@ -32,6 +32,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="qwen3_8b")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="> 0: replace the configuration's block size B (drafting cost against B)")
     ap.add_argument("--no-graph", action="store_true", help="report eager launches only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--inject", action="store_true", help="also time steady-state inject (B positions)")
@@ -254,7 +256,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": 1 << 30, "copies": 3}), flush=True)
         return
-    cfg = S.get_config(args.config)
+    cfg = S.get_config(args.config, **({"block_size": args.block_size} if args.block_size > 0 else {}))
     b, B = cfg.batch, cfg.block_size
     w = S.drafter_weights(cfg, seed=0)
     lens = S.ctx_lens(cfg, seed=0)
@@ -435,7 +437,7 @@ def main():
                  "mfma_frac_step": round((gemm_f + lm_f) / (ms / 1e3) / MFMA_PEAK_FLOPS, 4)},
         "roofline": {"kernel": "lmhead_argmax (vocabulary GEMM with argmax epilogue + argmax reduce)" if temp <= 0
                      else "lmhead logits (vocabulary GEMM, fp32 store) + dflash_sample", **roof,
-                     "traffic": recorded_traffic() if args.config == "qwen3_8b" and temp <= 0 else None,
+                     "traffic": recorded_traffic() if args.config == "qwen3_8b" and temp <= 0 and args.block_size in (0, 16) else None,
                      "bytes_per_launch": int(lm_b), "avg_launch_us": round(lm_s * 1e6, 2)},
     }
     if args.inject:
