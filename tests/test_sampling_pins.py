@@ -122,3 +122,19 @@ def test_residual_draw_is_where_the_target_exceeds_the_draft():
             assert p[bonus] > q[bonus]
             hits += 1
     assert hits > 20
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_speculative_sampling_loop_at_zero_temperature_is_greedy_decoding(seed):
+    """The whole speculative-sampling loop (draws, accept rule, commit and
+    inject) at T -> 0 reproduces the target's greedy decoding token for token."""
+    import dflash_synth as S
+    from oracle import target as T
+    cfg = S.get_config("tiny")
+    tw = S.target_weights(cfg, seed, layer_std=0.05)
+    prompt = S.prompt_ids(cfg, seed)
+    greedy = T.greedy_decode(T.TinyTarget(tw, cfg), prompt, cfg.new_tokens)
+    out, taus = P.spec_sample(T.TinyTarget(tw, cfg), D.OracleDrafter(S.drafter_weights(cfg, seed), cfg), prompt,
+                              cfg.new_tokens, 1e-6, 1234 + seed, cfg.dtype)
+    assert np.array_equal(out, greedy)
+    assert all(1 <= t <= cfg.block_size for t in taus)
