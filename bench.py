@@ -197,15 +197,35 @@ def e2e_cycle(args, cfg, R, dr, lens, b, B, draft_step_ms, inject_ms):
     tkv = R.PagedKV(tcfg, lay.block_table, lens, lay.n_pages)
     tkv.k, tkv.v = kc, vc
     out = {}
+    temp, L, V = args.temperature, R.L, cfg.vocab
+    if temp > 0:
+        # at temperature > 0 the verify also writes the target's logits, draws
+        # its rows and runs the accept / resample rule against drafter logits
+        # (a synthetic stand-in, drawn once); a decode step draws its token
+        dz = torch.randn((b * (B - 1), V), generator=gen, device="cuda")
+        sws = torch.empty(L.dflash_sample_workspace_size(b * B, V), dtype=torch.uint8, device="cuda")
+        dids, dlse = R.Drafter.sample(dz, temp, 7, 0, 0, ws=sws)
+        tau = torch.empty(b, dtype=torch.int32, device="cuda")
+        bonus = torch.empty(b, dtype=torch.int32, device="cuda")
     for Bt, name in ((B, "verify"), (2, "decode")):
         h = tv[Bt]
         ids = torch.randint(0, cfg.vocab, (b, Bt), generator=gen, device="cuda", dtype=torch.int32)
         hid = torch.empty((b * Bt, H), dtype=torch.int16, device="cuda")
         tp = torch.empty((b * Bt, len(taps) * H), dtype=torch.int16, device="cuda")
+        if temp > 0:
+            lg = torch.empty((b * Bt, V), dtype=torch.float32, device="cuda")
+            tids = torch.empty(b * Bt, dtype=torch.int32, device="cuda")
+            tlse = torch.empty(b * Bt, dtype=torch.float32, device="cuda")
 
         def once():
             h.target_verify(ids, tkv, taps, hidden_out=hid, taps_out=tp)
-            h.lmhead_argmax(hid, want_max=False)
+            if temp <= 0:
+                h.lmhead_argmax(hid, want_max=False)
+                return
+            L.dflash_lmhead_argmax(h.handle, hid, b * Bt, None, None, lg, h.ws)
+            L.dflash_sample(lg, b * Bt, V, temp, 7, 0, 1, tids, tlse, sws)
+            if Bt == B:
+                L.dflash_accept_sample(dz, dlse, dids, lg, tlse, tids, b, B, None, V, temp, 7, 0, tau, bonus, sws)
         for _ in range(3):
             once()
         torch.cuda.synchronize()
@@ -224,6 +244,7 @@ def e2e_cycle(args, cfg, R, dr, lens, b, B, draft_step_ms, inject_ms):
     tau_syn = (1 - a ** B) / (1 - a)
     out.update({
         "target": f"{nL} layers of the drafter's shape, hidden {H}, vocab {cfg.vocab}, taps {taps}",
+        "temperature": temp,
         "target_weight_bytes": int(weight_bytes),
         "target_verify_hbm_gbs": round(weight_bytes / (out["target_verify_ms"] / 1e3) / 1e9, 1),
         "cycle_ms": round(cycle, 4), "inject_in_cycle": inject_ms is not None,
