@@ -1,6 +1,7 @@
 // C ABI of libdflash: argument validation, workspace layout and the launch
 // sequence of each entry point.  All compute happens in the HIP kernels; this
 // file only plans and enqueues.
+#include <algorithm>
 #include <cmath>
 #include <math.h>
 #include <string.h>
@@ -150,22 +151,27 @@ int launch_stream(dflash_handle_s *h, Epilogue epi, int amode, GemmArgs &a, int 
   return launch_gemm_stream(h->bf16, epi, amode, a, grid, z, st) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
-// Residual projection (EPI_RESID, K within the LDS capacity) over 17..64 rows
-// on the streaming GEMM: one grid slice per 16-row group (grid.y).  Each slice
-// gets an equal share of the compute units, rounded down to a multiple of 8,
-// so that the slices' workgroups for one column tile run on the same XCD and
-// its L2 serves them the weights after the first read.
-int launch_rows(dflash_handle_s *h, GemmArgs &a, hipStream_t st) {
+// Residual projection or LM head argmax (K within the LDS capacity) over
+// 17..64 rows on the streaming GEMM: one grid slice per 16-row group (grid.y).
+// Each slice gets an equal share of the compute units, a multiple of 8, so
+// that the slices' workgroups for one column tile run on the same XCD and its
+// L2 serves them the weights after the first read.
+int launch_rows(dflash_handle_s *h, Epilogue epi, GemmArgs &a, hipStream_t st, int *grid_out = nullptr) {
   const int groups = (a.M + 15) / 16;
   a.row_groups = groups;
   a.m_groups = 1;
-  a.n_groups = gemm_tiles(EPI_RESID, a.N, a.ffn);
+  a.n_groups = gemm_tiles(epi, a.N, a.ffn);
   int cu = compute_units(h) / groups / 8 * 8;
   if (cu < 8) cu = 8;
   const int per = (a.n_groups + cu - 1) / cu;
-  const int grid = (a.n_groups + per - 1) / per;
-  return launch_gemm_stream(h->bf16, EPI_RESID, AM_COPY_ROWS, a, grid, groups, st) == hipSuccess ? DFLASH_OK
-                                                                                                : DFLASH_ERR_HIP;
+  int grid = (a.n_groups + per - 1) / per;        // <= n_groups: every workgroup has a tile
+  // a multiple of 8 keeps a tile's workgroups of all slices on one XCD; only
+  // where that still gives every workgroup a tile
+  const int g8 = (grid + 7) / 8 * 8;
+  if (g8 <= cu && g8 <= a.n_groups) grid = g8;
+  if (grid_out) *grid_out = grid;
+  return launch_gemm_stream(h->bf16, epi, AM_COPY_ROWS, a, grid, groups, st) == hipSuccess ? DFLASH_OK
+                                                                                         : DFLASH_ERR_HIP;
 }
 
 int validate_config(const dflash_config *c) {
@@ -462,7 +468,7 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
     // one tile per workgroup: activation fragments read straight from L2 beat
     // staging the rows through LDS first
     st = fast     ? launch_stream(h, EPI_RESID, AM_GLOBAL, o, 1, s)
-         : sliced ? launch_rows(h, o, s)
+         : sliced ? launch_rows(h, EPI_RESID, o, s)
                   : launch(h, EPI_RESID, o, 1, s);
     if (st != DFLASH_OK) return st;
 
@@ -557,6 +563,10 @@ int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int3
   hipStream_t s = (hipStream_t)stream;
   const bool small = rows <= 16;
   const int KR = stream_res_k(h->bf16);
+  // 17..32 rows with resident K: two 16-row groups sharing each weight tile
+  // through L2 (with more groups each slice's compute units stream too many
+  // tiles: 60 rows took 524 us against 181 us on the LDS-tiled path)
+  const bool grouped = !small && rows <= 32 && c.hidden <= KR;
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.A = hidden;
@@ -576,9 +586,11 @@ int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int3
     a.ldo = c.vocab;
     return small ? launch_stream(h, EPI_STORE_F32, am, a, 1, s) : launch(h, EPI_STORE_F32, a, 1, s);
   }
-  st = small ? launch_stream(h, EPI_ARGMAX, am, a, 1, s, &parts) : launch(h, EPI_ARGMAX, a, 1, s);
+  st = small     ? launch_stream(h, EPI_ARGMAX, am, a, 1, s, &parts)
+       : grouped ? launch_rows(h, EPI_ARGMAX, a, s, &parts)
+                 : launch(h, EPI_ARGMAX, a, 1, s);
   if (st != DFLASH_OK) return st;
-  if (!small) parts = a.n_groups;
+  if (!small && !grouped) parts = a.n_groups;
   if (launch_argmax_reduce(a.amax_val, a.amax_idx, rows, parts, ids_out, max_logit_out, s) != hipSuccess)
     return DFLASH_ERR_HIP;
   if (logits_out) {

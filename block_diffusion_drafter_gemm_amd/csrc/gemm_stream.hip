@@ -251,10 +251,10 @@ __device__ __forceinline__ void s_finish_tile(const GemmArgs &a, f32x4 &acc, flo
   s_epilogue<T, EPI>(a, ct, t, layer, best_v, best_i, inv_freq, pre, first);
 }
 
-// A_COPY_ROWS (residual projection only): grid.y is a 16-row group; the
-// activation and residual rows move to the group's first row and M becomes the
-// group's row count (at most 16).  Field by field, so the arguments stay in
-// registers.
+// A_COPY_ROWS (residual projection and LM head argmax): grid.y is a 16-row
+// group; the activation and residual rows move to the group's first row and M
+// becomes the group's row count (at most 16).  Field by field, so the
+// arguments stay in registers.
 template <typename T>
 __device__ __forceinline__ GemmArgs row_slice(const GemmArgs &a0) {
   GemmArgs a = a0;
@@ -262,13 +262,14 @@ __device__ __forceinline__ GemmArgs row_slice(const GemmArgs &a0) {
   a.row0 = r0;
   a.M = min(16, a0.M - r0);
   a.A = (const T *)a0.A + (size_t)r0 * a0.lda;
-  a.X = a0.X + (size_t)r0 * a0.ldx;
+  if (a0.X) a.X = a0.X + (size_t)r0 * a0.ldx;
   return a;
 }
 
 template <typename T, int EPI, int AM>
 __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a0) {
-  static_assert(AM != A_COPY_ROWS || EPI == EPI_RESID, "row groups serve the residual projection");
+  static_assert(AM != A_COPY_ROWS || EPI == EPI_RESID || EPI == EPI_ARGMAX,
+                "row groups serve the residual projection and the LM head");
   // grid.y is the weight slice (layer), or the 16-row group of A_COPY_ROWS
   constexpr bool ROWS = AM == A_COPY_ROWS;
   const int layer = ROWS ? 0 : blockIdx.y;
@@ -457,8 +458,8 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
 
   if constexpr (EPI == EPI_ARGMAX) {
     if (tid < 16 && tid < a.M) {
-      a.amax_val[(size_t)tid * gridDim.x + blockIdx.x] = best_v;
-      a.amax_idx[(size_t)tid * gridDim.x + blockIdx.x] = best_i;
+      a.amax_val[(size_t)(a.row0 + tid) * gridDim.x + blockIdx.x] = best_v;
+      a.amax_idx[(size_t)(a.row0 + tid) * gridDim.x + blockIdx.x] = best_i;
     }
   }
 }
@@ -561,8 +562,8 @@ __global__ __launch_bounds__(kSThreads) void gemm_portion_kernel(const GemmArgs 
   s_finish_tile<T, EPI>(a, acc, red, ct, t, layer, &best_v, &best_i, inv_freq, pre, true);
   if constexpr (EPI == EPI_ARGMAX) {
     if (tid < 16 && tid < a.M) {
-      a.amax_val[(size_t)tid * gridDim.x + blockIdx.x] = best_v;
-      a.amax_idx[(size_t)tid * gridDim.x + blockIdx.x] = best_i;
+      a.amax_val[(size_t)(a.row0 + tid) * gridDim.x + blockIdx.x] = best_v;
+      a.amax_idx[(size_t)(a.row0 + tid) * gridDim.x + blockIdx.x] = best_i;
     }
   }
 }
@@ -578,7 +579,7 @@ static hipError_t launch_s(int am, const GemmArgs &a, dim3 grid, hipStream_t st)
       hipLaunchKernelGGL((gemm_stream_kernel<T, EPI, A_EMBED_NORM>), grid, block, 0, st, a);
       break;
     case A_COPY_ROWS:   // grid.y = 16-row groups
-      if constexpr (EPI == EPI_RESID) {
+      if constexpr (EPI == EPI_RESID || EPI == EPI_ARGMAX) {
         hipLaunchKernelGGL((gemm_stream_kernel<T, EPI, A_COPY_ROWS>), grid, block, 0, st, a);
         break;
       } else {
