@@ -157,13 +157,19 @@ def test_full_inject(name, dtype, n_new):
 
 
 @pytest.mark.timeout(600)
-def test_full_lmhead_identical_input():
+@pytest.mark.parametrize("rows", [15, 31])
+def test_full_lmhead_identical_input(rows):
+    """Full vocabulary on fixed hidden states: 15 rows (one streaming pass) and
+    31 rows (two 16-row streaming slices sharing the weight tiles)."""
     st = state("qwen3_8b", "bf16", None)
     cfg, w, dr = st["cfg"], st["w"], st["dr"]
-    z = S.normal_matrix(cfg, 88, (15, cfg.hidden), 1.0, seed=0)
-    log("[qwen3_8b] GPU LM head on fixed hidden states")
-    ids, mx, lg = dr.lmhead_argmax(st["R"].to_device(z), want_logits=True)
+    z = S.normal_matrix(cfg, 88, (rows, cfg.hidden), 1.0, seed=0)
+    log(f"[qwen3_8b] GPU LM head on fixed hidden states, {rows} rows")
+    h = dr if rows <= 15 else st["R"].Drafter(cfg, dr.w, max_batch=3, max_ctx=16, max_new=1)
+    ids, mx, lg = h.lmhead_argmax(st["R"].to_device(z), want_logits=True)
     torch.cuda.synchronize()
+    if h is not dr:
+        h.close()
     ids_o, best_o, logits_o = D.lm_argmax(w["lm_head"], z)
     assert_close(lg.cpu().numpy(), logits_o, 1e-4, "full-vocab logits")
     check_ids(ids.cpu().numpy(), ids_o, logits_o, 2e-2, "full-vocab ids")

@@ -65,6 +65,7 @@ def test_accept_len(B):
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("name,rows", [(n, r) for n in ["tiny", "mini_bf16", "mini_f32", "mini_b10"]
                                        for r in [1, 15, 33, 70]] + [("mini_b8", r) for r in [65, 130, 300]]
+                         + [("mini_bf16", 17), ("mini_f32", 31), ("tiny", 32), ("mini_b10", 24)]
                          + [("mini_wide", r) for r in [20, 47]] + [("mini_big", r) for r in [150, 300]])
 def test_lmhead_argmax(name, rows):
     cfg = MINI[name]
