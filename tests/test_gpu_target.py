@@ -300,3 +300,27 @@ def test_speculative_sampling_on_gpu_matches_oracle(seed, temp):
     log(f"  taus gpu {taus} oracle {taus_o}")
     assert np.array_equal(got, want)
     assert taus == taus_o
+
+
+def test_target_verify_with_a_smaller_block_size():
+    """A verify block of B_s < B rows (dflash_kv::block_len): rows 0..B_s-1
+    equal the oracle target's pass over those B_s tokens."""
+    cfg = MINI["tiny"]
+    tw = S.target_weights(cfg, 6, layer_std=0.05)
+    tgt = T.TinyTarget(tw, cfg)
+    prompt = S.prompt_ids(cfg, 6)
+    P_, B = len(prompt), cfg.block_size
+    g = GpuTarget(cfg, tw, P_ + 2 * B, (P_, B))
+    g.run(prompt, 0)
+    tgt.run(prompt, 0)
+    g.commit(P_)
+    block = [int(t) for t in S.prompt_ids(cfg, 7)[:B]]
+    for bs in (3, 2, 1):
+        g.kv.set_block_len(np.array([bs]))
+        lg, taps = g.run(block, P_)
+        tgt.truncate(P_)
+        lo, to = tgt.run(block[:bs], P_)
+        assert_close(lg[:bs], lo, 1e-4, f"verify logits, B_s = {bs}")
+        assert_close(taps[:bs], to, 1e-4, f"verify taps, B_s = {bs}")
+    g.kv.set_block_len(None)
+    g.close()
