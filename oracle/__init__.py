@@ -28,7 +28,7 @@ Sources, cited by page title and section:
 
 Modules: ``numerics`` (storage rounding), ``drafter`` (inject, draft block,
 LM head, accept length), ``target`` (tiny target, greedy and speculative
-decoding), ``sampling`` (Philox4x32-10 draws, Gumbel-max sampling and the
+decoding, the causal block verify under the storage rounding contract), ``sampling`` (Philox4x32-10 draws, Gumbel-max sampling and the
 speculative-sampling accept rule at temperature > 0).
 """
 from .numerics import round_bf16, round_f32, round_storage, bf16_bits, from_storage  # noqa: F401

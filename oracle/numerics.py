@@ -53,4 +53,4 @@ def from_storage(a) -> np.ndarray:
     a = np.asarray(a)
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    return a.astype(np.float64)
+    return a.astype(np.float64, copy=False)

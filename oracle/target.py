@@ -18,6 +18,10 @@ Speculative cycle ([FN] §1, §2; [PKR] ``spec_generate`` example):
    there, so output equals the target's own greedy decoding ([FN] §1).
 The target's hidden states at the tapped layers for the committed positions are
 the drafter's new context features ([SUM] §2.2).
+
+``verify_block`` is the same causal pass over a whole block at once, with the
+storage rounding of the drafter's layers (bf16 or fp32): the reference for the
+GPU target verify at the large model shapes.
 """
 from __future__ import annotations
 
@@ -25,8 +29,8 @@ from typing import List, Sequence, Tuple
 
 import numpy as np
 
-from .drafter import accept_len, rms_norm, rope, silu
-from .numerics import from_storage, round_storage
+from .drafter import accept_len, attention, rms_norm, rope, silu
+from .numerics import from_storage, round_f32, round_storage
 
 
 class TinyTarget:
@@ -103,6 +107,64 @@ class TinyTarget:
             logits.append(lg)
             taps.append(tp)
         return np.stack(logits), np.stack(taps)
+
+
+def verify_block(w: dict, cfg, ids: Sequence[int], K_ctx: np.ndarray, V_ctx: np.ndarray,
+                 tap_layers: Sequence[int] = ()) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """The target's causal pass over one drafted block, under the storage
+    rounding contract of the drafter's layers.
+
+    The target checks the whole block [anchor, d_1 .. d_{B-1}] in one forward
+    pass ([FN] §1 and the §2 cycle, step 4), and its hidden states at a few
+    uniformly spaced layers are the drafter's context features ([SUM] §2.2;
+    [INS]).  ``w`` holds a decoder of the drafter's layer structure (keys as
+    ``dflash_synth.drafter_weights``; ``cfg.n_layers`` layers), ``ids`` the
+    block's tokens at positions p .. p+len(ids)-1 with p = ``K_ctx.shape[1]``,
+    and ``K_ctx, V_ctx [n_layers, p, nkv, d]`` the target's cached keys and
+    values of positions 0 .. p-1.
+
+    Row j attends to the p context keys and to block keys 0 .. j (causal).
+    Rounding points as in ``drafter.draft_block`` (storage type ``cfg.dtype``;
+    "f64" rounds nothing and keeps a float64 residual): RMSNorm outputs, q/k/v
+    after RoPE, the attention output, the SwiGLU product, the taps and the
+    final hidden states are rounded; the residual stream is fp32.
+
+    Returns ``Z [n, H]`` (final-norm hidden states of every row), ``taps [n,
+    len(tap_layers) * H]`` (the residual stream after each listed 0-indexed
+    layer, before the final norm, in list order) and the block's own keys and
+    values ``Kb, Vb [n_layers, n, nkv, d]`` as they join the cache.
+    """
+    dt = cfg.dtype
+    H = cfg.hidden
+    nq, nkv, d, F = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn
+    ids = np.asarray(ids, dtype=np.int64)
+    n = len(ids)
+    p = K_ctx.shape[1]
+    pos = np.arange(p, p + n)
+    res = (lambda a: a) if dt == "f64" else round_f32      # fp32 residual stream
+    X = res(from_storage(w["embed"][ids]))
+    taps = {}
+    Kb = np.empty((cfg.n_layers, n, nkv, d))
+    Vb = np.empty((cfg.n_layers, n, nkv, d))
+    for l in range(cfg.n_layers):
+        Y = round_storage(rms_norm(X, from_storage(w["attn_norm"][l]), cfg.rms_eps), dt)
+        qkv = Y @ from_storage(w["w_qkv"][l]).T
+        q = rope(qkv[:, :nq * d].reshape(n, nq, d), pos, cfg.rope_theta)
+        k = rope(qkv[:, nq * d:(nq + nkv) * d].reshape(n, nkv, d), pos, cfg.rope_theta)
+        v = qkv[:, (nq + nkv) * d:].reshape(n, nkv, d)
+        q, Kb[l], Vb[l] = round_storage(q, dt), round_storage(k, dt), round_storage(v, dt)
+        Kall = np.concatenate([K_ctx[l], Kb[l]], axis=0)
+        Vall = np.concatenate([V_ctx[l], Vb[l]], axis=0)
+        O = round_storage(attention(q, Kall, Vall, causal_from=p), dt)   # row j sees keys 0 .. p+j
+        X = res(X + O.reshape(n, nq * d) @ from_storage(w["w_o"][l]).T)
+        Y = round_storage(rms_norm(X, from_storage(w["mlp_norm"][l]), cfg.rms_eps), dt)
+        gu = Y @ from_storage(w["w_gate_up"][l]).T
+        hmid = round_storage(silu(gu[:, :F]) * gu[:, F:], dt)
+        X = res(X + hmid @ from_storage(w["w_down"][l]).T)
+        taps[l] = round_storage(X, dt)
+    Z = round_storage(rms_norm(X, from_storage(w["final_norm"]), cfg.rms_eps), dt)
+    T = np.concatenate([taps[l] for l in tap_layers], axis=1) if len(tap_layers) else np.zeros((n, 0))
+    return Z, T, Kb, Vb
 
 
 def greedy_decode(target: TinyTarget, prompt: Sequence[int], n_new: int) -> np.ndarray:

@@ -539,6 +539,117 @@ def test_lossless_with_extreme_drafters():
 
 
 # ----------------------------------------------------------------------------
+# the target's causal block verify under the storage rounding contract
+# ----------------------------------------------------------------------------
+def _bf_verify(w, cfg, ids, Kc, Vc, tap_layers):
+    """Scalar-loop causal pass: row r sees the p context keys and block keys 0..r."""
+    L = lambda a: from_storage(a).tolist()
+    dt, H = cfg.dtype, cfg.hidden
+    nq, nkv, d, Fw = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn
+    n, p = len(ids), len(Kc[0])
+    res = (lambda v: v) if dt == "f64" else (lambda v: _bf_round(v, "f32"))
+    E = L(w["embed"])
+    X = [[res(v) for v in E[t]] for t in ids]
+    taps = {}
+    kb_all, vb_all = [], []
+    for l in range(cfg.n_layers):
+        Wqkv, Wo, Wgu, Wd = L(w["w_qkv"][l]), L(w["w_o"][l]), L(w["w_gate_up"][l]), L(w["w_down"][l])
+        ga, gm = L(w["attn_norm"][l]), L(w["mlp_norm"][l])
+        q, k, v = [], [], []
+        for r in range(n):
+            y = [_bf_round(t, dt) for t in _bf_rms(X[r], ga, cfg.rms_eps)]
+            o = _bf_matvec(Wqkv, y)
+            q.append([[_bf_round(t, dt) for t in _bf_rope(o[h * d:(h + 1) * d], p + r, cfg.rope_theta)]
+                      for h in range(nq)])
+            k.append([[_bf_round(t, dt) for t in _bf_rope(o[(nq + g) * d:(nq + g + 1) * d], p + r, cfg.rope_theta)]
+                      for g in range(nkv)])
+            v.append([[_bf_round(t, dt) for t in o[(nq + nkv + g) * d:(nq + nkv + g + 1) * d]] for g in range(nkv)])
+        kb_all.append(k)
+        vb_all.append(v)
+        for r in range(n):
+            keys = [Kc[l][t] for t in range(p)] + k[:r + 1]
+            vals = [Vc[l][t] for t in range(p)] + v[:r + 1]
+            att = []
+            for h in range(nq):
+                g = h * nkv // nq
+                sc = [sum(q[r][h][j] * keys[t][g][j] for j in range(d)) / math.sqrt(d) for t in range(len(keys))]
+                m = max(sc)
+                e = [math.exp(x - m) for x in sc]
+                z = sum(e)
+                att += [_bf_round(sum(e[t] / z * vals[t][g][j] for t in range(len(keys))), dt) for j in range(d)]
+            delta = _bf_matvec(Wo, att)
+            X[r] = [res(X[r][i] + delta[i]) for i in range(H)]
+        for r in range(n):
+            y = [_bf_round(t, dt) for t in _bf_rms(X[r], gm, cfg.rms_eps)]
+            gu = _bf_matvec(Wgu, y)
+            hm = [_bf_round(gu[i] / (1.0 + math.exp(-gu[i])) * gu[Fw + i], dt) for i in range(Fw)]
+            delta = _bf_matvec(Wd, hm)
+            X[r] = [res(X[r][i] + delta[i]) for i in range(H)]
+        taps[l] = [[_bf_round(t, dt) for t in X[r]] for r in range(n)]
+    gf = L(w["final_norm"])
+    Z = [[_bf_round(t, dt) for t in _bf_rms(X[r], gf, cfg.rms_eps)] for r in range(n)]
+    T_ = [sum((taps[l][r] for l in tap_layers), []) for r in range(n)]
+    return Z, T_, kb_all, vb_all
+
+
+@pytest.mark.parametrize("dtype,nq,nkv", [("bf16", 2, 1), ("f32", 4, 2), ("f64", 2, 2)])
+def test_verify_block_matches_brute_force(dtype, nq, nkv):
+    cfg = small_cfg(dtype, n_q_heads=nq, n_kv_heads=nkv, block_size=4)
+    w, feats, K, V, anchor = small_setup(cfg, seed=5 + nq)
+    ids = [anchor, 3, 7, 3]
+    Z, T_, Kb, Vb = T.verify_block(w, cfg, ids, K, V, tap_layers=(1, 0))
+    Zb, Tb, Kbb, Vbb = _bf_verify(w, cfg, ids, K.tolist(), V.tolist(), (1, 0))
+    tol = dict(rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(Z, np.array(Zb), **tol)
+    np.testing.assert_allclose(T_, np.array(Tb), **tol)
+    np.testing.assert_allclose(Kb, np.array(Kbb), **tol)
+    np.testing.assert_allclose(Vb, np.array(Vbb), **tol)
+    if dtype == "bf16":
+        for a in (Z, T_, Kb, Vb):
+            assert np.array_equal(round_bf16(a), a)
+
+
+def test_verify_block_equals_tiny_target_in_float64():
+    """Without storage rounding the block pass is the tiny target's own
+    row-by-row decoding: logits, taps and the appended cache rows agree."""
+    cfg = S.get_config("tiny")
+    w = S.target_weights(cfg, seed=2, layer_std=0.1)
+    c64 = dataclasses.replace(cfg, dtype="f64", n_layers=cfg.target_layers)
+    prompt = S.prompt_ids(cfg, 2)
+    tgt = T.TinyTarget(w, cfg)
+    tgt.run(prompt[:40], 0)
+    Kc, Vc = np.stack(tgt.K), np.stack(tgt.V)
+    block = [int(t) for t in prompt[40:40 + 6]]
+    lo, to = tgt.run(block, 40)
+    Z, T_, Kb, Vb = T.verify_block(w, c64, block, Kc, Vc, tap_layers=cfg.feat_layer_ids)
+    np.testing.assert_allclose(Z @ from_storage(w["lm_head"]).T, lo, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(T_, to, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(Kb, np.stack(tgt.K)[:, 40:], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(Vb, np.stack(tgt.V)[:, 40:], rtol=1e-10, atol=1e-12)
+
+
+def test_verify_block_reproduces_incremental_decoding():
+    """bf16 storage: one pass over n rows equals n one-row passes, each appending
+    its rounded K/V to the cache (causality and the position of every row)."""
+    cfg = small_cfg("bf16", n_q_heads=4, n_kv_heads=2, block_size=5)
+    w, feats, K, V, anchor = small_setup(cfg, seed=9)
+    ids = [anchor, 4, 4, 11, 0]
+    Z, T_, Kb, Vb = T.verify_block(w, cfg, ids, K, V, tap_layers=(0, 1))
+    Kc, Vc = K, V
+    for r, t in enumerate(ids):
+        z1, t1, k1, v1 = T.verify_block(w, cfg, [t], Kc, Vc, tap_layers=(0, 1))
+        np.testing.assert_allclose(z1[0], Z[r], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(t1[0], T_[r], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(k1[:, 0], Kb[:, r], rtol=1e-12, atol=1e-12)
+        Kc, Vc = np.concatenate([Kc, k1], axis=1), np.concatenate([Vc, v1], axis=1)
+    # a later token never changes an earlier row
+    ids2 = ids[:2] + [7, 7, 7]
+    Z2, T2, _, _ = T.verify_block(w, cfg, ids2, K, V, tap_layers=(0, 1))
+    np.testing.assert_array_equal(Z2[:2], Z[:2])
+    assert not np.allclose(Z2[2:], Z[2:])
+
+
+# ----------------------------------------------------------------------------
 # P10: shape plausibility
 # ----------------------------------------------------------------------------
 def test_drafter_size_matches_pages():
