@@ -5,9 +5,11 @@ One step = dflash_draft_block + dflash_lmhead_argmax + dflash_accept_len over
 one batch of synthetic input (the Qwen3-8B-shaped drafter at batch 1, context
 2048, B = 16 by default), with weights, context cache and ids resident in HBM
 before the timed region.  Prints one JSON line: drafted tokens/s as ``value``,
-the step latency, the HBM fraction of the step, the roofline of the dominant
-kernel (the LM-head GEMM with its argmax), and the CPU oracle timed on a
-bounded sample of the same workload.
+the step latency, the HBM fraction of the step, per-stage kernel times (HIP
+events recorded by the library around each stage of every layer, on the launch
+stream, during the eager timed steps), the roofline of the stage with the
+largest share of the step, and the CPU oracle timed on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -70,8 +72,11 @@ def step_flops(cfg, lens):
     return gemm, lm, attn
 
 
-PROFILE = os.path.join(ROOT, "profiles", "lmhead_argmax_qwen3_8b_b1.md")
+# counter summaries of the batch-1 Qwen3-8B-shape step: HBM bytes per launch of
+# each kernel, valid while the kernel sources hash to the recorded value
+PROFILE = os.path.join(ROOT, "profiles", "draft_step_qwen3_8b_b1.md")
 KERNEL_SOURCES = ["block_diffusion_drafter_gemm_amd/csrc/gemm_stream.hip",
+                  "block_diffusion_drafter_gemm_amd/csrc/attention.hip",
                   "block_diffusion_drafter_gemm_amd/csrc/dflash_device.h",
                   "block_diffusion_drafter_gemm_amd/csrc/dflash_internal.h"]
 
@@ -96,22 +101,65 @@ def read_stream_gbs(torch, nbytes=1 << 30, reps=10):
     return gbs
 
 
-def recorded_traffic():
-    """HBM bytes per LM-head launch from the committed counter summary, or None
-    when the kernel sources changed since the counters were taken."""
+def recorded_traffic(stage: str):
+    """HBM bytes (read + written) per launch of a stage's kernel from the
+    committed counter summary, or None when the kernel sources changed since the
+    counters were taken."""
     import hashlib
     import re
     try:
         text = open(PROFILE).read()
         h = hashlib.sha256()
-        for s in KERNEL_SOURCES:
-            h.update(open(os.path.join(ROOT, s), "rb").read())
+        for src in KERNEL_SOURCES:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
         sha = re.search(r"kernel_source_sha256_16: (\w+)", text).group(1)
         if sha != h.hexdigest()[:16]:
             return None
-        return int(re.search(r"traffic_bytes_per_launch: (\d+)", text).group(1))
+        return int(re.search(rf"traffic_bytes_per_launch\[{stage}\]: (\d+)", text).group(1))
     except (OSError, AttributeError):
         return None
+
+
+def stage_costs(cfg, lens):
+    """Algorithmic bytes and flops of one launch of each stage (one layer; the
+    LM head over all mask rows): weights once, valid context K/V once."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    H, F, nq, nkv, d, B = cfg.hidden, cfg.ffn, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_size
+    R = cfg.batch * B
+    ctx = int(sum(lens))
+    return {
+        "qkv": (cfg.qkv_rows * H * e + H * e, 2 * R * cfg.qkv_rows * H),
+        "attention": (ctx * nkv * d * 2 * e, sum(4 * B * nq * d * (int(p) + B) for p in lens)),
+        "o": (H * nq * d * e, 2 * R * H * nq * d),
+        "gate_up": (2 * F * H * e + H * e, 2 * R * 2 * F * H),
+        "down": (H * F * e, 2 * R * H * F),
+        "lm_head": (cfg.vocab * H * e, 2 * cfg.batch * (B - 1) * cfg.vocab * H),
+    }
+
+
+def roofline_of(name, nbytes, flops, us):
+    """Roofline entry of one launch: MFMA-bound above the ridge (peak flops /
+    peak bandwidth, ~312 flop per byte), HBM-bound below it."""
+    if flops > nbytes * MFMA_PEAK_FLOPS / (HBM_PEAK_GBS * 1e9):
+        a = flops / (us / 1e6)
+        return {"kernel": name, "bound": "mfma", "achieved": round(a / 1e12, 1), "peak": MFMA_PEAK_FLOPS / 1e12,
+                "unit": "TFLOP/s", "frac": round(a / MFMA_PEAK_FLOPS, 4), "flops_per_launch": int(flops),
+                "bytes_per_launch": int(nbytes), "avg_launch_us": round(us, 2)}
+    a = nbytes / (us / 1e6) / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4), "bytes_per_launch": int(nbytes), "flops_per_launch": int(flops),
+            "avg_launch_us": round(us, 2)}
+
+
+def host_threads():
+    """Threads the CPU oracle may use: this process's cores, capped by
+    OMP_NUM_THREADS when the environment sets it (the share of a shared host)."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    try:
+        n = min(n, int(os.environ.get("OMP_NUM_THREADS", n)))
+    except ValueError:
+        pass
+    return max(1, n)
 
 
 def cpu_baseline(cfg, w, Kp, Vp, lay, lens, anchors, y, min_seconds=10.0, max_steps=20):
@@ -119,38 +167,34 @@ def cpu_baseline(cfg, w, Kp, Vp, lay, lens, anchors, y, min_seconds=10.0, max_st
     block, LM-head argmax, accept length), repeated until at least min_seconds of
     work (at most max_steps steps)."""
     import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import drafter as D
     from oracle.numerics import from_storage
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    cores = host_threads()
     t = np.arange(int(lens[0]))
     pages, slots = lay.block_table[0, t // cfg.page_size], t % cfg.page_size
     Kc, Vc = from_storage(Kp[:, pages, slots]), from_storage(Vp[:, pages, slots])
-    t0 = time.perf_counter()
-    steps = 0
-    while steps < max_steps and (steps == 0 or time.perf_counter() - t0 < min_seconds):
-        Z = D.draft_block(w, cfg, int(anchors[0]), Kc, Vc)
-        ids, _, _ = D.lm_argmax(w["lm_head"], Z)
-        D.accept_len(ids, y[0])
-        steps += 1
-    dt = time.perf_counter() - t0
-    # one more step on a single host thread
-    single = None
-    try:
-        from threadpoolctl import threadpool_limits
-        with threadpool_limits(limits=1):
-            t1 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        used = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        t0 = time.perf_counter()
+        steps = 0
+        while steps < max_steps and (steps == 0 or time.perf_counter() - t0 < min_seconds):
             Z = D.draft_block(w, cfg, int(anchors[0]), Kc, Vc)
-            D.lm_argmax(w["lm_head"], Z)
-            d1 = time.perf_counter() - t1
-        single = {"value": round((cfg.block_size - 1) / d1, 3), "seconds": round(d1, 2)}
-    except ImportError:
-        pass
+            ids, _, _ = D.lm_argmax(w["lm_head"], Z)
+            D.accept_len(ids, y[0])
+            steps += 1
+        dt = time.perf_counter() - t0
+    # one more step on a single host thread
+    with threadpool_limits(limits=1):
+        t1 = time.perf_counter()
+        Z = D.draft_block(w, cfg, int(anchors[0]), Kc, Vc)
+        D.lm_argmax(w["lm_head"], Z)
+        d1 = time.perf_counter() - t1
+    single = {"value": round((cfg.block_size - 1) / d1, 3), "seconds": round(d1, 2)}
     return {"value": round(steps * (cfg.block_size - 1) / dt, 3), "unit": "drafted tokens/s",
-            "cores": int(cores), "kind": "oracle", "seconds": round(dt, 2), "single_thread": single,
+            "cores": int(used), "host_cpu_count": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "kind": "oracle", "seconds": round(dt, 2), "single_thread": single,
             "sample": f"{steps} draft steps of sequence 0 ({cfg.block_size - 1} drafted tokens each, context "
                       f"{int(lens[0])}) in float64 numpy"}
 
@@ -354,13 +398,21 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # eager timed region: events on the launch stream bracket the draft pass and the LM head
+    # eager timed region: events on the launch stream bracket the draft pass and
+    # the LM head, and the library records a pair around each stage of every
+    # layer (dflash_set_stage_events) on the same stream
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    n_ev = 2 * len(L.STAGES) * cfg.n_layers
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
+    for evs in sev:            # a torch event creates its HIP event at its first record
+        for e in evs:
+            e.record()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for i in range(K):
+        L.dflash_set_stage_events(h, [e.cuda_event for e in sev[i]])
         ev[i][0].record()
         draft()
         ev[i][1].record()
@@ -369,9 +421,15 @@ def main():
         accept()
     e1.record()
     torch.cuda.synchronize()
+    L.dflash_set_stage_events(h, None)
     eager_ms = e0.elapsed_time(e1) / K
     draft_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
     lm_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    # stage_us[name]: every launch's duration in microseconds (K steps x layers)
+    stage_us = {name: np.array([sev[i][2 * (l * len(L.STAGES) + j)].elapsed_time(
+        sev[i][2 * (l * len(L.STAGES) + j) + 1]) * 1e3 for i in range(K) for l in range(cfg.n_layers)])
+        for j, name in enumerate(L.STAGES)}
+    stage_us["lm_head"] = lm_ms * 1e3
     assert np.array_equal(ids.cpu().numpy().reshape(b, B - 1), d0), "drafts changed between steps"
 
     graph_ms = None
@@ -414,20 +472,32 @@ def main():
     layers_b, lm_b, kv_b, emb_b = step_bytes(cfg, lens)
     total_b = layers_b + lm_b + kv_b + emb_b
     gemm_f, lm_f, attn_f = step_flops(cfg, lens)
-    lm_s = float(np.mean(lm_ms)) / 1e3
+    # per-stage figures; the roofline entry is the stage with the largest share
+    # of the step (its launches per step x average launch time)
+    costs = stage_costs(cfg, lens)
     if temp > 0:   # logits written and read back by the draw
-        lm_b += 2 * b * (B - 1) * cfg.vocab * 4
-    # the LM head is HBM-bound while its flops per weight byte (= rows) stay
-    # below the ridge peak_flops / peak_bandwidth (~312), MFMA-bound above
-    lm_rows = b * (B - 1)
-    lm_mfma = lm_rows > MFMA_PEAK_FLOPS / (HBM_PEAK_GBS * 1e9)
-    if lm_mfma:
-        roof = {"bound": "mfma", "achieved": round(lm_f / lm_s / 1e12, 1), "peak": MFMA_PEAK_FLOPS / 1e12,
-                "unit": "TFLOP/s", "frac": round(lm_f / lm_s / MFMA_PEAK_FLOPS, 4), "flops_per_launch": int(lm_f)}
-    else:
-        achieved = lm_b / lm_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        nb, nf = costs["lm_head"]
+        costs["lm_head"] = (nb + 2 * b * (B - 1) * cfg.vocab * 4, nf)
+    stage_step_us = {k: (1 if k == "lm_head" else cfg.n_layers) * float(np.mean(v)) for k, v in stage_us.items()}
+    stages = {}
+    for k, v in stage_us.items():
+        stages[k] = roofline_of(k, *costs[k], float(np.mean(v)))
+        stages[k].pop("kernel")
+        stages[k]["us_per_step"] = round(stage_step_us[k], 2)
+        stages[k]["share_of_step"] = round(stage_step_us[k] / (float(np.mean(draft_ms + lm_ms)) * 1e3), 4)
+    dom = max(stage_step_us, key=stage_step_us.get)
+    names = {"qkv": "attention RMSNorm + QKV projection + RoPE (one layer)",
+             "attention": "block attention over context + block (one layer)",
+             "o": "O projection + residual (one layer)",
+             "gate_up": "MLP RMSNorm + gate/up projection + SwiGLU (one layer)",
+             "down": "down projection + residual (one layer)",
+             "lm_head": ("lmhead_argmax (vocabulary GEMM with argmax epilogue + argmax reduce)" if temp <= 0
+                         else "lmhead logits (vocabulary GEMM, fp32 store) + dflash_sample")}
+    roof = roofline_of(names[dom], *costs[dom], float(np.mean(stage_us[dom])))
+    default_shape = args.config == "qwen3_8b" and temp <= 0 and args.block_size in (0, 16)
+    roof["traffic"] = recorded_traffic(dom) if default_shape else None
+    roof["launches_per_step"] = 1 if dom == "lm_head" else cfg.n_layers
+    roof["share_of_step"] = stages[dom]["share_of_step"]
     out = {
         "metric": METRIC,
         "value": round(b * (B - 1) / (ms / 1e3), 1),
@@ -456,10 +526,8 @@ def main():
                  "read_stream_gbs": round(stream_gbs, 1),
                  "hbm_frac_of_read_stream": round(total_b / (ms / 1e3) / 1e9 / stream_gbs, 4),
                  "mfma_frac_step": round((gemm_f + lm_f) / (ms / 1e3) / MFMA_PEAK_FLOPS, 4)},
-        "roofline": {"kernel": "lmhead_argmax (vocabulary GEMM with argmax epilogue + argmax reduce)" if temp <= 0
-                     else "lmhead logits (vocabulary GEMM, fp32 store) + dflash_sample", **roof,
-                     "traffic": recorded_traffic() if args.config == "qwen3_8b" and temp <= 0 and args.block_size in (0, 16) else None,
-                     "bytes_per_launch": int(lm_b), "avg_launch_us": round(lm_s * 1e6, 2)},
+        "roofline": roof,
+        "stages": stages,
     }
     if args.inject:
         fe = R.to_device(S.features(cfg, B * b, seed=1))

@@ -20,7 +20,11 @@ DFLASH_F32, DFLASH_BF16 = 0, 1
 EXPORTS = ("dflash_create", "dflash_destroy", "dflash_workspace_size", "dflash_workspace_init",
            "dflash_inject_context", "dflash_draft_block", "dflash_target_verify", "dflash_lmhead_argmax",
            "dflash_accept_len", "dflash_accept_len_ragged", "dflash_sample_workspace_size", "dflash_sample",
-           "dflash_accept_sample", "dflash_check_inputs", "dflash_stream_read", "dflash_status_str")
+           "dflash_accept_sample", "dflash_check_inputs", "dflash_set_stage_events", "dflash_stream_read",
+           "dflash_status_str")
+
+# measurement hook stages (include/dflash.h)
+STAGES = ("qkv", "attention", "o", "gate_up", "down")
 
 
 class DflashError(RuntimeError):
@@ -82,6 +86,7 @@ def load() -> ctypes.CDLL:
     lib.dflash_accept_sample.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, i32, f32, u64, u32, vp, vp, vp, sz,
                                          vp]
     lib.dflash_check_inputs.argtypes = [vp, ctypes.POINTER(DflashKV), vp, vp, i32, vp, vp, i32, vp, vp]
+    lib.dflash_set_stage_events.argtypes = [vp, ctypes.POINTER(vp), i32]
     lib.dflash_stream_read.argtypes = [vp, sz, vp, vp]
     lib.dflash_status_str.argtypes = [ctypes.c_int]
     lib.dflash_status_str.restype = ctypes.c_char_p
@@ -242,6 +247,16 @@ def make_kv(k, v, block_table, ctx_len, batch: int, max_pages: int, n_pages: int
             block_len=None) -> DflashKV:
     return DflashKV(k.data_ptr(), v.data_ptr(), block_table.data_ptr(), ctx_len.data_ptr(), batch, max_pages,
                     n_pages, max_ctx, ptr(block_len))
+
+
+def dflash_set_stage_events(h: int, events: Optional[Sequence[int]]) -> None:
+    """Turn the per-stage event hook on (a list of 2 * len(STAGES) * n_layers
+    raw hipEvent_t handles) or off (None)."""
+    if events is None:
+        _check(load().dflash_set_stage_events(h, None, 0), "dflash_set_stage_events")
+        return
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check(load().dflash_set_stage_events(h, arr, len(events)), "dflash_set_stage_events")
 
 
 def dflash_stream_read(src, sink, stream: Optional[int] = None) -> None:

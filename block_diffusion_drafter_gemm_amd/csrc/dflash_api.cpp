@@ -22,6 +22,8 @@ struct dflash_handle_s {
   bool bf16;
   size_t esz;  // bytes per stored element
   int n_cu;    // compute units of the current device (queried at the first launch)
+  // measurement hook: hipEvent_t pairs around each stage of each layer (empty: off)
+  std::vector<hipEvent_t> stage_events;
 };
 
 namespace {
@@ -105,12 +107,27 @@ InjectLayout inject_layout(const dflash_handle_s *h, int n_new) {
 
 int compute_units(dflash_handle_s *h);
 
-// Fill the launch geometry of ``a`` and launch: the LDS-tiled kernel for many
-// rows (bf16), and for 17..64 rows when its 128-row tiles still number at least
-// 64 (wide outputs: LM head, gate/up); otherwise the few-rows kernel.
+// Kernel choice of launch(): the LDS-tiled kernel for many rows (bf16), and for
+// 17..64 rows when its 128-row tiles still number at least 64 (wide outputs: LM
+// head, gate/up); otherwise the few-rows kernel.
+bool use_tiled(const dflash_handle_s *h, Epilogue epi, int M, int N, int K, int ffn, int hd, int z) {
+  const bool tiled_ok = h->bf16 && gemm_tiled_ok(epi, N, K, ffn, hd);
+  return tiled_ok && (M > 64 || (M > 16 && gemm_tiled_cols(epi, N, ffn) * z >= 64));
+}
+
+// Whether launch() can take this GEMM: the few-rows kernel puts its row groups
+// times the weight slices in grid.y (at most 65535).  Checked for every GEMM of
+// a call before that call enqueues anything.
+int gemm_fits(const dflash_handle_s *h, Epilogue epi, int M, int N, int K, int ffn, int hd, int z) {
+  if (use_tiled(h, epi, M, N, K, ffn, hd, z)) return DFLASH_OK;
+  const int MP = gemm_rows_per_group(M);
+  return (long)((M + MP - 1) / MP) * z > 65535 ? DFLASH_ERR_SHAPE : DFLASH_OK;
+}
+
+// Fill the launch geometry of ``a`` and launch (the kernel choice of use_tiled;
+// the caller has checked gemm_fits).
 int launch(const dflash_handle_s *h, Epilogue epi, GemmArgs &a, int z, hipStream_t st) {
-  const bool tiled_ok = h->bf16 && gemm_tiled_ok(epi, a.N, a.K, a.ffn, a.hd);
-  if (tiled_ok && (a.M > 64 || (a.M > 16 && gemm_tiled_cols(epi, a.N, a.ffn) * z >= 64))) {
+  if (use_tiled(h, epi, a.M, a.N, a.K, a.ffn, a.hd, z)) {
     a.m_groups = 1;
     a.n_groups = gemm_tiled_cols(epi, a.N, a.ffn);
     return launch_gemm_tiled(epi, a, z, compute_units(const_cast<dflash_handle_s *>(h)), st) == hipSuccess
@@ -120,7 +137,7 @@ int launch(const dflash_handle_s *h, Epilogue epi, GemmArgs &a, int z, hipStream
   const int MP = gemm_rows_per_group(a.M);
   a.m_groups = (a.M + MP - 1) / MP;
   a.n_groups = gemm_tiles(epi, a.N, a.ffn);
-  if ((long)a.m_groups * z > 65535) return DFLASH_ERR_SHAPE;
+  if ((long)a.m_groups * z > 65535) return DFLASH_ERR_SHAPE;   // unreachable after gemm_fits
   return launch_gemm(h->bf16, epi, a, z, st) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
@@ -294,6 +311,11 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
   const int kvd = c.n_kv_heads * c.head_dim, qd = c.n_q_heads * c.head_dim;
   const int KR = stream_res_k(h->bf16);
   const bool small = n_new <= 16;
+  // every launch shape is checked before anything is enqueued
+  if (!small && (gemm_fits(h, c.ctx_norm ? EPI_STORE_F32 : EPI_STORE, n_new, c.hidden, c.n_feat_layers * c.hidden,
+                           0, 0, 1) != DFLASH_OK ||
+                 gemm_fits(h, EPI_INJECT, n_new, 2 * kvd, c.hidden, 0, c.head_dim, c.n_layers) != DFLASH_OK))
+    return DFLASH_ERR_SHAPE;
 
   // A1: c = feats * W_fc^T (then RMSNorm(c) when the handle has ctx_norm)
   GemmArgs a;
@@ -341,6 +363,14 @@ int dflash_inject_context(dflash_handle h, const void *feats, const int32_t *seq
                : launch(h, EPI_INJECT, b, c.n_layers, s);
 }
 
+// Records the measurement hook's event for (layer, stage), before (end = 0) or
+// after (end = 1) the stage's launches; nothing when the hook is off.
+static int mark_stage(const dflash_handle_s *h, int layer, int stage, int end, hipStream_t s) {
+  if (h->stage_events.empty()) return DFLASH_OK;
+  const size_t i = 2 * ((size_t)layer * DFLASH_N_STAGES + stage) + end;
+  return hipEventRecord(h->stage_events[i], s) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
 // One pass of the handle's decoder over a block of B rows per sequence at
 // positions ctx_len[s] .. ctx_len[s] + B - 1.  Drafter (ids == NULL): rows are
 // the anchor and B - 1 mask tokens, attention is non-causal, the context cache
@@ -368,12 +398,19 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
   // (measured against the few-rows GEMM at 64 rows: O 26.4 -> 15.4 us; QKV and
   // down were slower that way and keep their kernels)
   const bool sliced = !fast && R <= 64 && qd <= KR;
+  // every launch shape is checked before anything is enqueued
+  if (!fast && (gemm_fits(h, EPI_QKV, R, qd + 2 * kvd, c.hidden, 0, c.head_dim, 1) != DFLASH_OK ||
+                (!sliced && gemm_fits(h, EPI_RESID, R, c.hidden, qd, 0, 0, 1) != DFLASH_OK) ||
+                gemm_fits(h, EPI_SWIGLU, R, 2 * c.ffn, c.hidden, c.ffn, 0, 1) != DFLASH_OK ||
+                gemm_fits(h, EPI_RESID, R, c.hidden, c.ffn, 0, 0, 1) != DFLASH_OK))
+    return DFLASH_ERR_SHAPE;
 
   if (!fast &&
       launch_embed(h->bf16, h->embed, anchor_ids, c.mask_token_id, ids, batch, B, c.hidden, X, s) != hipSuccess)
     return DFLASH_ERR_HIP;
   for (int l = 0; l < c.n_layers; ++l) {
     // A4: RMSNorm, QKV projection, RoPE; block q/k/v to the workspace
+    if ((st = mark_stage(h, l, DFLASH_STAGE_QKV, 0, s)) != DFLASH_OK) return st;
     GemmArgs q;
     memset(&q, 0, sizeof(q));
     q.W[0] = h->w_qkv[l];
@@ -415,6 +452,8 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
       st = launch(h, EPI_QKV, q, 1, s);
     }
     if (st != DFLASH_OK) return st;
+    if ((st = mark_stage(h, l, DFLASH_STAGE_QKV, 1, s)) != DFLASH_OK) return st;
+    if ((st = mark_stage(h, l, DFLASH_STAGE_ATTENTION, 0, s)) != DFLASH_OK) return st;
 
     // A5: attention over the paged context plus the block, no mask
     AttnArgs at;
@@ -450,8 +489,10 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
                                    static_cast<char *>(kv->v) + l * cache_layer, kv->block_table, kv->ctx_len, batch,
                                    B, kvd, kv->max_pages, c.page_size, s) != hipSuccess)
       return DFLASH_ERR_HIP;
+    if ((st = mark_stage(h, l, DFLASH_STAGE_ATTENTION, 1, s)) != DFLASH_OK) return st;
 
     // A6: O projection + residual
+    if ((st = mark_stage(h, l, DFLASH_STAGE_O, 0, s)) != DFLASH_OK) return st;
     GemmArgs o;
     memset(&o, 0, sizeof(o));
     o.A = w + L.O;
@@ -471,8 +512,10 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
          : sliced ? launch_rows(h, EPI_RESID, o, s)
                   : launch(h, EPI_RESID, o, 1, s);
     if (st != DFLASH_OK) return st;
+    if ((st = mark_stage(h, l, DFLASH_STAGE_O, 1, s)) != DFLASH_OK) return st;
 
     // A7: RMSNorm, gate/up + SwiGLU, down + residual
+    if ((st = mark_stage(h, l, DFLASH_STAGE_GATE_UP, 0, s)) != DFLASH_OK) return st;
     GemmArgs gu;
     memset(&gu, 0, sizeof(gu));
     gu.W[0] = h->w_gate_up[l];
@@ -497,6 +540,8 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
       st = launch(h, EPI_SWIGLU, gu, 1, s);
     }
     if (st != DFLASH_OK) return st;
+    if ((st = mark_stage(h, l, DFLASH_STAGE_GATE_UP, 1, s)) != DFLASH_OK) return st;
+    if ((st = mark_stage(h, l, DFLASH_STAGE_DOWN, 0, s)) != DFLASH_OK) return st;
 
     GemmArgs dn;
     memset(&dn, 0, sizeof(dn));
@@ -514,6 +559,7 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
     st = fast ? launch_stream(h, EPI_RESID, c.ffn <= KR ? AM_COPY : AM_PORTION, dn, 1, s)
               : launch(h, EPI_RESID, dn, 1, s);
     if (st != DFLASH_OK) return st;
+    if ((st = mark_stage(h, l, DFLASH_STAGE_DOWN, 1, s)) != DFLASH_OK) return st;
     for (int i = 0; i < n_taps; ++i)   // target hidden-state taps after this layer
       if (tap_layers[i] == l && launch_tap(h->bf16, X, R, c.hidden, i, n_taps, taps_out, s) != hipSuccess)
         return DFLASH_ERR_HIP;
@@ -523,6 +569,20 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
   if (launch_rmsnorm(h->bf16, X, h->final_norm, c.rms_eps, out_rows, c.hidden, B, !verify, hidden_out, s) !=
       hipSuccess)
     return DFLASH_ERR_HIP;
+  return DFLASH_OK;
+}
+
+int dflash_set_stage_events(dflash_handle h, void *const *events, int32_t n_events) {
+  if (!h) return DFLASH_ERR_NULL;
+  if (!events) {
+    h->stage_events.clear();
+    return DFLASH_OK;
+  }
+  if (n_events != 2 * DFLASH_N_STAGES * h->cfg.n_layers) return DFLASH_ERR_SHAPE;
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return DFLASH_ERR_NULL;
+  h->stage_events.assign(reinterpret_cast<const hipEvent_t *>(events),
+                         reinterpret_cast<const hipEvent_t *>(events) + n_events);
   return DFLASH_OK;
 }
 
@@ -567,6 +627,10 @@ int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int3
   // through L2 (with more groups each slice's compute units stream too many
   // tiles: 60 rows took 524 us against 181 us on the LDS-tiled path)
   const bool grouped = !small && rows <= 32 && c.hidden <= KR;
+  if (!small && !grouped &&
+      (gemm_fits(h, EPI_ARGMAX, rows, c.vocab, c.hidden, 0, 0, 1) != DFLASH_OK ||
+       gemm_fits(h, EPI_STORE_F32, rows, c.vocab, c.hidden, 0, 0, 1) != DFLASH_OK))
+    return DFLASH_ERR_SHAPE;
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.A = hidden;

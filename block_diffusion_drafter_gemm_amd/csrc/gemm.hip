@@ -107,14 +107,15 @@ __device__ void gemm_epilogue(const GemmArgs &a, const float *ct, int MP, int ro
       Storage<T>::store(dst, off + half, hi);
     }
   } else if constexpr (EPI == EPI_ARGMAX) {
-    // one thread per row: maximum of the 16 columns, lowest column on ties
+    // one thread per row: maximum of the 16 columns, lowest column on ties (a
+    // NaN never wins; no number above -inf leaves the first column)
     for (int r = tid; r < MP; r += blockDim.x) {
       const int row = row0 + r;
       if (row >= a.M) continue;
-      float best = ct[r * 16];
+      float best = -INFINITY;
       int bc = 0;
 #pragma unroll
-      for (int c = 1; c < 16; ++c) {
+      for (int c = 0; c < 16; ++c) {
         const float v = ct[r * 16 + c];
         if (v > best) { best = v; bc = c; }
       }

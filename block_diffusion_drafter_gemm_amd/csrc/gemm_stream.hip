@@ -170,16 +170,19 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
     }
   } else if constexpr (EPI == EPI_ARGMAX) {
     // running (max, lowest id) per row across this workgroup's tiles; tiles
-    // arrive in increasing order, so a strict comparison keeps the lowest id
+    // arrive in increasing order, so a strict comparison keeps the lowest id.
+    // A NaN never compares greater, so it never wins; the first tile always
+    // sets the id (best_i < 0), which keeps it a valid column when a row holds
+    // no number above -inf.
     if (tid < 16) {
-      float b = ct[tid * 16];
+      float b = -INFINITY;
       int bc = 0;
 #pragma unroll
-      for (int c = 1; c < 16; ++c) {
+      for (int c = 0; c < 16; ++c) {
         const float v = ct[tid * 16 + c];
         if (v > b) { b = v; bc = c; }
       }
-      if (b > *best_v) { *best_v = b; *best_i = t * 16 + bc; }
+      if (b > *best_v || *best_i < 0) { *best_v = b; *best_i = t * 16 + bc; }
     }
   }
 }
@@ -433,7 +436,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   }
 
   float best_v = -INFINITY;
-  int best_i = 0x7fffffff;
+  int best_i = -1;   // set by the first tile
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   // static ping-pong between two register buffers (dynamic selection would
   // spill the fragments to scratch): the next batch is issued before the
@@ -558,7 +561,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_portion_kernel(const GemmArgs 
 #undef DF_PORTION_STORE
 #undef DF_PORTION_MMA
   float best_v = -INFINITY;
-  int best_i = 0x7fffffff;
+  int best_i = -1;   // set by the first tile
   s_finish_tile<T, EPI>(a, acc, red, ct, t, layer, &best_v, &best_i, inv_freq, pre, true);
   if constexpr (EPI == EPI_ARGMAX) {
     if (tid < 16 && tid < a.M) {

@@ -125,12 +125,13 @@ __device__ void t_epilogue(const GemmArgs &a, const float *ct, int rb, int cb, i
       Storage<T>::store(dst, off + half, hi);
     }
   } else if constexpr (EPI == EPI_ARGMAX) {
-    // 2 threads per row, 64 columns each; lowest column on ties
+    // 2 threads per row, 64 columns each; lowest column on ties (a NaN never
+    // wins; no number above -inf leaves each half's first column)
     static_assert(BM % (NT / 2) == 0, "whole passes of NT / 2 rows");
     for (int r0 = 0; r0 < BM; r0 += NT / 2) {
       const int r = r0 + (tid >> 1), h = tid & 1, row = row0 + r;
       float best = -INFINITY;
-      int bc = 0x7fffffff;
+      int bc = h * 64;
       if (row < a.M) {
         for (int c = h * 64; c < h * 64 + 64; ++c) {
           const float v = ct[r * kTCStride + c];

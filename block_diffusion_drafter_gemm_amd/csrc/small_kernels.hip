@@ -72,7 +72,10 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const float *X, c
 }
 
 // Second level of the vocabulary argmax: one workgroup per row scans the
-// per-column-group maxima; the lowest id wins ties.
+// per-column-group maxima; the lowest id wins ties.  NaN partials count as
+// -inf and negative ids (a partial with no column) are skipped; the GEMM
+// epilogues start every partial at a valid column, so a row with no number
+// above -inf gets the lowest partial id, 0.
 __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float *val, const int *idx, int n_groups,
                                                             int *ids_out, float *max_out) {
   __shared__ float sv[4];
@@ -81,9 +84,10 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float *val, co
   float best = -INFINITY;
   int bidx = 0x7fffffff;
   for (int i = threadIdx.x; i < n_groups; i += blockDim.x) {
-    const float v = val[(size_t)r * n_groups + i];
+    const float v0 = val[(size_t)r * n_groups + i];
+    const float v = v0 != v0 ? -INFINITY : v0;
     const int id = idx[(size_t)r * n_groups + i];
-    if (v > best || (v == best && id < bidx)) { best = v; bidx = id; }
+    if (id >= 0 && (v > best || (v == best && id < bidx))) { best = v; bidx = id; }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float *val, co
   if (threadIdx.x == 0) {
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w)
       if (sv[w] > best || (sv[w] == best && si[w] < bidx)) { best = sv[w]; bidx = si[w]; }
-    ids_out[r] = bidx;
+    ids_out[r] = bidx == 0x7fffffff ? 0 : bidx;   // n_groups >= 1: always set
     if (max_out) max_out[r] = best;
   }
 }

@@ -16,8 +16,8 @@
  * (dflash_inject_context, dflash_draft_block, dflash_lmhead_argmax,
  * dflash_accept_len); the rest of the speculative cycle (dflash_target_verify,
  * dflash_accept_len_ragged, dflash_sample_workspace_size, dflash_sample,
- * dflash_accept_sample); dflash_check_inputs, dflash_stream_read and
- * dflash_status_str.
+ * dflash_accept_sample); dflash_check_inputs; measurement
+ * (dflash_set_stage_events, dflash_stream_read); dflash_status_str.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -203,7 +203,9 @@ int dflash_target_verify(dflash_handle h, const int32_t *ids, const dflash_kv *k
 
 /* A9: shared LM head and greedy argmax ([FN] §3.1; [SUM] §2.3).
  * logits = hidden * lm_head^T in fp32; ids_out[r] = the lowest id among the
- * maxima of row r.
+ * maxima of row r.  A NaN logit never wins; a row with no logit above -inf
+ * (all NaN or -inf) gets id 0 and max logit -inf, so ids_out always lies in
+ * [0, vocab).
  *   hidden        [rows, hidden] storage type
  *   ids_out       [rows] int32; may be NULL when logits_out is given (logits only,
  *                 the input of temperature sampling; max_logit_out is then unused)
@@ -312,6 +314,34 @@ int dflash_accept_sample(const float *draft_logits, const float *draft_lse, cons
                          int32_t batch, int32_t block_size, const int32_t *block_len, int32_t vocab,
                          float temperature, uint64_t seed, uint32_t offset, int32_t *accept_len_out,
                          int32_t *bonus_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Measurement hook (not a step of the method): HIP events recorded on the
+ * launch stream around each stage of every layer of dflash_draft_block and
+ * dflash_target_verify, so that a caller can time each kernel of the pass in
+ * place (the draft step is memory-bound, [FN] introduction and section 1, and
+ * each stage is reported against its own roofline).  Stages: QKV = the
+ * attention RMSNorm and QKV projection with RoPE; ATTENTION = block attention
+ * (and, in a target verify over more than 16 rows, the cache append); O = the
+ * output projection and residual; GATE_UP = the MLP RMSNorm, gate/up
+ * projection and SwiGLU; DOWN = the down projection and residual.
+ *   events   HOST array of n_events hipEvent_t handles (as void*), created by
+ *            the caller, or NULL to turn the hook off (the default).  The
+ *            array is copied; the events must outlive every call that records
+ *            them.  For layer l and stage s the pass records
+ *            events[2 * (l * DFLASH_N_STAGES + s)] before the stage's first
+ *            launch and events[2 * (l * DFLASH_N_STAGES + s) + 1] after its last.
+ *   n_events 2 * DFLASH_N_STAGES * n_layers when events is not NULL.
+ * Errors: NULL handle or a NULL entry (DFLASH_ERR_NULL), a wrong n_events
+ * (DFLASH_ERR_SHAPE). */
+enum {
+    DFLASH_STAGE_QKV = 0,
+    DFLASH_STAGE_ATTENTION = 1,
+    DFLASH_STAGE_O = 2,
+    DFLASH_STAGE_GATE_UP = 3,
+    DFLASH_STAGE_DOWN = 4,
+    DFLASH_N_STAGES = 5
+};
+int dflash_set_stage_events(dflash_handle h, void *const *events, int32_t n_events);
 
 /* Streaming read of `bytes` bytes at `src` (device, 16-byte aligned, bytes a
  * multiple of 16): every 32-bit word is XOR-folded into *sink (device, one

@@ -134,6 +134,48 @@ def test_target_verify_host_validation(lib):
         assert lib.dflash_destroy(h) == 0
 
 
+def test_launch_shapes_are_checked_before_anything_is_enqueued(lib):
+    """A call whose GEMM grid would not fit (fp32 handle: the few-rows kernel puts
+    row groups x weight slices in grid.y, at most 65535) returns
+    DFLASH_ERR_SHAPE before its first launch.  On this host any launch would
+    fail with DFLASH_ERR_HIP, so the shape error also shows nothing was
+    enqueued first (draft: the embedding kernel; inject: the fusion GEMM, whose
+    row groups alone still fit)."""
+    cfg = good_config(dtype="f32", block_size=16)
+    st, h = create(cfg)
+    assert st == 0 and h
+    huge = 1 << 62          # workspace size large enough for any of these calls
+    try:
+        rows = 64 * 65535 + 1
+        kv = L.DflashKV(FAKE, FAKE, FAKE, FAKE, (rows + 15) // 16, 8, 8, 64)
+        assert lib.dflash_draft_block(h, FAKE, ctypes.byref(kv), FAKE, FAKE, huge, None) == -2
+        assert lib.dflash_target_verify(h, FAKE, ctypes.byref(kv), None, 0, None, FAKE, FAKE, huge, None) == -2
+        kv1 = L.DflashKV(FAKE, FAKE, FAKE, FAKE, 1, 8, 8, 64)
+        n_new = 64 * 40000      # 40000 row groups: the fusion fits, 2 layers of K/V do not
+        assert lib.dflash_inject_context(h, FAKE, FAKE, FAKE, n_new, ctypes.byref(kv1), FAKE, huge, None) == -2
+    finally:
+        assert lib.dflash_destroy(h) == 0
+
+
+def test_stage_events_host_validation(lib):
+    """The measurement hook stores event handles only (no HIP call): NULL turns
+    it off; the count must be 2 * stages * layers; entries must not be NULL."""
+    st, h = create(good_config())
+    assert st == 0 and h
+    try:
+        n = 2 * len(L.STAGES) * 2
+        ev = (ctypes.c_void_p * n)(*([FAKE] * n))
+        se = lib.dflash_set_stage_events
+        assert se(None, ev, n) == -1
+        assert se(h, ev, n - 2) == -2
+        assert se(h, ev, n) == 0
+        assert se(h, None, 0) == 0
+        ev[3] = None
+        assert se(h, ev, n) == -1
+    finally:
+        assert lib.dflash_destroy(h) == 0
+
+
 def test_check_inputs_host_validation(lib):
     st, h = create(good_config())
     assert st == 0 and h

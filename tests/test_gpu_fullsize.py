@@ -6,16 +6,20 @@ context 16384).  The oracle recomputes sampled sequences one by one.
 
 Each workload runs in three variants:
 * bf16 storage, all layers.  Bar: per-row relative error of the hidden states
-  and of the logit vectors <= 5e-2.  An fp32-accumulation evaluation of the
-  same bf16 rounding contract already sits 2.2% (row norm) from the float64
-  oracle at the Qwen3-8B shape, because rounding flips cascade through the
-  layers; the bar is that floor with a factor ~2 margin.
-* fp32 storage of the same shapes, all layers: per-row relative error <= 1e-4
-  (measured floor 1.6e-5).  Same kernels and indexing as bf16, tight bar.
-* bf16 storage, one layer: elementwise <= 2e-2 * max(1, |oracle|)
-  (measured floor 7.8e-3).
+  and of the logit vectors <= 5e-2.  The bar is derived on the CPU by
+  ``tests/test_bf16_floor.py``: evaluating the same bf16 rounding contract with
+  fp32 instead of float64 accumulation already moves the Qwen3-8B-shape hidden
+  states by ~2.3% per row after 5 layers (rounding flips cascade through the
+  layers); 5e-2 is that floor with a factor ~2 margin.
+* fp32 storage of the same shapes, all layers: hidden states and the full
+  logit vectors elementwise within 1e-4 * max(1, |oracle|).  Same kernels and
+  indexing as bf16, tight bar.
+* bf16 storage, one layer: elementwise <= 2e-2 * max(1, |oracle|).
 Token ids must match except on oracle near-ties (2e-2 bf16 / 1e-4 fp32 of
-max(1, |logit|)); accept lengths must match exactly whenever the ids do.
+max(1, |logit|)).  Accept lengths and bonus tokens are compared bit for bit on
+identical inputs for every sampled sequence: the GPU's accept kernel on the
+oracle's own drafts (with the synthetic targets drawn for them) against the
+oracle's accept length, whatever the tie excuses.
 """
 import dataclasses
 
@@ -93,7 +97,7 @@ def test_full_draft_step(name, dtype, layers):
     log(f"[{name} {dtype} layers={cfg.n_layers}] GPU draft step")
     k0 = kv.k[:, :4].clone()
     hid = dr.draft_block(torch.from_numpy(anchors).cuda(), kv)
-    ids, mx, _ = dr.lmhead_argmax(hid)
+    ids, mx, lg = dr.lmhead_argmax(hid, want_logits=cfg.dtype == "f32")
     torch.cuda.synchronize()
     d_gpu = ids.cpu().numpy().reshape(b, B - 1)
     y_gpu = S.target_ids_for(cfg, d_gpu, seed=0)
@@ -102,17 +106,19 @@ def test_full_draft_step(name, dtype, layers):
     assert torch.equal(kv.k[:, :4], k0)
     tau, bonus = tau.cpu().numpy(), bonus.cpu().numpy()
     hid_h = from_storage(st["R"].to_host_storage(hid)).reshape(b, B - 1, cfg.hidden)
+    lg_h = lg.cpu().numpy().reshape(b, B - 1, cfg.vocab) if lg is not None else None
     pick = SAMPLED[name]
     seqs = (list(range(b)) if pick is None else
             [int(np.argmin(lens)), int(np.argmax(lens))] if pick == "minmax" else pick)
     tol = tol_of(cfg)
-    d_mixed = d_gpu.copy()
+    d_oracle = d_gpu.copy()
     for s in seqs:
         log(f"  oracle for sequence {s} (context {lens[s]})")
         Z = oracle_draft(cfg, w, anchors[s], st["Kp"], st["Vp"], lay.block_table, s, int(lens[s]))
         ids_o, best_o, logits_o = D.lm_argmax(w["lm_head"], Z)
         if cfg.dtype == "f32":
-            assert_rows_close(hid_h[s], Z, 1e-4, f"seq {s} hidden")
+            assert_close(hid_h[s], Z, 1e-4, f"seq {s} hidden")
+            assert_close(lg_h[s], logits_o, 1e-4, f"seq {s} logits ({cfg.vocab} per row)")
             assert_close(mx.cpu().numpy().reshape(b, B - 1)[s], best_o, 1e-4, f"seq {s} max logit")
         elif cfg.n_layers == 1:
             assert_close(hid_h[s], Z, 2e-2, f"seq {s} hidden")
@@ -120,14 +126,20 @@ def test_full_draft_step(name, dtype, layers):
         else:
             assert_rows_close(hid_h[s], Z, 5e-2, f"seq {s} hidden")
             logits_g = D.lm_logits(w["lm_head"], hid_h[s])   # oracle LM head on the GPU's hidden states
-            assert_rows_close(logits_o, D.lm_logits(w["lm_head"], Z), 1e-12, f"seq {s} oracle logits")
             assert_rows_close(logits_g, logits_o, 5e-2, f"seq {s} logits")
-        excused = check_ids(d_gpu[s], ids_o, logits_o, tol, f"seq {s} ids")
-        d_mixed[s] = ids_o
-        if not excused:
-            y_o = S.target_ids_for(cfg, d_mixed, seed=0)[s]
-            t_o, b_o = D.accept_len(ids_o, y_o)
-            assert (tau[s], bonus[s]) == (t_o, b_o)
+        check_ids(d_gpu[s], ids_o, logits_o, tol, f"seq {s} ids")
+        # accept length on identical inputs: the GPU's own drafts ...
+        assert (tau[s], bonus[s]) == D.accept_len(d_gpu[s], y_gpu[s])
+        d_oracle[s] = ids_o
+    # ... and the oracle's drafts with the targets drawn for them, through the
+    # GPU accept kernel: bit for bit, excused ids or not
+    y_oracle = S.target_ids_for(cfg, d_oracle, seed=0)
+    tau_o, bonus_o = dr.accept_len(torch.from_numpy(d_oracle).cuda(), torch.from_numpy(y_oracle).cuda(), B)
+    tau_o, bonus_o = tau_o.cpu().numpy(), bonus_o.cpu().numpy()
+    for s in seqs:
+        want = D.accept_len(d_oracle[s], y_oracle[s])
+        log(f"  seq {s}: tau {tau_o[s]} bonus {bonus_o[s]} on the oracle's drafts (oracle {want})")
+        assert (tau_o[s], bonus_o[s]) == want
     assert np.all((tau >= 1) & (tau <= B))
 
 
@@ -172,4 +184,5 @@ def test_full_lmhead_identical_input(rows):
         h.close()
     ids_o, best_o, logits_o = D.lm_argmax(w["lm_head"], z)
     assert_close(lg.cpu().numpy(), logits_o, 1e-4, "full-vocab logits")
-    check_ids(ids.cpu().numpy(), ids_o, logits_o, 2e-2, "full-vocab ids")
+    # identical inputs: ids may differ only within the fp32 logit bar
+    check_ids(ids.cpu().numpy(), ids_o, logits_o, 1e-4, "full-vocab ids")

@@ -76,19 +76,57 @@ def test_lmhead_argmax(name, rows):
     w["lm_head"][cfg.vocab - 3] = w["lm_head"][5]
     dr = R.Drafter(cfg, w, max_batch=(rows + cfg.block_size - 2) // (cfg.block_size - 1), max_ctx=16, max_new=1)
     z = S.normal_matrix(cfg, 77, (rows, cfg.hidden), 1.0, seed=rows)
-    # row 0 points at vocabulary row 5, so ids 5 and vocab-3 tie exactly at the top
-    z[0] = storage_of(cfg, round_storage(from_storage(w["lm_head"][5]) * 50.0, cfg.dtype))
+    # rows 0, 17 and 31 (the first, second and third 16-row groups when there are
+    # that many rows) point at vocabulary row 5, so ids 5 and vocab-3 tie
+    # exactly at the top
+    tie_rows = [r for r in (0, 17, 31) if r < rows]
+    for r in tie_rows:
+        z[r] = storage_of(cfg, round_storage(from_storage(w["lm_head"][5]) * (50.0 + r), cfg.dtype))
     z_dev = R.to_device(z)
     ids, mx, lg = dr.lmhead_argmax(z_dev, want_max=True, want_logits=True)
     torch.cuda.synchronize()
     ids_o, best_o, logits_o = D.lm_argmax(w["lm_head"], z)
     assert_close(lg.cpu().numpy(), logits_o, 1e-4, f"{name} logits")
     assert_close(mx.cpu().numpy(), best_o, 1e-4, f"{name} max logit")
-    check_ids(ids.cpu().numpy(), ids_o, logits_o, tol_of(cfg), f"{name} ids")
+    # identical inputs: ids may differ only within the fp32 logit bar
+    check_ids(ids.cpu().numpy(), ids_o, logits_o, 1e-4, f"{name} ids")
     # rows whose best is the duplicated row: the GPU must return the lower id 5
     g = ids.cpu().numpy()
-    assert g[0] == 5 and ids_o[0] == 5
+    for r in tie_rows:
+        assert g[r] == 5 and ids_o[r] == 5, r
     assert not np.any(g == cfg.vocab - 3)
+    dr.close()
+
+
+@pytest.mark.parametrize("name,rows", [("mini_bf16", 15), ("mini_bf16", 31), ("mini_b8", 130), ("mini_f32", 40),
+                                       ("mini_big", 300)])
+def test_lmhead_argmax_nan_logits(name, rows):
+    """NaN logits never win, and a row whose logits are all NaN returns id 0 with
+    max logit -inf (an id inside the vocabulary) on every LM-head path: the
+    streaming kernel (15 rows), two 16-row slices (31), the LDS-tiled (130) and
+    256 x 256-tile (300) kernels, and the fp32 few-rows kernel (40)."""
+    cfg = MINI[name]
+    log(f"lmhead_argmax NaN logits {name} rows={rows}")
+    R = runtime()
+    w = S.drafter_weights(cfg, seed=3)
+    nan = np.uint16(0x7FC0) if cfg.dtype == "bf16" else np.float32(np.nan)   # a quiet NaN
+    w["lm_head"][7] = nan                                     # column 7 of every row is NaN
+    z = S.normal_matrix(cfg, 78, (rows, cfg.hidden), 1.0, seed=rows)
+    z[rows // 2] = nan                                        # every logit of this row is NaN
+    dr = R.Drafter(cfg, w, max_batch=(rows + cfg.block_size - 2) // (cfg.block_size - 1), max_ctx=16, max_new=1)
+    ids, mx, _ = dr.lmhead_argmax(R.to_device(z), want_max=True)
+    torch.cuda.synchronize()
+    g, m = ids.cpu().numpy(), mx.cpu().numpy()
+    with np.errstate(invalid="ignore"):
+        logits_o = D.lm_logits(w["lm_head"], z)
+    for r in range(rows):
+        if r == rows // 2:
+            assert g[r] == 0 and m[r] == -np.inf, (r, g[r], m[r])
+            continue
+        o = int(np.nanargmax(logits_o[r]))
+        assert g[r] != 7 and 0 <= g[r] < cfg.vocab
+        lo = logits_o[r, o]
+        assert logits_o[r, g[r]] >= lo - 1e-4 * max(1.0, abs(lo)), (r, g[r], o)
     dr.close()
 
 
@@ -375,6 +413,29 @@ class GpuDrafter:
         return ids.cpu().numpy()
 
 
+class ShadowDrafter:
+    """The GPU drafter, checked at every cycle against the oracle drafter fed the
+    same injected features: the drafts must agree (ids may differ only on an
+    oracle near-tie within the fp32 bar)."""
+
+    def __init__(self, gpu: GpuDrafter, oracle: D.OracleDrafter):
+        self.gpu, self.oracle = gpu, oracle
+        self.excused, self.cycles = 0, 0
+
+    def inject(self, feats, pos):
+        self.gpu.inject(feats, pos)
+        self.oracle.inject(feats, pos)
+
+    def draft(self, anchor):
+        g = self.gpu.draft(anchor)
+        o = self.oracle
+        Z = D.draft_block(o.w, o.cfg, anchor, o.K, o.V)
+        ids_o, _, logits_o = D.lm_argmax(o.w["lm_head"], Z)
+        self.excused += check_ids(g, ids_o, logits_o, 1e-4, f"cycle {self.cycles} drafts")
+        self.cycles += 1
+        return g
+
+
 @pytest.mark.parametrize("seed,layer_std", [(0, 0.02), (1, 0.1), (2, 0.05)])
 def test_lossless_speculative_decoding_with_gpu_drafter(seed, layer_std):
     from oracle import target as T
@@ -384,13 +445,16 @@ def test_lossless_speculative_decoding_with_gpu_drafter(seed, layer_std):
     prompt = S.prompt_ids(cfg, seed)
     g = T.greedy_decode(tgt, prompt, cfg.new_tokens)
     gd = GpuDrafter(cfg, S.drafter_weights(cfg, seed), cfg.prompt_len + cfg.new_tokens + 2 * cfg.block_size)
-    s, taus = T.spec_decode(tgt, gd, prompt, cfg.new_tokens, cfg.dtype)
+    shadow = ShadowDrafter(gd, D.OracleDrafter(S.drafter_weights(cfg, seed), cfg))
+    s, taus = T.spec_decode(tgt, shadow, prompt, cfg.new_tokens, cfg.dtype)
     assert np.array_equal(g, s)
-    # the oracle drafter, run on the same inputs, drafts the same blocks
+    # the oracle drafter alone takes the same cycles unless a near-tie was excused
     s2, taus2 = T.spec_decode(tgt, D.OracleDrafter(S.drafter_weights(cfg, seed), cfg), prompt, cfg.new_tokens,
                               cfg.dtype)
     assert np.array_equal(s2, g)
-    log(f"  taus gpu {taus} oracle {taus2}")
+    log(f"  taus gpu {taus} oracle {taus2}; {shadow.excused} draft ids tie-excused over {shadow.cycles} cycles")
+    if shadow.excused == 0:
+        assert taus == taus2
     gd.d.close()
 
 
