@@ -16,6 +16,16 @@ B = 16) with the seeded inputs of the benchmark and asserts:
   fp32-exact implementation of the contract no margin) and within 2.5e-2, half
   the multi-layer bar 5e-2 the GPU tests use; the logit rows (a 16384-id slice
   of the vocabulary through the shared LM head) likewise.
+
+The target's causal verify pass (``oracle.target.verify_block``) over a block of
+random tokens at the same layer shape cascades further inside one layer: its
+residual-stream taps have a row RMS of ~2.4, and a flip in a row's normalised
+input moves every K/V element of the row.  ``test_bf16_verify_floor_at_qwen3_8b_layer``
+measures one layer at contexts 17, 77 and 300 and asserts that the floor stays
+within half the bars ``tests/test_gpu_target_bf16.py`` uses: the layer's own
+cache K/V rows elementwise (2e-2 * max(1, |oracle|)), the taps and final hidden
+states elementwise against max(1, |oracle|, RMS of the oracle row) (5e-2) and
+per row (2e-2).
 """
 import dataclasses
 
@@ -140,3 +150,75 @@ def test_bf16_contract_floor_at_qwen3_8b_shape(qwen3_inputs):
     assert el1 <= 1e-2
     assert 1.5e-2 < rows5 <= 2.5e-2
     assert lg5 <= 2.5e-2
+
+
+def verify_block_fp32_acc(w, cfg, ids, Kc, Vc):
+    """The oracle's causal verify pass (one layer per ``cfg.n_layers``) with every
+    product accumulated in fp32 and the same bf16 rounding points; returns the
+    final hidden states, the tap after every layer and the block K/V."""
+    n, p = len(ids), Kc.shape[1]
+    pos = np.arange(p, p + n)
+    nq, nkv, d, Fw = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn
+    X = np.stack([from_storage(w["embed"][i]) for i in ids]).astype(F32)
+    taps, Kb, Vb = [], [], []
+    allow = np.arange(p + n)[None, :] <= (p + np.arange(n))[:, None]
+    for l in range(cfg.n_layers):
+        W = lambda k: from_storage(w[k][l]).astype(F32)
+        Y = _st(_rms(X, W("attn_norm"), cfg.rms_eps))
+        qkv = Y @ W("w_qkv").T
+        q = _st(_rope(qkv[:, :nq * d].reshape(n, nq, d), pos, cfg.rope_theta))
+        k = _st(_rope(qkv[:, nq * d:(nq + nkv) * d].reshape(n, nkv, d), pos, cfg.rope_theta))
+        v = _st(qkv[:, (nq + nkv) * d:].reshape(n, nkv, d))
+        K = np.concatenate([Kc[l].astype(F32), k])
+        V = np.concatenate([Vc[l].astype(F32), v])
+        O = np.empty((n, nq, d), dtype=F32)
+        for h in range(nq):
+            g = h // (nq // nkv)
+            sc = np.where(allow, (q[:, h] @ K[:, g].T) / F32(np.sqrt(d)), F32(-np.inf))
+            e = np.exp(sc - sc.max(axis=1, keepdims=True))
+            O[:, h] = (e / e.sum(axis=1, keepdims=True, dtype=F32)) @ V[:, g]
+        X = X + _st(O).reshape(n, nq * d) @ W("w_o").T
+        Y = _st(_rms(X, W("mlp_norm"), cfg.rms_eps))
+        gu = Y @ W("w_gate_up").T
+        hm = _st(gu[:, :Fw] / (F32(1) + np.exp(-gu[:, :Fw])) * gu[:, Fw:])
+        X = X + hm @ W("w_down").T
+        taps.append(_st(X).astype(np.float64))
+        Kb.append(k.astype(np.float64))
+        Vb.append(v.astype(np.float64))
+    Z = _st(_rms(X, from_storage(w["final_norm"]).astype(F32), cfg.rms_eps)).astype(np.float64)
+    return Z, taps, np.stack(Kb), np.stack(Vb)
+
+
+def scaled_by_row(got, want):
+    """max |got - want| / max(1, |want|, RMS of want's row)."""
+    rms = np.sqrt((want ** 2).mean(axis=-1, keepdims=True))
+    return float((np.abs(got - want) / np.maximum(np.maximum(1.0, np.abs(want)), rms)).max())
+
+
+@pytest.mark.timeout(900)
+def test_bf16_verify_floor_at_qwen3_8b_layer():
+    from oracle import target as T
+    base = S.get_config("qwen3_8b")
+    worst = dict(kv=0.0, el=0.0, rows=0.0)
+    for ctx in (17, 77, 300):
+        cfg = dataclasses.replace(base, name="verify_floor", cid=121, vocab=2048, n_layers=1, n_feat_layers=1,
+                                  block_size=16, batch=1, ctx_min=ctx, ctx_max=ctx)
+        w = S.drafter_weights(cfg, seed=3, random_gain=True)
+        lens = np.array([ctx], dtype=np.int32)
+        lay = S.paged_layout(cfg, lens, headroom=16, seed=4)
+        Kp, Vp = S.ctx_kv_cache(cfg, lay, seed=4)
+        t = np.arange(ctx)
+        Kc = from_storage(Kp[:, lay.block_table[0, t // 16], t % 16])
+        Vc = from_storage(Vp[:, lay.block_table[0, t // 16], t % 16])
+        ids = np.random.default_rng(ctx + 16).integers(0, cfg.vocab, 16)
+        Z, To, Kb, Vb = T.verify_block(w, cfg, ids, Kc, Vc, tap_layers=[0])
+        Z32, taps32, Kb32, Vb32 = verify_block_fp32_acc(w, cfg, ids, Kc, Vc)
+        kv = max(float((np.abs(a - b) / np.maximum(1.0, np.abs(b))).max()) for a, b in ((Kb32, Kb), (Vb32, Vb)))
+        el = max(scaled_by_row(taps32[0], To), scaled_by_row(Z32, Z))
+        rows = max(_row_rel(taps32[0], To), _row_rel(Z32, Z))
+        print(f"verify floor, context {ctx}: cache K/V {kv:.3e}; taps and hidden {el:.3e} (row-scaled), "
+              f"{rows:.3e} per row")
+        worst = {k: max(worst[k], v) for k, v in dict(kv=kv, el=el, rows=rows).items()}
+    assert worst["kv"] <= 1e-2
+    assert worst["el"] <= 2.5e-2
+    assert worst["rows"] <= 1e-2

@@ -10,12 +10,23 @@ Three launch paths of the verify:
   slices and the cache append kernel;
 * 8 sequences x 32 rows (256 rows, one sequence a prompt prefill at context 0):
   the LDS-tiled GEMMs and the cache append kernel.
-Each runs with one decoder layer (hidden states, taps and cache rows
-elementwise within 2e-2 * max(1, |oracle|)) and two layers (the first layer's
-tap and cache rows elementwise; the final hidden states by per-row relative
-error within the multi-layer bar 5e-2), and with per-sequence block sizes
-B_s < B (rows below B_s against the oracle's pass over the first B_s tokens).
-The cache outside the written rows must be untouched.
+Each runs with one and with two decoder layers, and with per-sequence block
+sizes B_s < B (rows below B_s against the oracle's pass over the first B_s
+tokens).  The cache outside the written rows must be untouched.
+
+Bars (derived on the CPU by ``tests/test_bf16_floor.py::test_bf16_verify_floor_at_qwen3_8b_layer``,
+which evaluates the same pass with fp32 accumulation, as the GPU does):
+* the first layer's block K/V rows in the cache: elementwise
+  |g - o| <= 2e-2 * max(1, |o|) (floor 6e-3);
+* the first layer's residual tap and, with one layer, the final hidden states:
+  elementwise |g - o| <= 5e-2 * max(1, |o|, RMS of the oracle row) (floor
+  1.2e-2) and per-row relative error <= 2e-2 (floor 3.4e-3).  The taps are the
+  raw residual stream (row RMS ~2.4 here), and a rounding flip in a row's
+  normalised input moves every K/V element of that row, so within one causal
+  layer the flips cascade further than in the drafter's pass;
+* everything after the first layer (its K/V rows, taps and the final hidden
+  states of the two-layer cases): per-row relative error <= 5e-2, the
+  multi-layer bar (``tests/test_bf16_floor.py``).
 """
 import dataclasses
 
@@ -27,6 +38,14 @@ from oracle import target as T
 from oracle.numerics import from_storage
 
 from gpu_cases import assert_close, assert_rows_close, gather_ctx, log
+
+
+def assert_row_scaled(got, want, tol, what):
+    """|got - want| <= tol * max(1, |want|, RMS of want's row), elementwise."""
+    rms = np.sqrt((want ** 2).mean(axis=-1, keepdims=True))
+    err = np.abs(got - want) / np.maximum(np.maximum(1.0, np.abs(want)), rms)
+    log(f"  {what}: max row-scaled error {err.max():.3e} (tol {tol:g})")
+    assert err.max() <= tol, f"{what}: max row-scaled error {err.max():.3e} > {tol:g}"
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -109,15 +128,18 @@ def test_target_verify_bf16_qwen3_8b_layers(layers, B, lens, blens):
         written[:, pages, slots] = True
         Kg_s = from_storage(Kg[:, pages[:n], slots[:n]])
         Vg_s = from_storage(Vg[:, pages[:n], slots[:n]])
-        # the first layer's outputs: elementwise
-        assert_close(tp_h[s, :n, :H], To[:, :H], 2e-2, f"{what} tap after layer 0")
+        # the first layer's outputs
         assert_close(Kg_s[0], Kb[0], 2e-2, f"{what} cache K layer 0")
         assert_close(Vg_s[0], Vb[0], 2e-2, f"{what} cache V layer 0")
+        assert_row_scaled(tp_h[s, :n, :H], To[:, :H], 5e-2, f"{what} tap after layer 0")
+        assert_rows_close(tp_h[s, :n, :H], To[:, :H], 2e-2, f"{what} tap after layer 0")
         if layers == 1:
-            assert_close(hid_h[s, :n], Z, 2e-2, f"{what} hidden")
+            assert_row_scaled(hid_h[s, :n], Z, 5e-2, f"{what} hidden")
+            assert_rows_close(hid_h[s, :n], Z, 2e-2, f"{what} hidden")
         else:
-            assert_close(Kg_s[1:], Kb[1:], 2e-2, f"{what} cache K/V layers 1..")
-            assert_close(Vg_s[1:], Vb[1:], 2e-2, f"{what} cache V layers 1..")
+            for l in range(1, layers):
+                assert_rows_close(Kg_s[l].reshape(n, -1), Kb[l].reshape(n, -1), 5e-2, f"{what} cache K layer {l}")
+                assert_rows_close(Vg_s[l].reshape(n, -1), Vb[l].reshape(n, -1), 5e-2, f"{what} cache V layer {l}")
             assert_rows_close(tp_h[s, :n, H:], To[:, H:], 5e-2, f"{what} taps after layers 1..")
             assert_rows_close(hid_h[s, :n], Z, 5e-2, f"{what} hidden")
     # the context rows and every other slot are unchanged
