@@ -19,6 +19,7 @@ DFLASH_F32, DFLASH_BF16 = 0, 1
 
 EXPORTS = ("dflash_create", "dflash_destroy", "dflash_workspace_size", "dflash_workspace_init",
            "dflash_inject_context", "dflash_draft_block", "dflash_target_verify", "dflash_lmhead_argmax",
+           "dflash_lmhead_argmax_noalloc",
            "dflash_accept_len", "dflash_accept_len_ragged", "dflash_sample_workspace_size", "dflash_sample",
            "dflash_accept_sample", "dflash_check_inputs", "dflash_set_stage_events", "dflash_stream_read",
            "dflash_status_str")
@@ -78,6 +79,7 @@ def load() -> ctypes.CDLL:
     lib.dflash_draft_block.argtypes = [vp, vp, ctypes.POINTER(DflashKV), vp, vp, sz, vp]
     lib.dflash_target_verify.argtypes = [vp, vp, ctypes.POINTER(DflashKV), vp, i32, vp, vp, vp, sz, vp]
     lib.dflash_lmhead_argmax.argtypes = [vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.dflash_lmhead_argmax_noalloc.argtypes = [vp, vp, i32, vp, vp, vp]
     lib.dflash_accept_len.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     lib.dflash_accept_len_ragged.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
     u32, u64, f32 = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float
@@ -168,6 +170,13 @@ def dflash_lmhead_argmax(h: int, hidden, rows: int, ids_out, max_logit_out, logi
     _check(load().dflash_lmhead_argmax(h, ptr(hidden), rows, ptr(ids_out), ptr(max_logit_out), ptr(logits_out),
                                        ptr(ws), ws.numel() * ws.element_size(),
                                        current_stream() if stream is None else stream), "dflash_lmhead_argmax")
+
+
+def dflash_lmhead_argmax_noalloc(h: int, hidden, rows: int, ids_out, max_logit_out,
+                                 stream: Optional[int] = None) -> None:
+    _check(load().dflash_lmhead_argmax_noalloc(h, ptr(hidden), rows, ptr(ids_out), ptr(max_logit_out),
+                                               current_stream() if stream is None else stream),
+           "dflash_lmhead_argmax_noalloc")
 
 
 def dflash_accept_len(draft_ids, target_ids, batch: int, block_size: int, accept_len_out, bonus_out,

@@ -6,6 +6,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -220,6 +221,32 @@ int validate_kv(const dflash_handle_s *h, const dflash_kv *kv) {
 }
 
 }  // namespace
+
+// Scratch memory of dflash_lmhead_argmax_noalloc: the argmax partials live in
+// this array instead of a caller workspace.  Each device holds its own copy,
+// at its own address, until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// it passes the device address hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static std::mutex g_scratch_mu;
+static void *g_scratch_addr[kMaxDevices];
+
+static int scratch_on_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DFLASH_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DFLASH_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DFLASH_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return DFLASH_OK;
+}
 
 extern "C" {
 
@@ -610,12 +637,13 @@ int dflash_target_verify(dflash_handle h, const int32_t *ids, const dflash_kv *k
                        (hipStream_t)stream);
 }
 
-int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int32_t *ids_out, float *max_logit_out,
-                         float *logits_out, void *ws, size_t ws_bytes, void *stream) {
-  if (!h) return DFLASH_ERR_NULL;
-  if (rows < 0) return DFLASH_ERR_SHAPE;
-  if (rows == 0) return DFLASH_OK;
-  if (!hidden || !ws || (!ids_out && !logits_out)) return DFLASH_ERR_NULL;
+}  // extern "C"
+
+// The LM head and its argmax over ``rows`` hidden rows with the argmax partials
+// in ``ws`` (the caller's workspace, or the scratch array); arguments checked
+// by the entry points.
+static int lmhead_argmax_impl(dflash_handle h, const void *hidden, int32_t rows, int32_t *ids_out,
+                              float *max_logit_out, float *logits_out, void *ws, size_t ws_bytes, void *stream) {
   const dflash_config &c = h->cfg;
   const LmLayout L = lm_layout(h, rows);
   if (ws_bytes < L.total) return DFLASH_ERR_WORKSPACE;
@@ -665,6 +693,30 @@ int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int3
     if (st != DFLASH_OK) return st;
   }
   return DFLASH_OK;
+}
+
+extern "C" {
+
+int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int32_t *ids_out, float *max_logit_out,
+                         float *logits_out, void *ws, size_t ws_bytes, void *stream) {
+  if (!h) return DFLASH_ERR_NULL;
+  if (rows < 0) return DFLASH_ERR_SHAPE;
+  if (rows == 0) return DFLASH_OK;
+  if (!hidden || !ws || (!ids_out && !logits_out)) return DFLASH_ERR_NULL;
+  return lmhead_argmax_impl(h, hidden, rows, ids_out, max_logit_out, logits_out, ws, ws_bytes, stream);
+}
+
+int dflash_lmhead_argmax_noalloc(dflash_handle h, const void *hidden, int32_t rows, int32_t *ids_out,
+                                 float *max_logit_out, void *stream) {
+  if (!h) return DFLASH_ERR_NULL;
+  if (rows < 0) return DFLASH_ERR_SHAPE;
+  if (rows == 0) return DFLASH_OK;
+  if (!hidden || !ids_out) return DFLASH_ERR_NULL;
+  if (lm_layout(h, rows).total > kScratchBytes) return DFLASH_ERR_WORKSPACE;
+  void *scr = nullptr;
+  const int st = scratch_on_current_device(&scr);
+  if (st != DFLASH_OK) return st;
+  return lmhead_argmax_impl(h, hidden, rows, ids_out, max_logit_out, nullptr, scr, kScratchBytes, stream);
 }
 
 int dflash_accept_len(const int32_t *draft_ids, const int32_t *target_ids, int32_t batch, int32_t block_size,

@@ -14,7 +14,8 @@
  * Entry points: handle and workspace (dflash_create, dflash_destroy,
  * dflash_workspace_size, dflash_workspace_init); the drafter step
  * (dflash_inject_context, dflash_draft_block, dflash_lmhead_argmax,
- * dflash_accept_len); the rest of the speculative cycle (dflash_target_verify,
+ * dflash_accept_len; dflash_lmhead_argmax_noalloc for callers that cannot
+ * allocate); the rest of the speculative cycle (dflash_target_verify,
  * dflash_accept_len_ragged, dflash_sample_workspace_size, dflash_sample,
  * dflash_accept_sample); dflash_check_inputs; measurement
  * (dflash_set_stage_events, dflash_stream_read); dflash_status_str.
@@ -213,6 +214,22 @@ int dflash_target_verify(dflash_handle h, const int32_t *ids, const dflash_kv *k
  *   logits_out    [rows, vocab] fp32, may be NULL */
 int dflash_lmhead_argmax(dflash_handle h, const void *hidden, int32_t rows, int32_t *ids_out,
                          float *max_logit_out, float *logits_out, void *ws, size_t ws_bytes, void *stream);
+
+/* dflash_lmhead_argmax without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments and results as dflash_lmhead_argmax
+ * with logits_out NULL.  The argmax partials live in a scratch array inside the
+ * library instead of a caller workspace: 8 MiB per device, held until the
+ * process ends, its address looked up once per device on the first call made
+ * with that device current.  Calls may use up to
+ *   256 KiB + 2 * (rows * (vocab / 16) * 4 bytes, rounded up to 256) <= 8 MiB
+ * (106 rows at vocab 151936); more rows return DFLASH_ERR_WORKSPACE.  The
+ * call allocates nothing.  Every call on one device shares that device's
+ * array: calls that overlap on one GPU (two streams, two threads) race, so
+ * order them on one stream.  Nothing in the array needs clearing between
+ * calls (each call writes every partial it reads). */
+int dflash_lmhead_argmax_noalloc(dflash_handle h, const void *hidden, int32_t rows, int32_t *ids_out,
+                                 float *max_logit_out, void *stream);
 
 /* A10: greedy verify ([FN] §1 and §2 box, point (b)).  For each sequence,
  * k = the number of leading positions where draft_ids equals target_ids
