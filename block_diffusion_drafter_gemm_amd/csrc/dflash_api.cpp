@@ -583,7 +583,7 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
     dn.ldx = c.hidden;
     dn.part = o.part;
     dn.part_bytes = o.part_bytes;
-    st = fast ? launch_stream(h, EPI_RESID, c.ffn <= KR ? AM_COPY : AM_PORTION, dn, 1, s)
+    st = fast ? launch_stream(h, EPI_RESID, c.ffn <= KR ? AM_COPY : AM_GLOBAL, dn, 1, s)
               : launch(h, EPI_RESID, dn, 1, s);
     if (st != DFLASH_OK) return st;
     if ((st = mark_stage(h, l, DFLASH_STAGE_DOWN, 1, s)) != DFLASH_OK) return st;
