@@ -104,17 +104,28 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4, ln = lane & 15;
   const int item = blockIdx.x;
   const int f = item / a.nkv, g = item % a.nkv;
-  if (wave == 0) {
-    int sq, first;
-    find_seq(a.ctx_len, a.window, a.batch, a.block_size, a.chunk, f, &sq, &first);
-    if (lane == 0) { s_seq = sq; s_first = first; }
+  // One sequence and no sliding window: item f is chunk f of sequence 0, so
+  // its page-table entries are requested together with the context length and
+  // the query fragments (one round trip) instead of after a lookup of the
+  // item's sequence (three round trips; 1 us per launch, measured).
+  const bool single = a.batch == 1 && a.window == 0;
+  int spec_page = 0;
+  if (single && tid <= a.chunk / kPage)
+    spec_page = a.block_table[min((f * a.chunk) / kPage + tid, a.max_pages - 1)];
+  if (!single) {
+    if (wave == 0) {
+      int sq, first;
+      find_seq(a.ctx_len, a.window, a.batch, a.block_size, a.chunk, f, &sq, &first);
+      if (lane == 0) { s_seq = sq; s_first = first; }
+    }
+    __syncthreads();
+    if (s_seq < 0) return;
   }
-  __syncthreads();
-  const int s = s_seq;
-  if (s < 0) return;
-  const int c = f - s_first;
+  const int s = single ? 0 : s_seq;
+  const int c = single ? f : f - s_first;
   const int B = a.block_size, G = a.nq / a.nkv, GB = G * B;
   const int ctx = a.ctx_len[s];
+  if (single && f * a.chunk >= ctx + B) return;   // past the sequence's chunks (uniform)
   // block keys this sequence attends to (a per-sequence block size): the
   // attended keys stay one contiguous range, so a smaller block only ends it
   // earlier (a chunk past the end is empty and its partial carries no weight)
@@ -164,8 +175,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
   // page ids of the item's context keys, read once (a dependent global load per
   // key would serialise every in-flight K/V load behind it)
   const int p0 = kbeg / kPage;
-  for (int i = tid; i <= (min(kend, ctx) - 1) / kPage - p0 && kbeg < ctx; i += NT)
-    s_pages[i] = a.block_table[(size_t)s * a.max_pages + p0 + i];
+  if (single) {
+    if (tid <= a.chunk / kPage) s_pages[tid] = spec_page;   // entries past the context are never read
+  } else {
+    for (int i = tid; i <= (min(kend, ctx) - 1) / kPage - p0 && kbeg < ctx; i += NT)
+      s_pages[i] = a.block_table[(size_t)s * a.max_pages + p0 + i];
+  }
   __syncthreads();
   auto key_ptr = [&](int t, const T *ctxp, const T *blkp) -> const T * {
     if (t < ctx) {
@@ -410,6 +425,71 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const AttnArgs a) {
   for (int e = 0; e < PER; ++e) Storage<T>::store(O, ob + lane + 64 * e, acc[e] * inv);
 }
 
+// One sequence: a workgroup of four waves per (KV head, query row).  Wave w
+// combines chunks w, w + 4, .. (at most DW of them), each lane holding HD/64
+// consecutive head dims.  The number of chunks the partial launch computed is
+// known without the context length, so the statistics and partial outputs of
+// all of them are requested at once, with the context length (one round trip;
+// chunks past the sequence's own count are masked after it arrives).  The four
+// waves' (max, sum, weighted output) states are combined in LDS in wave order
+// (deterministic).
+template <typename T, int HD, int DW>
+__global__ __launch_bounds__(256) void attn_merge1_kernel(const AttnArgs a) {
+  constexpr int PER = HD / 64;
+  __shared__ float s_m[4], s_l[4];
+  __shared__ float s_o[4][HD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = a.block_size, G = a.nq / a.nkv, GB = G * B;
+  const int GBP = (GB + 15) / 16 * 16;
+  const int r = blockIdx.x % GB, g = blockIdx.x / GB;
+  const int nl = a.max_items / a.nkv;                  // chunks launched (>= the sequence's)
+  const int ctx = a.ctx_len[0];
+  float2 st[DW];
+  float po[DW][PER];
+#pragma unroll
+  for (int j = 0; j < DW; ++j) {
+    const int cc = min(wave + 4 * j, nl - 1);
+    const size_t it = (size_t)cc * a.nkv + g;
+    st[j] = *reinterpret_cast<const float2 *>(a.stats + (it * GBP + r) * 2);
+    const float *pp = a.partial + (it * GBP + r) * HD + PER * lane;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) po[j][e] = pp[e];
+  }
+  const int nch = min(nl, (attended_ctx(ctx, a.window) + B + a.chunk - 1) / a.chunk);
+  float m = -1e30f;
+#pragma unroll
+  for (int j = 0; j < DW; ++j)
+    if (wave + 4 * j < nch) m = fmaxf(m, st[j].x);
+  float l = 0.f, o[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) o[e] = 0.f;
+#pragma unroll
+  for (int j = 0; j < DW; ++j) {
+    const bool live = wave + 4 * j < nch;
+    const float wgt = live ? exp2f(st[j].x - m) : 0.f;
+    l += live ? wgt * st[j].y : 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] += live ? wgt * po[j][e] : 0.f;
+  }
+  if (lane == 0) { s_m[wave] = m; s_l[wave] = l; }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) s_o[wave][PER * lane + e] = o[e];
+  __syncthreads();
+  if (tid < HD) {
+    const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    float L = 0.f, v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float sc = exp2f(s_m[w] - M);
+      L += sc * s_l[w];
+      v += sc * s_o[w][tid];
+    }
+    const int hh = r / B, jb = r % B;
+    T *O = (T *)a.o;
+    Storage<T>::store(O, ((size_t)jb * a.nq + g * G + hh) * HD + tid, L > 0.f ? v / L : 0.f);
+  }
+}
+
 template <typename T, int HD>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   const int GBq = (a.nq / a.nkv) * a.block_size;
@@ -419,7 +499,12 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int GB = (a.nq / a.nkv) * a.block_size;
   const int max_chunks = a.max_items / (a.batch * a.nkv);
-  if (max_chunks <= 16)
+  if (a.batch == 1 && max_chunks <= 64) {
+    const dim3 grid(a.nkv * GB), block(256);
+    if (max_chunks <= 16) hipLaunchKernelGGL((attn_merge1_kernel<T, HD, 4>), grid, block, 0, st, a);
+    else if (max_chunks <= 32) hipLaunchKernelGGL((attn_merge1_kernel<T, HD, 8>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_merge1_kernel<T, HD, 16>), grid, block, 0, st, a);
+  } else if (max_chunks <= 16)
     hipLaunchKernelGGL((attn_merge_kernel<T, HD, 16>), dim3(a.batch * a.nkv * GB), dim3(64), 0, st, a);
   else
     hipLaunchKernelGGL((attn_merge_kernel<T, HD, 64>), dim3(a.batch * a.nkv * GB), dim3(64), 0, st, a);

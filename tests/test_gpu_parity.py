@@ -254,6 +254,34 @@ def test_draft_block(name):
     run_draft_case(MINI[name], seed=0)
 
 
+@pytest.mark.parametrize("ctx,window,blen", [(17, 0, 0), (1500, 0, 0), (3000, 0, 0), (1500, 100, 0), (3000, 0, 5),
+                                              (0, 0, 0)])
+def test_draft_block_single_sequence(ctx, window, blen):
+    """One sequence (the batch-1 attention path: page-table entries requested
+    with the context length, four-wave merge of the chunk partials) at contexts
+    of 1, 24 and 48 chunks, with a sliding window and with a block size B_s < B,
+    against the oracle."""
+    cfg = dataclasses.replace(MINI["mini_bf16"], name="mini_one", batch=1, window=window)
+    log(f"draft_block one sequence ctx={ctx} window={window} B_s={blen or cfg.block_size}")
+    R = runtime()
+    w = S.drafter_weights(cfg, seed=7, random_gain=True)
+    lens = np.array([ctx], dtype=np.int32)
+    lay = S.paged_layout(cfg, lens, headroom=cfg.block_size, seed=7)
+    Kp, Vp = S.ctx_kv_cache(cfg, lay, seed=7)
+    anchors = S.anchor_ids(cfg, seed=7, batch=1)
+    dr = R.Drafter(cfg, w, max_batch=1, max_ctx=ctx, max_new=1)
+    kv = R.PagedKV(cfg, lay.block_table, lens, lay.n_pages, k=Kp, v=Vp)
+    bs = blen or cfg.block_size
+    if blen:
+        kv.set_block_len(np.array([blen]))
+    hid = dr.draft_block(torch.from_numpy(anchors).cuda(), kv)
+    torch.cuda.synchronize()
+    hid_h = from_storage(R.to_host_storage(hid)).reshape(cfg.block_size - 1, cfg.hidden)
+    Z = oracle_draft(dataclasses.replace(cfg, block_size=bs), w, anchors[0], Kp, Vp, lay.block_table, 0, ctx)
+    assert_close(hid_h[:bs - 1], Z, tol_of(cfg), f"one sequence ctx {ctx} hidden")
+    dr.close()
+
+
 @pytest.mark.parametrize("name,window", [("mini_bf16", 100), ("mini_d64", 50), ("mini_f32", 40)])
 def test_draft_block_sliding_window(name, window):
     """Sliding-window context (ragged contexts above and below the window;
