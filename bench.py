@@ -120,6 +120,56 @@ def recorded_traffic(stage: str):
         return None
 
 
+class FenceFreeEvents:
+    """HIP timing events created with hipEventDisableSystemFence: recording one
+    adds no system-scope cache writeback and invalidate to the stream (torch's
+    events do), so a pair brackets a stage the way the kernel trace times it.
+    Made through the HIP runtime that torch and the library share in this
+    process."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n: int):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) >= 6 and os.path.basename(parts[-1]).startswith("libamdhip64.so"):
+                    path = parts[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime library is not loaded")
+        rt = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        rt.hipEventRecord.argtypes = [vp, vp]
+        rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        rt.hipEventDestroy.argtypes = [vp]
+        self.ctypes, self.rt, self.ev = ctypes, rt, []
+        for _ in range(n):
+            e = vp()
+            self._check(rt.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE), "create")
+            self.ev.append(e.value)
+
+    @staticmethod
+    def _check(err, what):
+        if err != 0:
+            raise RuntimeError(f"hipEvent {what} failed: error {err}")
+
+    def record(self, i: int, stream: int) -> None:
+        self._check(self.rt.hipEventRecord(self.ev[i], stream), "record")
+
+    def ms(self, i: int, j: int) -> float:
+        f = self.ctypes.c_float()
+        self._check(self.rt.hipEventElapsedTime(self.ctypes.byref(f), self.ev[i], self.ev[j]), "elapsed")
+        return f.value
+
+    def close(self) -> None:
+        for e in self.ev:
+            self.rt.hipEventDestroy(e)
+        self.ev = []
+
+
 def stage_costs(cfg, lens):
     """Algorithmic bytes and flops of one launch of each stage (one layer; the
     LM head over all mask rows): weights once, valid context K/V once."""
@@ -400,36 +450,41 @@ def main():
 
     # eager timed region: events on the launch stream bracket the draft pass and
     # the LM head, and the library records a pair around each stage of every
-    # layer (dflash_set_stage_events) on the same stream
+    # layer (dflash_set_stage_events) on the same stream.  Event i of step k is
+    # E.ev[2 + k * per + i]: 0, 1, 2 around the draft pass and the LM head, then
+    # the stage pairs; E.ev[0], E.ev[1] bracket all K steps.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     n_ev = 2 * len(L.STAGES) * cfg.n_layers
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(K)]
-    for evs in sev:            # a torch event creates its HIP event at its first record
-        for e in evs:
-            e.record()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = 3 + n_ev
+    E = FenceFreeEvents(2 + K * per)
+    ev = lambda k, i: 2 + k * per + i
+    stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
-    e0.record()
+    # hold the stream with a spin kernel while the host enqueues the K steps, so
+    # the GPU runs them back to back: launched one by one, an eager step takes
+    # longer to enqueue than to run, and the gaps would count as stage time
+    torch.cuda._sleep(int(K * 3e-3 * 2.1e9))
+    E.record(0, stream)
     for i in range(K):
-        L.dflash_set_stage_events(h, [e.cuda_event for e in sev[i]])
-        ev[i][0].record()
+        L.dflash_set_stage_events(h, E.ev[ev(i, 3):ev(i, per)])
+        E.record(ev(i, 0), stream)
         draft()
-        ev[i][1].record()
+        E.record(ev(i, 1), stream)
         lmhead()
-        ev[i][2].record()
+        E.record(ev(i, 2), stream)
         accept()
-    e1.record()
+    E.record(1, stream)
     torch.cuda.synchronize()
     L.dflash_set_stage_events(h, None)
-    eager_ms = e0.elapsed_time(e1) / K
-    draft_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
-    lm_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    eager_ms = E.ms(0, 1) / K
+    draft_ms = np.array([E.ms(ev(i, 0), ev(i, 1)) for i in range(K)])
+    lm_ms = np.array([E.ms(ev(i, 1), ev(i, 2)) for i in range(K)])
     # stage_us[name]: every launch's duration in microseconds (K steps x layers)
-    stage_us = {name: np.array([sev[i][2 * (l * len(L.STAGES) + j)].elapsed_time(
-        sev[i][2 * (l * len(L.STAGES) + j) + 1]) * 1e3 for i in range(K) for l in range(cfg.n_layers)])
-        for j, name in enumerate(L.STAGES)}
+    stage_us = {name: np.array([E.ms(ev(i, 3 + 2 * (l * len(L.STAGES) + j)), ev(i, 4 + 2 * (l * len(L.STAGES) + j)))
+                                * 1e3 for i in range(K) for l in range(cfg.n_layers)])
+                for j, name in enumerate(L.STAGES)}
     stage_us["lm_head"] = lm_ms * 1e3
+    E.close()
     assert np.array_equal(ids.cpu().numpy().reshape(b, B - 1), d0), "drafts changed between steps"
 
     graph_ms = None
@@ -451,17 +506,16 @@ def main():
             g.replay()
         torch.cuda.synchronize()
         ids.zero_()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        gev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-        g0.record()
-        gev[0].record()
+        # event i brackets replay i - 1 and i (fence-free events, as above)
+        GE = FenceFreeEvents(K + 1)
+        GE.record(0, stream)
         for i in range(K):
             g.replay()
-            gev[i + 1].record()
-        g1.record()
+            GE.record(i + 1, stream)
         torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / K
-        graph_step_ms = np.array([gev[i].elapsed_time(gev[i + 1]) for i in range(K)])
+        graph_ms = GE.ms(0, K) / K
+        graph_step_ms = np.array([GE.ms(i, i + 1) for i in range(K)])
+        GE.close()
         assert np.array_equal(ids.cpu().numpy().reshape(b, B - 1), d0), "graph replay drafts differ from eager"
 
     ms = graph_ms if graph_ms is not None else eager_ms
