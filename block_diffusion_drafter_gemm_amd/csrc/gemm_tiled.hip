@@ -461,6 +461,167 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const GemmArgs a, int n_r
   }
 }
 
+// ---- 256 x 192 tiles for gate/up + SwiGLU -------------------------------------
+//
+// The 256 x 256 kernel's schedule with 192 weight rows per tile (96 gate rows
+// beside their 96 up rows): each wave accumulates 128 rows x 96 columns as
+// 4 x 3 tiles of 32x32x16 products, so a 512-row gate/up of FFN 12288 is 256
+// tiles, one per compute unit, instead of 192 tiles of 256 x 256 that leave a
+// quarter of the compute units idle.  Per step a wave issues 4 activation and
+// 3 weight loads (weight stage: 192 rows of 128 bytes, 24 pieces of 1 KB, half
+// a stage per step).  The smaller weight stages leave room for a fourth one,
+// so weight halves are requested 7 steps ahead instead of 5 (the weights come
+// from HBM; the loop waits on them, not on the matrix cores).  K is walked in the same order as the 256 x 256 kernel,
+// so both give identical sums.  Epilogue: the up waves (wc = 1) hand their
+// accumulators to the gate waves through LDS, which write silu(gate) * up.
+constexpr int kB3N = 192, kB3WStage = kB3N * 128, kB3WStages = 4;
+constexpr int kB3WBase = kBAStages * kBAStage;
+constexpr int kB3Lds = kB3WBase + kB3WStages * kB3WStage;   // 160 KB
+static_assert(2 * 128 * 96 * 4 <= kB3Lds, "up-value exchange fits");
+
+__global__ __launch_bounds__(256) void gemm_swiglu192_kernel(const GemmArgs a, int n_rb, int n_ct, int per_xcd) {
+  using T = bf16_t;
+  constexpr int NJ = 3, WPW = 3;                           // column tiles and weight loads per wave
+  __shared__ __align__(16) unsigned char lds[kB3Lds];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int layer = blockIdx.y;
+  // row-block-major order: an XCD's tiles share one 256-row block of the
+  // activations (2 MB at 4096 columns, resident in that XCD's L2 beside the
+  // weight stream) instead of needing both
+  const int tile = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (tile >= n_rb * n_ct) return;
+  const int rb = tile / n_ct, ct_ = tile % n_ct;
+  const T *A = (const T *)a.A;
+  const T *W = (const T *)a.W[layer];
+  const int row0 = rb * kBT;
+
+  // activation pieces as in the 256 x 256 kernel; weight piece i of half h:
+  // rows 8q .. 8q+7, q = 12h + 3*wave + i (tile column c -> gate row ct*96 + c
+  // for c < 96, else up row ffn + ct*96 + c - 96)
+  const T *asrc[4], *wsrc[2][WPW];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * (4 * wave + i) + (lane >> 2);
+    asrc[i] = A + (size_t)min(row0 + r, a.M - 1) * a.lda + ((lane & 3) ^ ((r >> 2) & 3)) * 8;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < WPW; ++i) {
+      const int c = 8 * (12 * h + WPW * wave + i) + (lane >> 3);
+      const int wrow = c < 96 ? ct_ * 96 + c : a.ffn + ct_ * 96 + (c - 96);
+      wsrc[h][i] = W + (size_t)wrow * a.ldw + ((lane & 7) ^ ((c >> 1) & 7)) * 8;
+    }
+  const int nk = a.K / kBK, nw = nk / 2;
+  const unsigned lds0 = lds_offset(lds);
+  auto a_load = [&](int s, int i) {
+    const int s_ = min(s, nk - 1);
+    lds_dma16(asrc[i] + s_ * kBK, lds0 + (s % kBAStages) * kBAStage + (4 * wave + i) * 1024);
+  };
+  auto w_load = [&](int j, int i) {
+    const int w = j >> 1, h = j & 1, w_ = min(w, nw - 1);
+    lds_dma16(wsrc[h][i] + w_ * 2 * kBK,
+              lds0 + kB3WBase + (w % kB3WStages) * kB3WStage + (12 * h + WPW * wave + i) * 1024);
+  };
+
+  const int wr = wave >> 1, wc = wave & 1;
+  f32x16 acc[4][NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const int fr = lane & 31, fk = lane >> 5;
+  const int swa = (fr >> 2) & 3, sww = (fr >> 1) & 7;
+  auto read_frag = [&](int kt, int g, Frag<T> (&af)[2][4], Frag<T> (&bf)[2][NJ]) {
+    const int sub = g >> 2, i = g & 3, c = 2 * sub + fk;
+    const unsigned char *ab = lds + (kt % kBAStages) * kBAStage;
+    const unsigned char *wb = lds + kB3WBase + ((kt >> 1) % kB3WStages) * kB3WStage;
+    af[sub][i].v = *reinterpret_cast<const uint4 *>(ab + (wr * 128 + i * 32 + fr) * 64 + ((c ^ swa) << 4));
+    if (i < NJ)
+      bf[sub][i].v = *reinterpret_cast<const uint4 *>(wb + (wc * 96 + i * 32 + fr) * 128 +
+                                                      (((4 * (kt & 1) + c) ^ sww) << 4));
+  };
+  constexpr int kLgkm0 = ~(0xF << 8);
+  constexpr int kPerStep = 4 + WPW;                        // loads a wave issues per step
+#define DF_B3STEP(kt, FA, FB, GA, GB)                                                               \
+  do {                                                                                              \
+    asm volatile("" ::: "memory");                                                                  \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPerStep) & kLgkm0);                                   \
+    __builtin_amdgcn_s_barrier();                                                                   \
+    asm volatile("" ::: "memory");                                                                  \
+    _Pragma("unroll") for (int g = 0; g < 8; ++g) {                                                 \
+      const int sub_ = g >> 2, i_ = g & 3;                                                          \
+      _Pragma("unroll") for (int j = 0; j < NJ; ++j) acc[i_][j] = mma32(acc[i_][j], FA[sub_][i_], FB[sub_][j]); \
+      if (g < 4) a_load((kt) + 4, g);                                                               \
+      else if (g - 4 < WPW) w_load((kt) + 7, g - 4);                                                \
+      read_frag((kt) + 1, g, GA, GB);                                                               \
+      __builtin_amdgcn_sched_barrier(0);                                                            \
+    }                                                                                               \
+  } while (0)
+  // prologue in the steady state's order: weight halves 0..2, then for
+  // p = -4 .. -1 activation stage p+4 and weight half p+7.  Step kt waits for
+  // everything issued before step kt-2; a weight half issued at step kt lands
+  // in the slot of a stage whose last fragments were read during step kt-1.
+  Frag<T> a0[2][4], b0[2][NJ], a1[2][4], b1[2][NJ];
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int i = 0; i < WPW; ++i) w_load(j, i);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a_load(p, i);
+#pragma unroll
+    for (int i = 0; i < WPW; ++i) w_load(p + 3, i);
+  }
+  // step 0 needs weight halves 0, 1 and activation stage 0: all but the last
+  // 3 rounds of 7 and the 3 loads of half 3
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kPerStep + WPW));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int g = 0; g < 8; ++g) read_frag(0, g, a0, b0);
+  for (int kt = 0; kt < nk; kt += 2) {
+    DF_B3STEP(kt, a0, b0, a1, b1);
+    DF_B3STEP(kt + 1, a1, b1, a0, b0);
+  }
+#undef DF_B3STEP
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // up waves hand their values to the gate waves: [wr][128 rows][96 columns] fp32
+  float *up = reinterpret_cast<float *>(lds) + wr * 128 * 96;
+  if (wc == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) up[(i * 32 + 8 * (e / 4) + 4 * fk + e % 4) * 96 + j * 32 + fr] = acc[i][j][e];
+  }
+  __syncthreads();
+  if (wc == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rl = i * 32 + 8 * (e / 4) + 4 * fk + e % 4, row = row0 + wr * 128 + rl;
+        if (row < a.M) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const float gt = acc[i][j][e], u = up[rl * 96 + j * 32 + fr];
+            Storage<T>::store((T *)a.out, (size_t)row * a.ldo + ct_ * 96 + j * 32 + fr, gt / (1.0f + expf(-gt)) * u);
+          }
+        }
+      }
+  }
+}
+
 template <int EPI>
 static void launch_big_t(const GemmArgs &a, int z_slices, hipStream_t st) {
   const int n_rb = (a.M + kBT - 1) / kBT, n_ct = (a.n_groups + 1) / 2;
@@ -534,7 +695,23 @@ static void launch_splitk_resid(const GemmArgs &a, int splits, int cu, hipStream
 hipError_t launch_gemm_tiled(Epilogue epi, GemmArgs &a, int z_slices, int cu, hipStream_t st) {
   a.kper = a.K;
   const long big_tiles = (long)((a.M + kBT - 1) / kBT) * ((a.n_groups + 1) / 2) * z_slices;
-  if (a.M > 128 && big_tiles >= kBigMinTiles) return launch_big(epi, a, z_slices, st);
+  if (a.M > 128 && big_tiles >= kBigMinTiles) {
+    // gate/up: 256 x 192 tiles where they fill the compute units' rounds
+    // better than 256 x 256 (e.g. 512 rows of FFN 12288: 256 tiles against 192)
+    if (epi == EPI_SWIGLU && a.ffn % 96 == 0 && a.K % (2 * kBK) == 0) {
+      const int n_rb = (a.M + kBT - 1) / kBT, n_ct3 = a.ffn / 96;
+      const long t3 = (long)n_rb * n_ct3 * z_slices;
+      const double fill3 = (double)t3 / (double)(((t3 + cu - 1) / cu) * cu);
+      const double fill4 = (double)big_tiles / (double)(((big_tiles + cu - 1) / cu) * cu);
+      if (fill3 > fill4 * 1.05) {
+        const int per_xcd = (int)((n_rb * (long)n_ct3 + 7) / 8);
+        hipLaunchKernelGGL(gemm_swiglu192_kernel, dim3(8 * per_xcd, z_slices), dim3(256), 0, st, a, n_rb, n_ct3,
+                           per_xcd);
+        return hipGetLastError();
+      }
+    }
+    return launch_big(epi, a, z_slices, st);
+  }
   const long tiles256 = (long)((a.M + 255) / 256) * a.n_groups * z_slices;
   if (tiles256 >= 512) return launch_tiled_bm<256>(epi, a, z_slices, 1, st);
   const long tiles = (long)((a.M + 127) / 128) * a.n_groups * z_slices;

@@ -254,6 +254,16 @@ def test_draft_block(name):
     run_draft_case(MINI[name], seed=0)
 
 
+def test_draft_block_gate_up_256x192_tiles():
+    """20 sequences x B 16 = 320 block rows of the mini_big shape (FFN 20544):
+    gate/up takes the 256 x 192-tile kernel with two row blocks, the second
+    ragged (64 of 256 rows), and 214 column tiles; checked against the oracle
+    on the first, a middle and the last sequence (rows 0, 150, 319)."""
+    cfg = dataclasses.replace(MINI["mini_big"], name="mini_big20", batch=20)
+    log("draft_block mini_big x 20 sequences (256 x 192 gate/up tiles)")
+    run_draft_case(cfg, seed=3, check_seqs=[0, 9, 19])
+
+
 @pytest.mark.parametrize("ctx,window,blen", [(17, 0, 0), (1500, 0, 0), (3000, 0, 0), (1500, 100, 0), (3000, 0, 5),
                                               (0, 0, 0)])
 def test_draft_block_single_sequence(ctx, window, blen):
