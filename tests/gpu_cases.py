@@ -69,6 +69,12 @@ MINI = {
     "mini_split": mini("mini_split", 110, dtype="bf16", hidden=256, n_q_heads=2, n_kv_heads=2, head_dim=128,
                        ffn=4096, vocab=8448, n_layers=2, n_feat_layers=2, block_size=16, batch=9,
                        ctx_min=3, ctx_max=120, rope_theta=1e6),
+    # 8 ragged sequences of up to 16384 positions: attention items of 256
+    # keys (4 K/V sub-blocks per item, the last item of a sequence partly
+    # empty), one layer
+    "mini_long": mini("mini_long", 111, dtype="bf16", hidden=256, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                      ffn=512, vocab=1040, n_layers=1, n_feat_layers=2, block_size=16, batch=8,
+                      ctx_min=2000, ctx_max=16384, rope_theta=1e6),
     "tiny": S.get_config("tiny"),
 }
 

@@ -248,7 +248,7 @@ def run_draft_case(cfg, seed=0, lens=None, check_seqs=None):
 
 
 @pytest.mark.parametrize("name", ["tiny", "mini_bf16", "mini_b10", "mini_d64", "mini_f32", "mini_b8", "mini_port",
-                                  "mini_wide", "mini_g8", "mini_big", "mini_split"])
+                                  "mini_wide", "mini_g8", "mini_big", "mini_split", "mini_long"])
 def test_draft_block(name):
     log(f"draft_block {name}")
     run_draft_case(MINI[name], seed=0)
