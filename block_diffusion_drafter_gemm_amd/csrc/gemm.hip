@@ -59,8 +59,7 @@ __device__ void gemm_epilogue(const GemmArgs &a, const float *ct, int MP, int ro
       const int r = i >> 3, c = i & 7, row = row0 + r;
       if (row >= a.M) continue;
       const float gt = ct[r * 16 + c], up = ct[r * 16 + 8 + c];
-      const float silu = gt / (1.0f + expf(-gt));
-      Storage<T>::store((T *)a.out, (size_t)row * a.ldo + t * 8 + c, silu * up);
+      Storage<T>::store((T *)a.out, (size_t)row * a.ldo + t * 8 + c, silu_mul(gt, up));
     }
   } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
     const int hd = a.hd, half = hd / 2;

@@ -109,7 +109,7 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
       const int r = tid >> 3, c = tid & 7;
       if (r < a.M) {
         const float gt = ct[r * 16 + c], up = ct[r * 16 + 8 + c];
-        Storage<T>::store((T *)a.out, (size_t)r * a.ldo + t * 8 + c, gt / (1.0f + expf(-gt)) * up);
+        Storage<T>::store((T *)a.out, (size_t)r * a.ldo + t * 8 + c, silu_mul(gt, up));
       }
     }
   } else if constexpr (qkv_epi(EPI) || EPI == EPI_INJECT) {

@@ -78,7 +78,7 @@ __device__ void t_epilogue(const GemmArgs &a, const float *ct, int rb, int cb, i
       const int r = i / 64, c = i % 64, row = row0 + r;
       if (row >= a.M) continue;
       const float gt = ct[r * kTCStride + c], up = ct[r * kTCStride + 64 + c];
-      Storage<T>::store((T *)a.out, (size_t)row * a.ldo + cb * 64 + c, gt / (1.0f + expf(-gt)) * up);
+      Storage<T>::store((T *)a.out, (size_t)row * a.ldo + cb * 64 + c, silu_mul(gt, up));
     }
   } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
     const int hd = a.hd, half = hd / 2;
@@ -309,8 +309,109 @@ __global__ __launch_bounds__(256) void gemm_splitk_resid_kernel(const GemmArgs a
 // Bank lines are 256 bytes: 64-byte rows XOR the 16-byte chunk index with
 // (row / 4) mod 4, 128-byte rows with (row / 2) mod 8, so the 16 consecutive
 // rows one quarter-wave reads land on 16 distinct bank groups.  The epilogue
-// runs on one 128-column half at a time through the LDS tile.
+// runs on one 128-column half at a time through the LDS tile, except the
+// argmax, which each wave reduces from its own accumulators (its 128 columns
+// are one 128-column block of the partials).
 constexpr int kBT = 256, kBK = 32;
+
+// (bv, bi) <- the larger of (bv, bi) and (ov, oi); equal values keep the lower
+// column.  Values are never NaN here (a NaN never enters: see below), so this is
+// a total order and any merge tree gives the same result as a scan in column
+// order with a strict comparison.
+__device__ __forceinline__ void amax_take(float &bv, int &bi, float ov, int oi) {
+  const bool t = (ov > bv) | ((ov == bv) & (oi < bi));   // selects, no branch
+  bv = t ? ov : bv;
+  bi = t ? oi : bi;
+}
+// Value of the partner lane (lane ^ PX inside the 32 lanes of a half-wave):
+// PX = 15, 7, 2, 1 by DPP lane moves inside 16-lane rows (row mirror, half-row
+// mirror, quad permutations), PX = 16 through the LDS crossbar.
+template <int PX> __device__ __forceinline__ int xchg(int x) {
+  if constexpr (PX == 16) return __shfl_xor(x, 16);
+  else if constexpr (PX == 15) return __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);
+  else if constexpr (PX == 7) return __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);
+  else if constexpr (PX == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
+  else return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);                        // [1,0,3,2]
+}
+template <int PX> __device__ __forceinline__ float xchg(float x) {
+  return __builtin_bit_cast(float, xchg<PX>(__builtin_bit_cast(int, x)));
+}
+// One exchange round over N row slots with the partner lane ^ PX: the lane
+// whose bit HB is set keeps the upper half and hands the lower half over, its
+// partner (bit HB clear) the reverse; each merges what it keeps with what it
+// receives.  Partners must hold the same slots, so PX may flip only lane bits
+// that no earlier round split on.
+template <int N, int PX, int HB>
+__device__ __forceinline__ void amax_round(float (&bv)[64], int (&bi)[64], int lane) {
+  constexpr int H = N / 2;
+  const bool hi = ((lane >> HB) & 1) != 0;
+  float rv[H];
+  int ri[H];
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    rv[k] = hi ? bv[k] : bv[k + H];
+    ri[k] = hi ? bi[k] : bi[k + H];
+  }
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    rv[k] = xchg<PX>(rv[k]);
+    ri[k] = xchg<PX>(ri[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < H; ++k) {
+    float kv = hi ? bv[k + H] : bv[k];
+    int ki = hi ? bi[k + H] : bi[k];
+    amax_take(kv, ki, rv[k], ri[k]);
+    bv[k] = kv;
+    bi[k] = ki;
+  }
+}
+// Per-row (max, lowest column) of one wave's 128 x 128 quadrant, straight from
+// its accumulators (rows row0 .., 128-column block blk of the argmax partials).
+// Lane (fr, fk) holds columns 32j + fr of rows 32i + 8(e/4) + 4fk + e%4: it
+// first scans its four columns of each of its 64 rows in column order (a NaN
+// never wins; a row with no number above -inf keeps column 0), then five
+// exchange rounds over the 32 lanes of its half-wave (partners lane ^ 15, ^ 7,
+// ^ 2, ^ 1, ^ 16; upper halves kept by lanes with bit 3, 2, 1, 0, 4 set) leave
+// it with row slots 2 * (16 b3 + 8 b2 + 4 b1 + 2 b0 + b4) + {0, 1} of the 64
+// (b = bits of fr), reduced over all 128 columns.
+__device__ __forceinline__ void quadrant_argmax(const GemmArgs &a, const f32x16 (&acc)[4][4], int row0, int blk,
+                                                int lane) {
+  const int fr = lane & 31, fk = lane >> 5;
+  float bv[64];
+  int bi[64];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float b = -INFINITY;
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool t = acc[i][j][e] > b;
+        b = t ? acc[i][j][e] : b;
+        c = t ? 32 * j + fr : c;
+      }
+      bv[16 * i + e] = b;
+      bi[16 * i + e] = c;
+    }
+  amax_round<64, 15, 3>(bv, bi, lane);
+  amax_round<32, 7, 2>(bv, bi, lane);
+  amax_round<16, 2, 1>(bv, bi, lane);
+  amax_round<8, 1, 0>(bv, bi, lane);
+  amax_round<4, 16, 4>(bv, bi, lane);
+  const int s0 = 2 * (16 * ((fr >> 3) & 1) + 8 * ((fr >> 2) & 1) + 4 * ((fr >> 1) & 1) + 2 * (fr & 1) + (fr >> 4));
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int s = s0 + k, i = s >> 4, e = s & 15;
+    const int row = row0 + 32 * i + 8 * (e >> 2) + 4 * fk + (e & 3);
+    if (row < a.M) {
+      a.amax_val[(size_t)row * a.n_groups + blk] = bv[k];
+      a.amax_idx[(size_t)row * a.n_groups + blk] = blk * kTBN + bi[k];
+    }
+  }
+}
+
 constexpr int kBAStage = kBT * 64, kBAStages = 4;              // activation ring
 constexpr int kBWStage = kBT * 128, kBWStages = 3;             // weight ring (two k-steps per stage)
 constexpr int kBWBase = kBAStages * kBAStage;
@@ -441,6 +542,12 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const GemmArgs a, int n_r
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
+  if constexpr (EPI == EPI_ARGMAX) {
+    // a wave's 128 columns are exactly one 128-column block of the partials
+    const int blk = 2 * ct_ + wc;
+    if (blk < n_cb) quadrant_argmax(a, acc, row0 + wr * 128, blk, lane);
+    return;
+  }
   float *ctile = reinterpret_cast<float *>(lds);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -472,12 +579,14 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const GemmArgs a, int n_r
 // a stage per step).  The smaller weight stages leave room for a fourth one,
 // so weight halves are requested 7 steps ahead instead of 5 (the weights come
 // from HBM; the loop waits on them, not on the matrix cores).  K is walked in the same order as the 256 x 256 kernel,
-// so both give identical sums.  Epilogue: the up waves (wc = 1) hand their
-// accumulators to the gate waves through LDS, which write silu(gate) * up.
+// so both give identical sums.  Epilogue: gate and up values pass through LDS
+// one 128-row half at a time, and all four waves write silu(gate) * up in
+// 16-byte pieces.
 constexpr int kB3N = 192, kB3WStage = kB3N * 128, kB3WStages = 4;
 constexpr int kB3WBase = kBAStages * kBAStage;
 constexpr int kB3Lds = kB3WBase + kB3WStages * kB3WStage;   // 160 KB
-static_assert(2 * 128 * 96 * 4 <= kB3Lds, "up-value exchange fits");
+constexpr int kB3Row = 100;                                  // floats per epilogue row (96 + 4)
+static_assert(2 * 128 * kB3Row * 4 <= kB3Lds, "gate and up values of 128 rows fit");
 
 __global__ __launch_bounds__(256) void gemm_swiglu192_kernel(const GemmArgs a, int n_rb, int n_ct, int per_xcd) {
   using T = bf16_t;
@@ -594,31 +703,38 @@ __global__ __launch_bounds__(256) void gemm_swiglu192_kernel(const GemmArgs a, i
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
-  // up waves hand their values to the gate waves: [wr][128 rows][96 columns] fp32
-  float *up = reinterpret_cast<float *>(lds) + wr * 128 * 96;
-  if (wc == 1) {
+  // Two passes over the row halves: in pass p the two waves with wr == p put
+  // their gate (wc = 0) and up (wc = 1) values in LDS ([128 rows][kB3Row]
+  // fp32 each), then all four waves write silu(gate) * up for those 128 rows,
+  // 8 columns (16 bytes) per store.
+  float *gl = reinterpret_cast<float *>(lds), *ul = gl + 128 * kB3Row;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int p = 0; p < 2; ++p) {
+    if (wr == p) {
+      float *dst = wc ? ul : gl;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) up[(i * 32 + 8 * (e / 4) + 4 * fk + e % 4) * 96 + j * 32 + fr] = acc[i][j][e];
-  }
-  __syncthreads();
-  if (wc == 0) {
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int rl = i * 32 + 8 * (e / 4) + 4 * fk + e % 4, row = row0 + wr * 128 + rl;
-        if (row < a.M) {
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const float gt = acc[i][j][e], u = up[rl * 96 + j * 32 + fr];
-            Storage<T>::store((T *)a.out, (size_t)row * a.ldo + ct_ * 96 + j * 32 + fr, gt / (1.0f + expf(-gt)) * u);
-          }
-        }
+          for (int e = 0; e < 16; ++e) dst[(i * 32 + 8 * (e / 4) + 4 * fk + e % 4) * kB3Row + j * 32 + fr] = acc[i][j][e];
+    }
+    __syncthreads();
+    for (int q = tid; q < 128 * 12; q += 256) {
+      const int rl = q / 12, c8 = (q % 12) * 8, row = row0 + p * 128 + rl;
+      if (row < a.M) {
+        const float4 g0 = *reinterpret_cast<const float4 *>(gl + rl * kB3Row + c8);
+        const float4 g1 = *reinterpret_cast<const float4 *>(gl + rl * kB3Row + c8 + 4);
+        const float4 u0 = *reinterpret_cast<const float4 *>(ul + rl * kB3Row + c8);
+        const float4 u1 = *reinterpret_cast<const float4 *>(ul + rl * kB3Row + c8 + 4);
+        const float f[8] = {silu_mul(g0.x, u0.x), silu_mul(g0.y, u0.y), silu_mul(g0.z, u0.z), silu_mul(g0.w, u0.w),
+                            silu_mul(g1.x, u1.x), silu_mul(g1.y, u1.y), silu_mul(g1.z, u1.z), silu_mul(g1.w, u1.w)};
+        Frag<T> o;
+        o.set(f);
+        o.store((T *)a.out + (size_t)row * a.ldo + ct_ * 96 + c8);
       }
+    }
+    __syncthreads();
   }
 }
 
@@ -697,8 +813,10 @@ hipError_t launch_gemm_tiled(Epilogue epi, GemmArgs &a, int z_slices, int cu, hi
   const long big_tiles = (long)((a.M + kBT - 1) / kBT) * ((a.n_groups + 1) / 2) * z_slices;
   if (a.M > 128 && big_tiles >= kBigMinTiles) {
     // gate/up: 256 x 192 tiles where they fill the compute units' rounds
-    // better than 256 x 256 (e.g. 512 rows of FFN 12288: 256 tiles against 192)
-    if (epi == EPI_SWIGLU && a.ffn % 96 == 0 && a.K % (2 * kBK) == 0) {
+    // better than 256 x 256 (e.g. 512 rows of FFN 12288: 256 tiles against 192);
+    // its epilogue stores 8 outputs (16 bytes) at a time
+    if (epi == EPI_SWIGLU && a.ffn % 96 == 0 && a.K % (2 * kBK) == 0 && a.ldo % 8 == 0 &&
+        reinterpret_cast<uintptr_t>(a.out) % 16 == 0) {
       const int n_rb = (a.M + kBT - 1) / kBT, n_ct3 = a.ffn / 96;
       const long t3 = (long)n_rb * n_ct3 * z_slices;
       const double fill3 = (double)t3 / (double)(((t3 + cu - 1) / cu) * cu);

@@ -98,6 +98,38 @@ def test_lmhead_argmax(name, rows):
     dr.close()
 
 
+@pytest.mark.parametrize("rows", [150, 300])
+def test_lmhead_argmax_ties_inside_one_block(rows):
+    """Exact ties inside one 128-column block of the 256 x 256-tile LM head:
+    five copies of one vocabulary row at ids in different lanes and column
+    tiles of block 3 (ids 384 + {70, 5, 100, 38, 6}); rows in both 128-row
+    halves of both row blocks point at it, so the winner is decided by the
+    per-row reduction inside the block, and it must be the lowest id, 389."""
+    cfg = MINI["mini_big"]
+    log(f"lmhead_argmax in-block ties mini_big rows={rows}")
+    R = runtime()
+    w = S.drafter_weights(cfg, seed=5)
+    base = 3 * 128
+    src = base + 70
+    for c in (5, 100, 38, 6):
+        w["lm_head"][base + c] = w["lm_head"][src]
+    z = S.normal_matrix(cfg, 79, (rows, cfg.hidden), 1.0, seed=rows)
+    tie_rows = [r for r in (0, 5, 37, 127, 128, 131, 200, 255, 256, 290, 299) if r < rows]
+    for r in tie_rows:
+        z[r] = storage_of(cfg, round_storage(from_storage(w["lm_head"][src]) * (40.0 + r % 7), cfg.dtype))
+    dr = R.Drafter(cfg, w, max_batch=(rows + cfg.block_size - 2) // (cfg.block_size - 1), max_ctx=16, max_new=1)
+    ids, mx, lg = dr.lmhead_argmax(R.to_device(z), want_max=True, want_logits=True)
+    torch.cuda.synchronize()
+    ids_o, best_o, logits_o = D.lm_argmax(w["lm_head"], z)
+    g = ids.cpu().numpy()
+    for r in tie_rows:
+        assert ids_o[r] == base + 5, (r, ids_o[r])
+        assert g[r] == base + 5, (r, g[r])
+    assert_close(mx.cpu().numpy(), best_o, 1e-4, "max logit")
+    check_ids(g, ids_o, logits_o, 1e-4, "ids")
+    dr.close()
+
+
 @pytest.mark.parametrize("name,rows", [("mini_bf16", 15), ("mini_bf16", 31), ("mini_b8", 130), ("mini_f32", 40),
                                        ("mini_big", 300)])
 def test_lmhead_argmax_nan_logits(name, rows):
