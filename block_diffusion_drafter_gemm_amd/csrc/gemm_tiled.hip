@@ -49,6 +49,7 @@ template <int BM> struct TCfg {
   static constexpr int per_wave = pieces / waves;        // ... per wave
   static constexpr int lds = kTStages * stage > BM * kTCStride * 4 ? kTStages * stage : BM * kTCStride * 4;
   static_assert(pieces % waves == 0, "stage pieces split evenly over the waves");
+  static_assert(lds >= BM * kTCStride * 4 + BM * 12, "epilogue row metadata fits past the fp32 tile");
 };
 
 template <int EPI>
@@ -84,43 +85,60 @@ __device__ void t_epilogue(const GemmArgs &a, const float *ct, int rb, int cb, i
     const int hd = a.hd, half = hd / 2;
     const int qcols = (EPI == EPI_QKV) ? a.nq * hd : 0;
     const int kcols = a.nkv * hd;
-    // one thread per (row, rotation pair); pairs are (c, c + d/2) inside each head
-    for (int i = tid; i < BM * 64; i += NT) {
-      const int r = i / 64, p = i % 64, row = row0 + r;
-      if (row >= a.M) continue;
-      const int c = (p / half) * hd + (p % half);     // lower element of the pair in the block
-      const int n = cb * kTBN + c;
-      const float x1 = ct[r * kTCStride + c], x2 = ct[r * kTCStride + c + half];
-      int pos;
-      size_t slot = 0;
+    // Row metadata first, once per row, into LDS past the fp32 tile: the
+    // position, and for the paged cache the row's slot (its page from the
+    // block table).  Reading these per element put two or three dependent
+    // global loads in every iteration of the loop below.
+    int *mpos = reinterpret_cast<int *>(const_cast<float *>(ct) + BM * kTCStride);
+    size_t *mslot = reinterpret_cast<size_t *>(mpos + BM);
+    for (int r = tid; r < BM; r += NT) {
+      const int row = min(row0 + r, a.M - 1);
       if constexpr (EPI == EPI_QKV) {
-        const int s = row / a.block_size, j = row - s * a.block_size;
-        pos = a.ctx_len[s] + j;
+        const int s = row / a.block_size;
+        mpos[r] = a.ctx_len[s] + (row - s * a.block_size);
+        mslot[r] = 0;
       } else {
-        pos = a.pos[row];
-        const int s = a.seq[row];
+        const int pos = a.pos[row], s = a.seq[row];
         const int page = a.block_table[(size_t)s * a.max_pages + pos / a.page_size];
-        slot = (size_t)layer * a.cache_layer_stride + ((size_t)page * a.page_size + (pos % a.page_size)) * kcols;
+        mpos[r] = pos;
+        mslot[r] = (size_t)layer * a.cache_layer_stride + ((size_t)page * a.page_size + (pos % a.page_size)) * kcols;
       }
+    }
+    __syncthreads();
+    // one thread per (row, rotation pair); pairs are (c, c + d/2) inside each
+    // head.  NT is a multiple of 64, so a thread's pair index p, and with it
+    // the pair's frequency, is the same in every iteration.
+    static_assert(NT % 64 == 0, "fixed pair index per thread");
+    const int p = tid % 64;
+    const int c = (p / half) * hd + (p % half);        // lower element of the pair in the block
+    const int n = cb * kTBN + c;
+    const bool rot = n < qcols + kcols;
+    const double inv_freq = rope_inv_freq(p % half, hd, a.log2_theta);
+    T *dst;
+    size_t coff;
+    if (n < qcols) {
+      dst = (T *)a.q_out;
+      coff = n;
+    } else if (n < qcols + kcols) {
+      dst = (T *)a.k_out;
+      coff = n - qcols;
+    } else {
+      dst = (T *)a.v_out;
+      coff = n - qcols - kcols;
+    }
+    const size_t rstride = (EPI == EPI_QKV) ? (size_t)(n < qcols ? qcols : kcols) : 0;
+    for (int r = tid / 64; r < BM; r += NT / 64) {
+      const int row = row0 + r;
+      if (row >= a.M) break;
+      const float x1 = ct[r * kTCStride + c], x2 = ct[r * kTCStride + c + half];
       float lo = x1, hi = x2;
-      if (n < qcols + kcols) {
+      if (rot) {
         float cs, sn;
-        rope_cs_inv(pos, rope_inv_freq(p % half, hd, a.log2_theta), &cs, &sn);
+        rope_cs_inv(mpos[r], inv_freq, &cs, &sn);
         lo = x1 * cs - x2 * sn;
         hi = x2 * cs + x1 * sn;
       }
-      T *dst;
-      size_t off;
-      if (n < qcols) {
-        dst = (T *)a.q_out;
-        off = (size_t)row * qcols + n;
-      } else if (n < qcols + kcols) {
-        dst = (T *)a.k_out;
-        off = (EPI == EPI_QKV ? (size_t)row * kcols : slot) + (n - qcols);
-      } else {
-        dst = (T *)a.v_out;
-        off = (EPI == EPI_QKV ? (size_t)row * kcols : slot) + (n - qcols - kcols);
-      }
+      const size_t off = (EPI == EPI_QKV ? (size_t)row * rstride : mslot[r]) + coff;
       Storage<T>::store(dst, off, lo);
       Storage<T>::store(dst, off + half, hi);
     }
@@ -417,6 +435,7 @@ constexpr int kBWStage = kBT * 128, kBWStages = 3;             // weight ring (t
 constexpr int kBWBase = kBAStages * kBAStage;
 constexpr int kBLdsStaging = kBWBase + kBWStages * kBWStage;   // 160 KB
 constexpr int kBLds = kBLdsStaging > kBT * kTCStride * 4 ? kBLdsStaging : kBT * kTCStride * 4;
+static_assert(kBLds >= kBT * kTCStride * 4 + kBT * 12, "epilogue row metadata fits past the fp32 tile");
 
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_big_kernel(const GemmArgs a, int n_rb, int n_ct, int per_xcd) {
