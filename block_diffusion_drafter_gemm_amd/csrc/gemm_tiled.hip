@@ -849,9 +849,13 @@ hipError_t launch_gemm_tiled(Epilogue epi, GemmArgs &a, int z_slices, int cu, hi
     }
     return launch_big(epi, a, z_slices, st);
   }
+  // 256 x 128 tiles (half the staged bytes per flop of 128 x 128) when their
+  // rounds of the compute units take no longer, counted in 128 x 128 tiles
+  // (e.g. 2048 x 4096: 256 tiles, one round, against 512 in two)
   const long tiles256 = (long)((a.M + 255) / 256) * a.n_groups * z_slices;
-  if (tiles256 >= 512) return launch_tiled_bm<256>(epi, a, z_slices, 1, st);
   const long tiles = (long)((a.M + 127) / 128) * a.n_groups * z_slices;
+  if (tiles256 >= cu && 2 * ((tiles256 + cu - 1) / cu) <= (tiles + cu - 1) / cu)
+    return launch_tiled_bm<256>(epi, a, z_slices, 1, st);
   int splits = 1;
   if (a.part && z_slices == 1 && epi == EPI_RESID) {
     while (splits < 4 && tiles * splits * 2 <= cu && a.K % (splits * 2 * kTBK) == 0 && a.K / (splits * 2) >= 1024 &&
