@@ -215,6 +215,8 @@ int validate_config(const dflash_config *c) {
 int validate_kv(const dflash_handle_s *h, const dflash_kv *kv) {
   if (!kv) return DFLASH_ERR_NULL;
   if (!kv->k || !kv->v || !kv->block_table || !kv->ctx_len) return DFLASH_ERR_NULL;
+  // cache rows are read and written in 16-byte pieces
+  if (reinterpret_cast<uintptr_t>(kv->k) % 16 || reinterpret_cast<uintptr_t>(kv->v) % 16) return DFLASH_ERR_RANGE;
   if (kv->batch < 1 || kv->max_pages < 1 || kv->n_pages < 1 || kv->max_ctx < 0) return DFLASH_ERR_SHAPE;
   (void)h;
   return DFLASH_OK;

@@ -58,9 +58,43 @@ __device__ __forceinline__ int t_weight_row(const GemmArgs &a, int cb, int c) {
   return cb * kTBN + c;
 }
 
-// Epilogue of a BM x 128 fp32 tile in LDS (row stride kTCStride), run by NT threads.
+// Per-row metadata of the RoPE epilogues, one row per thread (threads past BM
+// hold nothing): the row's position and, for the paged cache, its slot (page
+// from the block table).  Loaded at kernel start, so that the dependent
+// position -> page lookup is hidden behind the k-loop.
+struct RowMeta {
+  int pos;
+  size_t slot;
+};
+template <int EPI, int BM>
+__device__ __forceinline__ RowMeta load_row_meta(const GemmArgs &a, int row0, int layer) {
+  RowMeta m{0, 0};
+  if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
+    const int tid = threadIdx.x;
+    if (tid < BM) {
+      const int row = min(row0 + tid, a.M - 1);
+      if constexpr (EPI == EPI_QKV) {
+        const int s = row / a.block_size;
+        m.pos = a.ctx_len[s] + (row - s * a.block_size);
+      } else {
+        const int pos = a.pos[row], s = a.seq[row];
+        const int page = a.block_table[(size_t)s * a.max_pages + pos / a.page_size];
+        m.pos = pos;
+        m.slot = (size_t)layer * a.cache_layer_stride +
+                 ((size_t)page * a.page_size + (pos % a.page_size)) * (size_t)(a.nkv * a.hd);
+      }
+    }
+  }
+  return m;
+}
+
+// Epilogue of a BM x 128 fp32 tile in LDS (row stride kTCStride), run by NT
+// threads.  `meta` is this thread's row metadata (RoPE epilogues); `first` is
+// false on the second 128-column half of the same rows, whose metadata is
+// already in LDS.
 template <int EPI, int BM, int NT>
-__device__ void t_epilogue(const GemmArgs &a, const float *ct, int rb, int cb, int layer) {
+__device__ void t_epilogue(const GemmArgs &a, const float *ct, int rb, int cb, int layer, const RowMeta &meta,
+                           bool first) {
   using T = bf16_t;
   const int tid = threadIdx.x;
   const int row0 = rb * BM;
@@ -85,62 +119,68 @@ __device__ void t_epilogue(const GemmArgs &a, const float *ct, int rb, int cb, i
     const int hd = a.hd, half = hd / 2;
     const int qcols = (EPI == EPI_QKV) ? a.nq * hd : 0;
     const int kcols = a.nkv * hd;
-    // Row metadata first, once per row, into LDS past the fp32 tile: the
-    // position, and for the paged cache the row's slot (its page from the
-    // block table).  Reading these per element put two or three dependent
-    // global loads in every iteration of the loop below.
+    // row metadata into LDS past the fp32 tile, once per tile
     int *mpos = reinterpret_cast<int *>(const_cast<float *>(ct) + BM * kTCStride);
     size_t *mslot = reinterpret_cast<size_t *>(mpos + BM);
-    for (int r = tid; r < BM; r += NT) {
-      const int row = min(row0 + r, a.M - 1);
-      if constexpr (EPI == EPI_QKV) {
-        const int s = row / a.block_size;
-        mpos[r] = a.ctx_len[s] + (row - s * a.block_size);
-        mslot[r] = 0;
-      } else {
-        const int pos = a.pos[row], s = a.seq[row];
-        const int page = a.block_table[(size_t)s * a.max_pages + pos / a.page_size];
-        mpos[r] = pos;
-        mslot[r] = (size_t)layer * a.cache_layer_stride + ((size_t)page * a.page_size + (pos % a.page_size)) * kcols;
+    if (first) {
+      if (tid < BM) {
+        mpos[tid] = meta.pos;
+        mslot[tid] = meta.slot;
       }
+      __syncthreads();
     }
-    __syncthreads();
-    // one thread per (row, rotation pair); pairs are (c, c + d/2) inside each
-    // head.  NT is a multiple of 64, so a thread's pair index p, and with it
-    // the pair's frequency, is the same in every iteration.
-    static_assert(NT % 64 == 0, "fixed pair index per thread");
-    const int p = tid % 64;
-    const int c = (p / half) * hd + (p % half);        // lower element of the pair in the block
-    const int n = cb * kTBN + c;
+    // One thread per (row, 8 consecutive rotation pairs): pairs are (c, c + d/2)
+    // inside each head, so the thread reads 8 consecutive lower and 8 upper
+    // elements and writes each group as one 16-byte piece.  NT is a multiple
+    // of 8, so a thread's pairs, and their frequencies, are fixed.
+    static_assert(NT % 8 == 0, "fixed pair group per thread");
+    const int q = tid % 8, p0 = 8 * q;                   // pairs p0 .. p0 + 7 of the block's 64
+    const int c0 = (p0 / half) * hd + (p0 % half);       // lower element of pair p0 (half % 8 == 0)
+    const int n = cb * kTBN + c0;
     const bool rot = n < qcols + kcols;
-    const double inv_freq = rope_inv_freq(p % half, hd, a.log2_theta);
+    double inv_freq[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) inv_freq[k] = rope_inv_freq((p0 + k) % half, hd, a.log2_theta);
     T *dst;
-    size_t coff;
+    size_t coff, rstride = 0;
     if (n < qcols) {
       dst = (T *)a.q_out;
       coff = n;
+      rstride = qcols;
     } else if (n < qcols + kcols) {
       dst = (T *)a.k_out;
       coff = n - qcols;
+      rstride = kcols;
     } else {
       dst = (T *)a.v_out;
       coff = n - qcols - kcols;
+      rstride = kcols;
     }
-    const size_t rstride = (EPI == EPI_QKV) ? (size_t)(n < qcols ? qcols : kcols) : 0;
-    for (int r = tid / 64; r < BM; r += NT / 64) {
+    for (int r = tid / 8; r < BM; r += NT / 8) {
       const int row = row0 + r;
       if (row >= a.M) break;
-      const float x1 = ct[r * kTCStride + c], x2 = ct[r * kTCStride + c + half];
-      float lo = x1, hi = x2;
+      const float *lp = ct + r * kTCStride + c0, *hp = lp + half;
+      const float4 l0 = *reinterpret_cast<const float4 *>(lp), l1 = *reinterpret_cast<const float4 *>(lp + 4);
+      const float4 h0 = *reinterpret_cast<const float4 *>(hp), h1 = *reinterpret_cast<const float4 *>(hp + 4);
+      float lo[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+      float hi[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
       if (rot) {
-        float cs, sn;
-        rope_cs_inv(mpos[r], inv_freq, &cs, &sn);
-        lo = x1 * cs - x2 * sn;
-        hi = x2 * cs + x1 * sn;
+        const int pos = mpos[r];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          float cs, sn;
+          rope_cs_inv(pos, inv_freq[k], &cs, &sn);
+          const float x1 = lo[k], x2 = hi[k];
+          lo[k] = x1 * cs - x2 * sn;
+          hi[k] = x2 * cs + x1 * sn;
+        }
       }
       const size_t off = (EPI == EPI_QKV ? (size_t)row * rstride : mslot[r]) + coff;
-      Storage<T>::store(dst, off, lo);
-      Storage<T>::store(dst, off + half, hi);
+      Frag<T> fl, fh;
+      fl.set(lo);
+      fh.set(hi);
+      fl.store(dst + off);
+      fh.store(dst + off + half);
     }
   } else if constexpr (EPI == EPI_ARGMAX) {
     // 2 threads per row, 64 columns each; lowest column on ties (a NaN never
@@ -183,6 +223,7 @@ __global__ __launch_bounds__(TCfg<BM>::threads) void gemm_tiled_kernel(const Gem
   const T *W = (const T *)a.W[layer];
   const int row0 = rb * BM;
   const int kz = blockIdx.z, kbase = kz * a.kper;        // split-K: this workgroup's K range
+  const RowMeta meta = load_row_meta<EPI, BM>(a, row0, layer);
 
   // LDS-direct staging: piece q of a stage covers staged rows 8q .. 8q+7
   // (A rows first, then W rows); this lane fills row 8q + lane/8, slot lane%8
@@ -270,7 +311,7 @@ __global__ __launch_bounds__(TCfg<BM>::threads) void gemm_tiled_kernel(const Gem
     }
     return;
   }
-  t_epilogue<EPI, BM, C::threads>(a, ct, rb, cb, layer);
+  t_epilogue<EPI, BM, C::threads>(a, ct, rb, cb, layer, meta, true);
 }
 
 // Split-K reduction of a residual projection: X += p_0 + p_1 + ... (summed in
@@ -450,6 +491,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const GemmArgs a, int n_r
   const T *A = (const T *)a.A;
   const T *W = (const T *)a.W[layer];
   const int row0 = rb * kBT;
+  const RowMeta meta = load_row_meta<EPI, kBT>(a, row0, layer);
 
   // Activation piece i of a stage (this wave's 4 of 16): rows 16q .. 16q+15,
   // q = 4*wave + i; this lane fills row 16q + lane/4, 16-byte slot lane%4.
@@ -582,7 +624,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const GemmArgs a, int n_r
             ctile[(wr * 128 + i * 32 + 8 * (e / 4) + 4 * fk + e % 4) * kTCStride + j * 32 + fr] = acc[i][j][e];
     }
     __syncthreads();
-    t_epilogue<EPI, kBT, 256>(a, ctile, rb, blk, layer);
+    t_epilogue<EPI, kBT, 256>(a, ctile, rb, blk, layer, meta, h == 0);
     __syncthreads();
   }
 }
@@ -783,7 +825,7 @@ int gemm_tiled_cols(Epilogue epi, int N, int ffn) { return epi == EPI_SWIGLU ? f
 bool gemm_tiled_ok(Epilogue epi, int N, int K, int ffn, int hd) {
   if (K % kTBK) return false;
   if (epi == EPI_SWIGLU) return ffn % 64 == 0;
-  if ((epi == EPI_QKV || epi == EPI_INJECT) && kTBN % hd) return false;
+  if ((epi == EPI_QKV || epi == EPI_INJECT) && (kTBN % hd || hd % 16)) return false;   // 8-pair groups
   return N % kTBN == 0;
 }
 

@@ -120,8 +120,9 @@ typedef struct {
  * t/page_size], slot t % page_size.  The anchor of sequence s sits at position
  * ctx_len[s]; positions 0..ctx_len[s]-1 are the context. */
 typedef struct {
-    void *k;                        /* [n_layers][n_pages][page_size][n_kv_heads][head_dim] */
-    void *v;                        /* same layout as k */
+    void *k;                        /* [n_layers][n_pages][page_size][n_kv_heads][head_dim],
+                                       16-byte aligned (DFLASH_ERR_RANGE otherwise) */
+    void *v;                        /* same layout and alignment as k */
     const int32_t *block_table;     /* device [batch][max_pages] */
     const int32_t *ctx_len;         /* device [batch] */
     int32_t batch;

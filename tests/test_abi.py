@@ -195,6 +195,22 @@ def test_check_inputs_host_validation(lib):
         assert lib.dflash_destroy(h) == 0
 
 
+def test_kv_cache_must_be_16_byte_aligned(lib):
+    """Cache rows are read and written in 16-byte pieces: a K or V base that is
+    not 16-byte aligned is refused (DFLASH_ERR_RANGE) before anything runs."""
+    st, h = create(good_config())
+    assert st == 0 and h
+    try:
+        n1 = L.dflash_workspace_size(h, 1, 64, 16)
+        for k, v in ((FAKE + 8, FAKE), (FAKE, FAKE + 2)):
+            kv = L.DflashKV(k, v, FAKE, FAKE, 1, 8, 8, 64)
+            assert lib.dflash_inject_context(h, FAKE, FAKE, FAKE, 4, ctypes.byref(kv), FAKE, n1, None) == -4
+            assert lib.dflash_draft_block(h, FAKE, ctypes.byref(kv), FAKE, FAKE, n1, None) == -4
+            assert lib.dflash_check_inputs(h, ctypes.byref(kv), None, None, 0, None, None, 0, FAKE, None) == -4
+    finally:
+        assert lib.dflash_destroy(h) == 0
+
+
 def test_workspace_size_and_host_validation(lib):
     st, h = create(good_config())
     assert st == 0 and h
