@@ -99,21 +99,71 @@ __device__ void t_epilogue(const GemmArgs &a, const float *ct, int rb, int cb, i
   const int tid = threadIdx.x;
   const int row0 = rb * BM;
   if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_F32 || EPI == EPI_RESID) {
-    for (int i = tid; i < BM * kTBN; i += NT) {
-      const int r = i / kTBN, c = i % kTBN, row = row0 + r;
-      if (row >= a.M) continue;
-      const int n = cb * kTBN + c;
-      const float v = ct[r * kTCStride + c];
-      if constexpr (EPI == EPI_STORE) Storage<T>::store((T *)a.out, (size_t)row * a.ldo + n, v);
-      else if constexpr (EPI == EPI_STORE_F32) ((float *)a.out)[(size_t)row * a.ldo + n] = v;
-      else a.X[(size_t)row * a.ldx + n] += v;
+    // 8 consecutive columns per thread and iteration, moved as 16-byte pieces
+    // when the output rows allow it (row stride and base aligned), else one
+    // element at a time
+    const bool vec = EPI == EPI_RESID ? (a.ldx % 4 == 0 && reinterpret_cast<uintptr_t>(a.X) % 16 == 0)
+                                      : (a.ldo % (EPI == EPI_STORE ? 8 : 4) == 0 &&
+                                         reinterpret_cast<uintptr_t>(a.out) % 16 == 0);
+    if (vec) {
+      for (int i = tid; i < BM * (kTBN / 8); i += NT) {
+        const int r = i / (kTBN / 8), c = (i % (kTBN / 8)) * 8, row = row0 + r;
+        if (row >= a.M) break;
+        const int n = cb * kTBN + c;
+        const float4 v0 = *reinterpret_cast<const float4 *>(ct + r * kTCStride + c);
+        const float4 v1 = *reinterpret_cast<const float4 *>(ct + r * kTCStride + c + 4);
+        if constexpr (EPI == EPI_STORE) {
+          const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+          Frag<T> o;
+          o.set(f);
+          o.store((T *)a.out + (size_t)row * a.ldo + n);
+        } else if constexpr (EPI == EPI_STORE_F32) {
+          float4 *o = reinterpret_cast<float4 *>((float *)a.out + (size_t)row * a.ldo + n);
+          o[0] = v0;
+          o[1] = v1;
+        } else {
+          float4 *x = reinterpret_cast<float4 *>(a.X + (size_t)row * a.ldx + n);
+          float4 x0 = x[0], x1 = x[1];
+          x0.x += v0.x; x0.y += v0.y; x0.z += v0.z; x0.w += v0.w;
+          x1.x += v1.x; x1.y += v1.y; x1.z += v1.z; x1.w += v1.w;
+          x[0] = x0;
+          x[1] = x1;
+        }
+      }
+    } else {
+      for (int i = tid; i < BM * kTBN; i += NT) {
+        const int r = i / kTBN, c = i % kTBN, row = row0 + r;
+        if (row >= a.M) continue;
+        const int n = cb * kTBN + c;
+        const float v = ct[r * kTCStride + c];
+        if constexpr (EPI == EPI_STORE) Storage<T>::store((T *)a.out, (size_t)row * a.ldo + n, v);
+        else if constexpr (EPI == EPI_STORE_F32) ((float *)a.out)[(size_t)row * a.ldo + n] = v;
+        else a.X[(size_t)row * a.ldx + n] += v;
+      }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    for (int i = tid; i < BM * 64; i += NT) {
-      const int r = i / 64, c = i % 64, row = row0 + r;
-      if (row >= a.M) continue;
-      const float gt = ct[r * kTCStride + c], up = ct[r * kTCStride + 64 + c];
-      Storage<T>::store((T *)a.out, (size_t)row * a.ldo + cb * 64 + c, silu_mul(gt, up));
+    const bool vec = a.ldo % 8 == 0 && reinterpret_cast<uintptr_t>(a.out) % 16 == 0;
+    if (vec) {
+      // gate columns 0..63 of the block, their up columns 64..127: 8 outputs per thread
+      for (int i = tid; i < BM * 8; i += NT) {
+        const int r = i / 8, c = (i % 8) * 8, row = row0 + r;
+        if (row >= a.M) break;
+        const float *g = ct + r * kTCStride + c, *u = g + 64;
+        const float4 g0 = *reinterpret_cast<const float4 *>(g), g1 = *reinterpret_cast<const float4 *>(g + 4);
+        const float4 u0 = *reinterpret_cast<const float4 *>(u), u1 = *reinterpret_cast<const float4 *>(u + 4);
+        const float f[8] = {silu_mul(g0.x, u0.x), silu_mul(g0.y, u0.y), silu_mul(g0.z, u0.z), silu_mul(g0.w, u0.w),
+                            silu_mul(g1.x, u1.x), silu_mul(g1.y, u1.y), silu_mul(g1.z, u1.z), silu_mul(g1.w, u1.w)};
+        Frag<T> o;
+        o.set(f);
+        o.store((T *)a.out + (size_t)row * a.ldo + cb * 64 + c);
+      }
+    } else {
+      for (int i = tid; i < BM * 64; i += NT) {
+        const int r = i / 64, c = i % 64, row = row0 + r;
+        if (row >= a.M) continue;
+        const float gt = ct[r * kTCStride + c], up = ct[r * kTCStride + 64 + c];
+        Storage<T>::store((T *)a.out, (size_t)row * a.ldo + cb * 64 + c, silu_mul(gt, up));
+      }
     }
   } else if constexpr (EPI == EPI_QKV || EPI == EPI_INJECT) {
     const int hd = a.hd, half = hd / 2;

@@ -130,6 +130,33 @@ def test_lmhead_argmax_ties_inside_one_block(rows):
     dr.close()
 
 
+@pytest.mark.parametrize("name,rows", [("mini_b8", 130), ("mini_big", 300)])
+def test_lmhead_logits_into_an_unaligned_buffer(name, rows):
+    """fp32 logits of the LDS-tiled (130 rows) and 256 x 256-tile (300 rows)
+    LM head written into a buffer that starts 4 bytes past a 16-byte boundary:
+    the epilogue then stores one element at a time instead of 16-byte pieces,
+    with the same values and ids as into an aligned buffer."""
+    cfg = MINI[name]
+    log(f"lmhead logits into an unaligned buffer {name} rows={rows}")
+    R = runtime()
+    from block_diffusion_drafter_gemm_amd import _lib as Lb
+    w = S.drafter_weights(cfg, seed=4)
+    dr = R.Drafter(cfg, w, max_batch=(rows + cfg.block_size - 2) // (cfg.block_size - 1), max_ctx=16, max_new=1)
+    z = R.to_device(S.normal_matrix(cfg, 80, (rows, cfg.hidden), 1.0, seed=rows))
+    ids_a, mx_a, lg_a = dr.lmhead_argmax(z, want_max=True, want_logits=True)
+    buf = torch.full((rows * cfg.vocab + 4,), float("nan"), dtype=torch.float32, device="cuda")
+    lg_u = buf[1:1 + rows * cfg.vocab]
+    assert lg_u.data_ptr() % 16 == 4
+    ids_u = torch.empty(rows, dtype=torch.int32, device="cuda")
+    mx_u = torch.empty(rows, dtype=torch.float32, device="cuda")
+    Lb.dflash_lmhead_argmax(dr.handle, z, rows, ids_u, mx_u, lg_u, dr.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(lg_u.view(rows, cfg.vocab), lg_a)
+    assert torch.equal(ids_u, ids_a) and torch.equal(mx_u, mx_a)
+    assert torch.isnan(buf[0]) and torch.isnan(buf[1 + rows * cfg.vocab:]).all()   # nothing written outside
+    dr.close()
+
+
 @pytest.mark.parametrize("name,rows", [("mini_bf16", 15), ("mini_bf16", 31), ("mini_b8", 130), ("mini_f32", 40),
                                        ("mini_big", 300)])
 def test_lmhead_argmax_nan_logits(name, rows):
