@@ -88,7 +88,9 @@ __device__ void find_seq(const int *ctx_len, int window, int batch, int B, int c
 // G*B <= 64, 8 for G*B <= 128); the first 256 threads stage K and V.  One tile
 // per wave keeps the register footprint small enough for 16 waves per CU.
 template <typename T, int HD, int NW>
-__global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(const AttnArgs a) {
+// Four waves per SIMD (the second bound counts waves per execution unit): four
+// 4-wave or two 8-wave workgroups per compute unit, at most 128 VGPRs.
+__global__ __launch_bounds__(NW * 64, 4) void attn_partial_kernel(const AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int EPV = 16 / (int)sizeof(T);      // elements per 16-byte vector
   constexpr int VPK = HD / EPV;                 // vectors per key row
@@ -189,9 +191,51 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
     }
     return blkp + ((size_t)(s * B + (t - ctx)) * a.nkv + g) * HD;
   };
+  // Fast path for a sub-block of context keys only, starting on a page
+  // boundary (every sub-block of a sequence but the last without a sliding
+  // window): a K thread's load j reads key tid/VPK + KPP*j, so its page is
+  // the same for the whole wave (read once, kept scalar) and its slot is
+  // tid/VPK + (KPP*j) % 16; a V thread's 8 consecutive keys share one page.
+  // Addresses are a base plus a 32-bit byte offset whose per-lane part is
+  // fixed before the loop: the K base is wave-uniform (page and slot), the V
+  // offset holds the lane's page too (a cache layer under 4 GB).
+  constexpr int KPP = 128 / VPK;                // keys per pass of the K threads
+  const unsigned slot_b = (unsigned)(a.nkv * HD * (int)sizeof(T));   // bytes per cache slot
+  const unsigned page_b = slot_b * kPage;
+  const int u128 = tid & 127, v_kg = u128 / (HD / 8);
+  // per-lane byte offset: K threads key slot tid/VPK, piece tid%VPK; V threads
+  // slot (kg%2)*8 of their 8-key group, dims dg*8..
+  const unsigned lane_b =
+      (unsigned)sizeof(T) * (tid < 128 ? (unsigned)((u128 / VPK) * (a.nkv * HD) + g * HD + (u128 % VPK) * EPV)
+                                       : (unsigned)(((v_kg & 1) * 8) * (a.nkv * HD) + g * HD + (u128 % (HD / 8)) * 8));
+  auto load_sub_fast = [&](int sub) {
+    const int pq = sub / kPage - p0;            // first page of the sub-block in s_pages
+    if (tid < 128) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (128 * j + tid >= kSub * VPK) break;   // never for HD = 128; HD = 64 stops at 4
+        const int pid = __builtin_amdgcn_readfirstlane(s_pages[pq + (KPP * j) / kPage]);
+        const char *pb = reinterpret_cast<const char *>(Kc) + (size_t)pid * page_b + ((KPP * j) % kPage) * slot_b;
+        pre[j] = *reinterpret_cast<const uint4 *>(pb + lane_b);
+      }
+    } else if (v_kg * 8 < kSub) {
+      // the group's page index is recomputed here from tid (laundered, so it
+      // is not hoisted out of the loop and kept live in a register)
+      int t_ = tid;
+      asm volatile("" : "+v"(t_));
+      const unsigned vo = (unsigned)s_pages[pq + ((t_ & 127) / (HD / 8)) / 2] * page_b + lane_b;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        pre[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(Vc) + (vo + j * slot_b));
+    }
+  };
   auto load_sub = [&](int sub) {
     if (tid >= 256) return;
     if constexpr (sizeof(T) == 2) {
+      if (a.off32 && sub % kPage == 0 && sub + kSub <= min(ctx, kend)) {   // uniform
+        load_sub_fast(sub);
+        return;
+      }
       if (tid < 128) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -222,17 +266,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
       } else {
         const int u = tid - 128, kg = u / (HD / 8), dg = u % (HD / 8);
         if (kg * 8 < kSub) {
-          // pre[j] holds dims dg*8..+7 of key kg*8+j; row e of V^T gets key j's dim e
+          // pre[j] holds dims dg*8..+7 of key kg*8+j; row e of V^T gets key j's
+          // dim e: word m of the row = (key 2m, key 2m+1), one byte permute each
           const uint32_t *w = reinterpret_cast<const uint32_t *>(pre);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             uint32_t o[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              const uint32_t lo = (w[(2 * m) * 4 + e / 2] >> (16 * (e & 1))) & 0xffffu;
-              const uint32_t hi = (w[(2 * m + 1) * 4 + e / 2] >> (16 * (e & 1))) & 0xffffu;
-              o[m] = lo | (hi << 16);
-            }
+            for (int m = 0; m < 4; ++m)
+              o[m] = __builtin_amdgcn_perm(w[(2 * m + 1) * 4 + e / 2], w[(2 * m) * 4 + e / 2],
+                                           (e & 1) ? 0x07060302u : 0x05040100u);
             *reinterpret_cast<uint4 *>(vt_lds + (dg * 8 + e) * VSTR + kg * 8) = make_uint4(o[0], o[1], o[2], o[3]);
           }
         }
@@ -295,11 +338,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 2) void attn_partial_kernel(
         bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
         bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
         const float m_new = fmaxf(m_run[t], bmax);
-        const float alpha = exp2f(m_run[t] - m_new);
+        // arguments are <= 0; the bare hardware exp2 (no denormal-range
+        // fix-up: weights below 2^-126 of the running max count as 0)
+        const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_new);
         float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = exp2f(p[e] - m_new);
+          p[e] = __builtin_amdgcn_exp2f(p[e] - m_new);
           psum += p[e];
         }
         l_run[t] = l_run[t] * alpha + psum;

@@ -509,6 +509,7 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
     at.causal = verify ? 1 : 0;
     at.window = c.window;
     at.block_len = kv->block_len;
+    at.off32 = (uint64_t)cache_layer < (1ull << 32) ? 1 : 0;
     if (launch_attention(h->bf16, at, s) != hipSuccess) return DFLASH_ERR_HIP;
     // target verify: the block's K/V join the context cache (the caller keeps
     // the accepted positions by advancing ctx_len; later blocks overwrite the rest)

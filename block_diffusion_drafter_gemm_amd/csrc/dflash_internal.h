@@ -105,6 +105,7 @@ struct AttnArgs {
   int causal;             // block row j sees block keys 0..j only (target verify)
   int window;             // > 0: only the last `window` context keys are attended
   const int *block_len;   // [batch] or NULL: block keys j >= block_len[s] are not attended
+  int off32;              // a cache layer spans < 4 GB: byte offsets inside it fit 32 bits
 };
 hipError_t launch_attention(bool is_bf16, const AttnArgs &a, hipStream_t st);
 int attn_chunk(int batch, int max_ctx, int block_size, int nq, int nkv, int cu);
