@@ -21,6 +21,7 @@
 namespace dflash {
 
 constexpr int kSub = 64;        // keys per LDS sub-block
+constexpr float kTau = 8.0f;    // log2 headroom of the lazy softmax rescale
 constexpr int kPage = 16;       // keys per cache page (the only page size accepted)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -139,6 +140,7 @@ __global__ __launch_bounds__(NW * 64, 4) void attn_partial_kernel(const AttnArgs
   const T *Q = (const T *)a.q;
   const T *Kc = (const T *)a.kc, *Vc = (const T *)a.vc, *Kb = (const T *)a.kb, *Vb = (const T *)a.vb;
   const float scale = kLog2e / sqrtf((float)HD);
+  const float mask_raw = -1e30f / scale;        // a masked key's raw score: -1e30 once scaled
 
   // query fragments of this wave's tiles (B operand: column = query row)
   Frag<T> qf[1][NU];
@@ -322,33 +324,49 @@ __global__ __launch_bounds__(NW * 64, 4) void attn_partial_kernel(const AttnArgs
             st[kt] = mma(st[kt], kf, qf[t][u]);
           }
         }
+        // raw scores; a masked key gets -1e30 / scale, i.e. -1e30 once scaled.
+        // When every key of this half is visible to every row (uniform) the
+        // per-key mask is skipped.  The scale folds into the exponent's FMA.
         float p[8];
-        float bmax = -1e30f;
+        if (!a.causal && sub + kb2 + 32 <= kend) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+          for (int e = 0; e < 8; ++e) p[e] = f4get(st[e / 4], e % 4);
+        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = sub + kb2 + kt * 16 + 4 * g4 + i;
+          for (int e = 0; e < 8; ++e) {
+            const int key = sub + kb2 + (e / 4) * 16 + 4 * g4 + e % 4;
             // causal (target verify): block row j sees keys up to position ctx + j
             const bool vis = key < kend && (!a.causal || key <= ctx + qrow_j[t]);
-            const float sc = vis ? f4get(st[kt], i) * scale : -1e30f;
-            p[kt * 4 + i] = sc;
-            bmax = fmaxf(bmax, sc);
+            p[e] = vis ? f4get(st[e / 4], e % 4) : mask_raw;
           }
+        }
+        // scale > 0: the max of the scaled scores, exactly
+        float bmax = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])), fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7]))) * scale;
         bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
         bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-        const float m_new = fmaxf(m_run[t], bmax);
-        // arguments are <= 0; the bare hardware exp2 (no denormal-range
-        // fix-up: weights below 2^-126 of the running max count as 0)
-        const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_new);
+        // Lazy rescale: the running reference m_run moves (and O, l are
+        // rescaled) only when some row's new maximum exceeds it by more than
+        // kTau; otherwise weights up to 2^kTau enter as they are.  O / l and
+        // the chunk merge do not depend on the reference, so the result is the
+        // same up to rounding, and the rescale becomes a rare uniform branch.
+        if (__any(bmax > m_run[t] + kTau)) {
+          const float m_new = fmaxf(m_run[t], bmax);
+          // arguments are <= 0; the bare hardware exp2 (no denormal-range
+          // fix-up: weights below 2^-126 of the reference count as 0)
+          const float alpha = __builtin_amdgcn_exp2f(m_run[t] - m_new);
+          l_run[t] *= alpha;
+#pragma unroll
+          for (int d = 0; d < ND; ++d) o[t][d] *= alpha;
+          m_run[t] = m_new;
+        }
+        const float mr = m_run[t];
         float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(p[e] - m_new);
+          p[e] = __builtin_amdgcn_exp2f(fmaf(p[e], scale, -mr));
           psum += p[e];
         }
-        l_run[t] = l_run[t] * alpha + psum;
-        m_run[t] = m_new;
+        l_run[t] += psum;
         // bf16: P = P_hi + P_lo, two bf16 terms, so the product keeps ~16
         // mantissa bits of the softmax weights instead of 8
         Frag<T> pf, pf_lo;
@@ -361,7 +379,6 @@ __global__ __launch_bounds__(NW * 64, 4) void attn_partial_kernel(const AttnArgs
         }
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          o[t][d] *= alpha;
           Frag<T> vf;
           const T *vr = vt_lds + (d * 16 + ln) * VSTR + kb2 + 4 * g4;
           if constexpr (sizeof(T) == 2) {
