@@ -96,7 +96,14 @@ __global__ __launch_bounds__(NW * 64, 4) void attn_partial_kernel(const AttnArgs
   constexpr int EPV = 16 / (int)sizeof(T);      // elements per 16-byte vector
   constexpr int VPK = HD / EPV;                 // vectors per key row
   constexpr int KSTR = HD + EPV;                // LDS row stride of K (elements)
-  constexpr int VSTR = kSub + EPV;              // LDS row stride of V^T (elements)
+  // LDS row stride of V^T (elements), padded: row r starts 4 (r % 8) dwords
+  // into the banks.  bf16 rows also XOR their 16-byte chunk index (8 keys)
+  // with (r / 8) % 8.  A V thread writes one chunk of rows dg*8 + e, so without
+  // it the 16 lanes of a key group (rows 8 apart, the same r % 8) all hit the
+  // same banks (16-way conflicts); with it they take 8 positions (2-way), and
+  // the fragment reads of 16 consecutive rows stay within 2 ways.
+  constexpr int VSTR = kSub + EPV;
+  auto vt_chunk = [](int row, int c) { return sizeof(T) == 2 ? c ^ ((row >> 3) & 7) : c; };
   constexpr int NU = HD / 32;                   // k-chunks over head_dim
   constexpr int ND = HD / 16;                   // d tiles
   __shared__ __align__(16) T k_lds[kSub * KSTR];
@@ -278,7 +285,8 @@ __global__ __launch_bounds__(NW * 64, 4) void attn_partial_kernel(const AttnArgs
             for (int m = 0; m < 4; ++m)
               o[m] = __builtin_amdgcn_perm(w[(2 * m + 1) * 4 + e / 2], w[(2 * m) * 4 + e / 2],
                                            (e & 1) ? 0x07060302u : 0x05040100u);
-            *reinterpret_cast<uint4 *>(vt_lds + (dg * 8 + e) * VSTR + kg * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+            const int row = dg * 8 + e;
+            *reinterpret_cast<uint4 *>(vt_lds + row * VSTR + vt_chunk(row, kg) * 8) = make_uint4(o[0], o[1], o[2], o[3]);
           }
         }
       }
@@ -382,8 +390,14 @@ __global__ __launch_bounds__(NW * 64, 4) void attn_partial_kernel(const AttnArgs
           Frag<T> vf;
           const T *vr = vt_lds + (d * 16 + ln) * VSTR + kb2 + 4 * g4;
           if constexpr (sizeof(T) == 2) {
-            const uint2 lo = *reinterpret_cast<const uint2 *>(vr);
-            const uint2 hi = *reinterpret_cast<const uint2 *>(vr + 16);
+            // keys k0 .. k0+3 (chunk k0/8) and k0+16 .. (chunk k0/8 + 2) of V^T
+            // row d*16 + ln.  The chunk bits (kb2/8: bit 2; g4/2: bit 0; +2:
+            // bit 1) and the swizzle ((2d + ln/8) % 8: bits 1-2 and bit 0) are
+            // disjoint, so the swizzled chunk is a compile-time part XOR the
+            // lane's bit (g4/2 ^ ln/8): one lane base and immediate offsets.
+            const T *vrow = vt_lds + ln * VSTR + 4 * (g4 & 1) + 8 * ((g4 >> 1) ^ (ln >> 3)) + d * 16 * VSTR;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + 8 * ((kb2 >> 3) ^ ((2 * d) & 7)));
+            const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 8 * ((kb2 >> 3) ^ ((2 * d) & 7) ^ 2));
             reinterpret_cast<Frag<bf16_t> &>(vf).v = make_uint4(lo.x, lo.y, hi.x, hi.y);
           } else {
             const float4 lo = *reinterpret_cast<const float4 *>(vr);
