@@ -217,32 +217,52 @@ __global__ __launch_bounds__(NW * 64, 4) void attn_partial_kernel(const AttnArgs
   const unsigned lane_b =
       (unsigned)sizeof(T) * (tid < 128 ? (unsigned)((u128 / VPK) * (a.nkv * HD) + g * HD + (u128 % VPK) * EPV)
                                        : (unsigned)(((v_kg & 1) * 8) * (a.nkv * HD) + g * HD + (u128 % (HD / 8)) * 8));
-  auto load_sub_fast = [&](int sub) {
-    const int pq = sub / kPage - p0;            // first page of the sub-block in s_pages
-    if (tid < 128) {
+  // waves 0, 1 stage K and waves 2, 3 stage V: a test the compiler knows is
+  // wave-uniform
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The fast path's page lookups for the next sub-block are read from LDS
+  // before this sub-block's LDS writes are issued: LDS operations complete in
+  // order, so a lookup queued behind the eight 16-byte writes waited for all
+  // of them.  K's four pages are wave-uniform, V keeps its byte offset.
+  struct FastPages {
+    int k[4];
+    unsigned vo;
+  };
+  auto fetch_fast = [&](int sub) {
+    FastPages f{{0, 0, 0, 0}, 0u};
+    const int pq = sub / kPage - p0;
+    if (wave_u < 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) f.k[q] = __builtin_amdgcn_readfirstlane(s_pages[pq + q]);
+    } else if (v_kg * 8 < kSub) {
+      int t_ = tid;
+      asm volatile("" : "+v"(t_));
+      f.vo = (unsigned)s_pages[pq + ((t_ & 127) / (HD / 8)) / 2] * page_b + lane_b;
+    }
+    return f;
+  };
+  auto load_sub_fast2 = [&](const FastPages &f) {
+    if (wave_u < 2) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (128 * j + tid >= kSub * VPK) break;   // never for HD = 128; HD = 64 stops at 4
-        const int pid = __builtin_amdgcn_readfirstlane(s_pages[pq + (KPP * j) / kPage]);
-        const char *pb = reinterpret_cast<const char *>(Kc) + (size_t)pid * page_b + ((KPP * j) % kPage) * slot_b;
+        const char *pb = reinterpret_cast<const char *>(Kc) + (size_t)f.k[(KPP * j) / kPage] * page_b +
+                         ((KPP * j) % kPage) * slot_b;
         pre[j] = *reinterpret_cast<const uint4 *>(pb + lane_b);
       }
     } else if (v_kg * 8 < kSub) {
-      // the group's page index is recomputed here from tid (laundered, so it
-      // is not hoisted out of the loop and kept live in a register)
-      int t_ = tid;
-      asm volatile("" : "+v"(t_));
-      const unsigned vo = (unsigned)s_pages[pq + ((t_ & 127) / (HD / 8)) / 2] * page_b + lane_b;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        pre[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(Vc) + (vo + j * slot_b));
+        pre[j] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(Vc) + (f.vo + j * slot_b));
     }
   };
+  auto fast_ok = [&](int sub) { return a.off32 && sub % kPage == 0 && sub + kSub <= min(ctx, kend); };
+  FastPages fp{{0, 0, 0, 0}, 0u};
   auto load_sub = [&](int sub) {
     if (tid >= 256) return;
     if constexpr (sizeof(T) == 2) {
-      if (a.off32 && sub % kPage == 0 && sub + kSub <= min(ctx, kend)) {   // uniform
-        load_sub_fast(sub);
+      if (fast_ok(sub)) {   // uniform
+        load_sub_fast2(fp);
         return;
       }
       if (tid < 128) {
@@ -307,9 +327,11 @@ __global__ __launch_bounds__(NW * 64, 4) void attn_partial_kernel(const AttnArgs
     }
   };
 
+  if (sizeof(T) == 2 && fast_ok(kbeg) && wave_u < 4) fp = fetch_fast(kbeg);
   load_sub(kbeg);
   for (int sub = kbeg; sub < kend; sub += kSub) {
     lds_barrier();
+    if (sizeof(T) == 2 && sub + kSub < kend && fast_ok(sub + kSub) && wave_u < 4) fp = fetch_fast(sub + kSub);
     store_sub(sub);
     if (sub + kSub < kend) load_sub(sub + kSub);
     lds_barrier();
