@@ -342,17 +342,20 @@ __global__ __launch_bounds__(NW * 64, 4) void attn_partial_kernel(const AttnArgs
 #pragma unroll
       for (int t = 0; t < 1; ++t) {
         if (!tile_on[t]) continue;
-        f32x4 st[2];
+        // S^T = K Q^T for two 16-key tiles; each K fragment is read one
+        // product ahead of its use
+        f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        auto read_kf = [&](int q) {
+          Frag<T> kf;
+          kf.load(k_lds + (kb2 + (q / NU) * 16 + ln) * KSTR + 8 * g4 + 32 * (q % NU));
+          return kf;
+        };
+        Frag<T> kcur = read_kf(0);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          const T *kr = k_lds + (kb2 + kt * 16 + ln) * KSTR + 8 * g4;
-#pragma unroll
-          for (int u = 0; u < NU; ++u) {
-            Frag<T> kf;
-            kf.load(kr + 32 * u);
-            st[kt] = mma(st[kt], kf, qf[t][u]);
-          }
+        for (int q = 0; q < 2 * NU; ++q) {
+          const Frag<T> knext = read_kf(q + 1 < 2 * NU ? q + 1 : q);
+          st[q / NU] = mma(st[q / NU], kcur, qf[t][q % NU]);
+          kcur = knext;
         }
         // raw scores; a masked key gets -1e30 / scale, i.e. -1e30 once scaled.
         // When every key of this half is visible to every row (uniform) the
@@ -407,10 +410,9 @@ __global__ __launch_bounds__(NW * 64, 4) void attn_partial_kernel(const AttnArgs
           for (int e = 0; e < 8; ++e) lo[e] = p[e] - pf.get(e);
           pf_lo.set(lo);
         }
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
+        // V^T fragment of d tile d (A operand: row = d, k = keys)
+        auto read_vf = [&](int d) {
           Frag<T> vf;
-          const T *vr = vt_lds + (d * 16 + ln) * VSTR + kb2 + 4 * g4;
           if constexpr (sizeof(T) == 2) {
             // keys k0 .. k0+3 (chunk k0/8) and k0+16 .. (chunk k0/8 + 2) of V^T
             // row d*16 + ln.  The chunk bits (kb2/8: bit 2; g4/2: bit 0; +2:
@@ -422,12 +424,21 @@ __global__ __launch_bounds__(NW * 64, 4) void attn_partial_kernel(const AttnArgs
             const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 8 * ((kb2 >> 3) ^ ((2 * d) & 7) ^ 2));
             reinterpret_cast<Frag<bf16_t> &>(vf).v = make_uint4(lo.x, lo.y, hi.x, hi.y);
           } else {
+            const T *vr = vt_lds + (d * 16 + ln) * VSTR + kb2 + 4 * g4;
             const float4 lo = *reinterpret_cast<const float4 *>(vr);
             const float4 hi = *reinterpret_cast<const float4 *>(vr + 16);
             reinterpret_cast<Frag<float> &>(vf).v = f32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
           }
-          o[t][d] = mma(o[t][d], vf, pf);
-          if constexpr (sizeof(T) == 2) o[t][d] = mma(o[t][d], vf, pf_lo);
+          return vf;
+        };
+        // one fragment of lookahead: tile d+1 is read before tile d's products
+        Frag<T> vcur = read_vf(0);
+#pragma unroll
+        for (int d = 0; d < ND; ++d) {
+          const Frag<T> vnext = read_vf(d + 1 < ND ? d + 1 : d);
+          o[t][d] = mma(o[t][d], vcur, pf);
+          if constexpr (sizeof(T) == 2) o[t][d] = mma(o[t][d], vcur, pf_lo);
+          vcur = vnext;
         }
       }
     }
