@@ -153,16 +153,29 @@ int compute_units(dflash_handle_s *h) {
   return h->n_cu;
 }
 
-enum { AM_GLOBAL = 0, AM_COPY = 1, AM_NORM = 2, AM_EMBED_NORM = 3, AM_PORTION = 4, AM_COPY_ROWS = 6 };
+enum { AM_GLOBAL = 0, AM_COPY = 1, AM_NORM = 2, AM_EMBED_NORM = 3, AM_PORTION = 4, AM_COPY_ROWS = 6, AM_TW8 = 16 };
 
 // Streaming GEMM (M <= 16): one persistent workgroup per compute unit.
 int launch_stream(dflash_handle_s *h, Epilogue epi, int amode, GemmArgs &a, int z, hipStream_t st,
                   int *grid_out = nullptr) {
   a.m_groups = 1;
   a.n_groups = gemm_tiles(epi, a.N, a.ffn);
+  const int cu = compute_units(h);
+  // bf16 QKV with RMSNorm staging: 8-column tiles (4 RoPE pairs) where they
+  // lower the weight bytes of the busiest workgroup (384 16-column tiles on
+  // 256 compute units: 2 per workgroup on 192 of them; 768 8-column tiles: 3
+  // per workgroup on all 256)
+  if (h->bf16 && (epi == EPI_QKV || epi == EPI_QKV_CACHE) && (amode == AM_NORM || amode == AM_EMBED_NORM) &&
+      a.hd % 8 == 0 && a.K % 64 == 0) {
+    const int per16 = (a.n_groups + cu - 1) / cu, per8 = (2 * a.n_groups + cu - 1) / cu;
+    if (per8 < 2 * per16) {
+      amode |= AM_TW8;
+      a.n_groups *= 2;
+    }
+  }
   // the fewest workgroups that keep the largest per-workgroup tile count (a
   // balanced grid); portions run one tile per workgroup
-  const int per = (a.n_groups + compute_units(h) - 1) / compute_units(h);
+  const int per = (a.n_groups + cu - 1) / cu;
   int grid = (a.n_groups + per - 1) / per;
   if (amode == AM_PORTION) grid = a.n_groups;
   if (grid_out) *grid_out = grid;

@@ -18,6 +18,16 @@
 //
 // Column maps and epilogues are those of the few-rows GEMM (RoPE pairs, SwiGLU
 // pairs, residual add, storage, per-row argmax).
+//
+// Tile width TW = 8 (bf16 QKV with resident rows): a tile is 4 RoPE pairs (8
+// weight rows), so that 6144 QKV columns make 768 tiles, 3 per workgroup on all
+// 256 compute units, where 384 16-column tiles leave a quarter of them idle.
+// One 1 KB weight load then covers 8 rows and two 32-wide k-chunks: lane
+// (l % 16, l / 16) reads row (l % 8) at chunk 2c + (l % 16) / 8.  Two products
+// per load, with the activation fragments of chunk 2c and of chunk 2c + 1,
+// leave x_2c . W_2c in columns 0-7 of the first accumulator and
+// x_2c+1 . W_2c+1 in columns 8-15 of the second; at the end of a tile lane l
+// adds lane (l ^ 8)'s second accumulator to its first.
 #include "dflash_device.h"
 #include "dflash_internal.h"
 
@@ -27,7 +37,7 @@ constexpr int kSWaves = 16;
 constexpr int kSThreads = kSWaves * 64;
 constexpr int kSResBytes = 128 * 1024;   // LDS budget of the resident activation rows
 
-enum AMode { A_GLOBAL = 0, A_COPY = 1, A_NORM = 2, A_EMBED_NORM = 3, A_COPY_ROWS = 6 };
+enum AMode { A_GLOBAL = 0, A_COPY = 1, A_NORM = 2, A_EMBED_NORM = 3, A_COPY_ROWS = 6, A_TW8 = 16 };
 
 // the QKV epilogues (with or without the copy into the paged cache)
 constexpr bool qkv_epi(int e) { return e == EPI_QKV || e == EPI_QKV_CACHE; }
@@ -37,14 +47,16 @@ __host__ __device__ constexpr int stream_res_k() {
   return kSResBytes / (16 * (int)sizeof(T));
 }
 
-template <int EPI>
+// weight row of column c (0 .. TW-1) of tile t
+template <int EPI, int TW = 16>
 __device__ __forceinline__ int s_weight_row(const GemmArgs &a, int t, int c) {
   if constexpr (EPI == EPI_SWIGLU) {
     return c < 8 ? t * 8 + c : a.ffn + t * 8 + (c - 8);
   } else if constexpr (qkv_epi(EPI) || EPI == EPI_INJECT) {
-    const int tph = a.hd / 16;
-    const int h = t / tph, j0 = (t - h * tph) * 8;
-    return h * a.hd + (c < 8 ? j0 + c : a.hd / 2 + j0 + (c - 8));
+    constexpr int P = TW / 2;                      // RoPE pairs per tile
+    const int tph = a.hd / TW;
+    const int h = t / tph, j0 = (t - h * tph) * P;
+    return h * a.hd + (c < P ? j0 + c : a.hd / 2 + j0 + (c - P));
   } else {
     return t * 16 + c;
   }
@@ -53,7 +65,7 @@ __device__ __forceinline__ int s_weight_row(const GemmArgs &a, int t, int c) {
 // Epilogue operands that do not depend on the weights, read at kernel start so
 // that the epilogue issues no dependent global load: the residual element of
 // the workgroup's first tile (thread tid < 256 owns row tid / 16, column
-// tid % 16) and the context length of the thread's row (QKV, tid < 128).
+// tid % 16) and the context length of the thread's row (QKV, tid < 16 * TW / 2).
 // Indices are clamped so every thread loads from a valid address.
 struct EpiPre {
   float x;
@@ -61,7 +73,7 @@ struct EpiPre {
   int page;   // QKV with a cache copy: page of the thread's row position (read after the staging loads)
 };
 
-template <int EPI>
+template <int EPI, int TW>
 __device__ __forceinline__ EpiPre s_epi_pre(const GemmArgs &a, int t0) {
   EpiPre p{0.f, 0, 0};
   const int tid = threadIdx.x;
@@ -69,14 +81,15 @@ __device__ __forceinline__ EpiPre s_epi_pre(const GemmArgs &a, int t0) {
     const int r = min(tid >> 4, a.M - 1), c = tid & 15;
     p.x = a.X[(size_t)r * a.ldx + t0 * 16 + c];
   } else if constexpr (qkv_epi(EPI)) {
-    p.ctx = a.ctx_len[min(tid >> 3, a.M - 1) / a.block_size];
+    p.ctx = a.ctx_len[min(tid / (TW / 2), a.M - 1) / a.block_size];
   }
   return p;
 }
 
-// Epilogue of one 16 x 16 tile held in LDS (ct, row-major [16][16]); ``first``
-// marks the workgroup's first tile, whose residual elements are in ``pre``.
-template <typename T, int EPI>
+// Epilogue of one 16 x 16 tile held in LDS (ct, row-major [16][16], columns
+// 0 .. TW-1 valid); ``first`` marks the workgroup's first tile, whose residual
+// elements are in ``pre``.
+template <typename T, int EPI, int TW>
 __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, int t, int layer, float *best_v,
                                            int *best_i, const double *inv_freq, const EpiPre &pre, bool first) {
   const int tid = threadIdx.x;
@@ -113,17 +126,18 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
       }
     }
   } else if constexpr (qkv_epi(EPI) || EPI == EPI_INJECT) {
-    if (tid < 128) {
-      const int r = tid >> 3, c = tid & 7;
+    constexpr int P = TW / 2;                         // RoPE pairs per tile
+    if (tid < 16 * P) {
+      const int r = tid / P, c = tid % P;
       if (r < a.M) {
         const int hd = a.hd, half = hd / 2;
         const int nqh = (qkv_epi(EPI)) ? a.nq : 0;  // q heads in the output
         const int qcols = nqh * hd;
         const int kcols = a.nkv * hd;
-        const int h = t / (hd / 16);                  // head of this tile (uniform)
-        const int j0 = (t % (hd / 16)) * 8;
-        const int n = s_weight_row<EPI>(a, t, c);
-        const float x1 = ct[r * 16 + c], x2 = ct[r * 16 + 8 + c];
+        const int h = t / (hd / TW);                  // head of this tile (uniform)
+        const int j0 = (t % (hd / TW)) * P;
+        const int n = s_weight_row<EPI, TW>(a, t, c);
+        const float x1 = ct[r * 16 + c], x2 = ct[r * 16 + P + c];
         int pos;
         size_t slot = 0;
         if constexpr (qkv_epi(EPI)) {
@@ -196,25 +210,43 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
 // exactly, so consuming one buffer waits only for that buffer's loads while
 // the other buffer's batch stays in flight.  Lanes of rows >= M read row 0;
 // their output rows are never stored.
-template <typename T, int U, bool RES>
+template <typename T, int U, bool RES, int TW = 16>
 struct StreamBuf {
+  static_assert(TW == 16 || (RES && sizeof(T) == 2), "8-column tiles: bf16 with resident rows");
+  static constexpr int CE = TW == 16 ? 32 : 64;   // k-elements per chunk step of one load
   Frag<T> w[U];
   Frag<T> x[RES ? 1 : U];
 
   template <int EPI>
   __device__ __forceinline__ void issue(const GemmArgs &a, const T *W, const T *arow, int t, int c0, int clast) {
     const int ln = threadIdx.x & 15, g = (threadIdx.x >> 4) & 3;
-    const T *wp = W + (size_t)s_weight_row<EPI>(a, t, ln) * a.ldw + 8 * g;
+    const T *wp = TW == 16 ? W + (size_t)s_weight_row<EPI, TW>(a, t, ln) * a.ldw + 8 * g
+                           : W + (size_t)s_weight_row<EPI, TW>(a, t, ln & 7) * a.ldw + 8 * g + 32 * (ln >> 3);
     __builtin_amdgcn_sched_barrier(0);   // loads issued before the batch stay before it
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int c = min(c0 + j, clast);
-      w[j].load(wp + 32 * c);
-      if constexpr (!RES) x[j].load(arow + 32 * c);
+      w[j].load(wp + CE * c);
+      if constexpr (!RES) x[j].load(arow + CE * c);
     }
     // the scheduler would otherwise sink the loads below the products that
     // free their registers, which serialises the stream
     __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // 8-column tiles: load j carries chunks 2c and 2c + 1 (c = c0 + j)
+  __device__ __forceinline__ void compute2(f32x4 &acc, f32x4 &acc2, const T *arow, int c0, int cend,
+                                           int clast) const {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      Frag<T> wj = w[j], a0, a1;
+      if (c0 + j >= cend) wj.zero();
+      const int c = min(c0 + j, clast);
+      a0.load(arow + 64 * c);
+      a1.load(arow + 64 * c + 32);
+      acc = mma(acc, a0, wj);
+      acc2 = mma(acc2, a1, wj);
+    }
   }
 
   __device__ __forceinline__ f32x4 compute(f32x4 acc, const T *arow, int c0, int cend, int clast) const {
@@ -235,7 +267,7 @@ struct StreamBuf {
 };
 
 // Tile finished: sum the 16 waves' partial tiles in wave order, run the epilogue.
-template <typename T, int EPI>
+template <typename T, int EPI, int TW>
 __device__ __forceinline__ void s_finish_tile(const GemmArgs &a, f32x4 &acc, float (*red)[256], float *ct, int t,
                                               int layer, float *best_v, int *best_i, const double *inv_freq,
                                               const EpiPre &pre, bool first) {
@@ -251,7 +283,7 @@ __device__ __forceinline__ void s_finish_tile(const GemmArgs &a, f32x4 &acc, flo
     ct[tid] = sm;
   }
   lds_barrier();
-  s_epilogue<T, EPI>(a, ct, t, layer, best_v, best_i, inv_freq, pre, first);
+  s_epilogue<T, EPI, TW>(a, ct, t, layer, best_v, best_i, inv_freq, pre, first);
 }
 
 // A_COPY_ROWS (residual projection and LM head argmax): grid.y is a 16-row
@@ -269,7 +301,7 @@ __device__ __forceinline__ GemmArgs row_slice(const GemmArgs &a0) {
   return a;
 }
 
-template <typename T, int EPI, int AM>
+template <typename T, int EPI, int AM, int TW = 16>
 __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a0) {
   static_assert(AM != A_COPY_ROWS || EPI == EPI_RESID || EPI == EPI_ARGMAX,
                 "row groups serve the residual projection and the LM head");
@@ -280,8 +312,9 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   constexpr bool RES = AM != A_GLOBAL;
   constexpr int KR = stream_res_k<T>();                        // resident k capacity
   constexpr int ASTR = (RES ? KR : 0) * (int)sizeof(T) + 16;   // bytes per resident row
-  // k-chunks per batch of loads (the double-buffered fragments stay within 64 VGPRs)
-  constexpr int U = (RES ? 8 : 4) / (int)(sizeof(T) / 2);
+  // k-chunks per batch of loads (the double-buffered fragments stay within 64
+  // VGPRs); an 8-column tile has half as many (double-width) chunk steps
+  constexpr int U = TW == 8 ? 4 : (RES ? 8 : 4) / (int)(sizeof(T) / 2);
   __shared__ __align__(16) unsigned char a_lds[RES ? 16 * ASTR : 16];
   __shared__ float red[kSWaves][256];
   __shared__ float ct[256];
@@ -300,7 +333,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
     }
     if constexpr (EPI == EPI_QKV_CACHE) {
       {
-        const int r = min(tid >> 3, a.M - 1);
+        const int r = min(tid / (TW / 2), a.M - 1);
         pre.page = a.block_table[(size_t)(r / a.block_size) * a.max_pages +
                                  (pre.ctx + r % a.block_size) / a.page_size];
       }
@@ -308,7 +341,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   };
   const T *W = (const T *)a0.W[layer];
   const int ntiles = a.n_groups;
-  const int CPT = a.K / 32;                                    // chunks per tile
+  const int CPT = a.K / StreamBuf<T, U, RES, TW>::CE;          // chunk steps per tile
   const int CPW = (CPT + kSWaves - 1) / kSWaves;               // chunks per wave
   const int cbeg = min(CPT, wave * CPW), cend = min(CPT, cbeg + CPW);
   const int clast = CPT - 1;                                   // always a valid chunk
@@ -327,12 +360,12 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
     BUF.template issue<EPI>(a, W, arow, tile_of(live_ ? (Q) : 0), live_ ? cbeg + ((Q) % nb) * U : d_, \
                             live_ ? clast : d_);                                               \
   }
-  pre = s_epi_pre<EPI>(a, tile_of(0));
+  pre = s_epi_pre<EPI, TW>(a, tile_of(0));
   const T *A = (const T *)a.A;
   const bool row_ok = ln < a.M;
   const T *arow = RES ? reinterpret_cast<const T *>(a_lds + ln * ASTR) + 8 * g
                       : A + (size_t)(row_ok ? ln : 0) * a.lda + 8 * g;
-  StreamBuf<T, U, RES> bufa, bufb;
+  StreamBuf<T, U, RES, TW> bufa, bufb;
 
   // ---- resident activation rows ---------------------------------------------
   // Wave w stages row w.  Every load of the row (and of the gain) is issued
@@ -440,6 +473,19 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   float best_v = -INFINITY;
   int best_i = -1;   // set by the first tile
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc2 = f32x4{0.f, 0.f, 0.f, 0.f};   // 8-column tiles: the odd chunks' products
+  // 8-column tiles: columns 8-15 of acc2 (lane l ^ 8) complete columns 0-7 of acc
+  auto fold = [&]() {
+    if constexpr (TW == 8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc2[i], 8);
+      acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto consume = [&](const StreamBuf<T, U, RES, TW> &b, int c0) {
+    if constexpr (TW == 8) b.compute2(acc, acc2, arow, c0, cend, clast);
+    else acc = b.compute(acc, arow, c0, cend, clast);
+  };
   // static ping-pong between two register buffers (dynamic selection would
   // spill the fragments to scratch): the next batch is issued before the
   // current one is consumed.  Every batch is issued whether or not it exists
@@ -451,13 +497,17 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   // consumes a dummy batch and finishes nothing.
   for (int q = 0; q < total; q += 2) {
     DF_ISSUE(bufb, q + 1);
-    acc = bufa.compute(acc, arow, cbeg + (q % nb) * U, cend, clast);
-    if (q % nb == nb - 1)
-      s_finish_tile<T, EPI>(a, acc, red, ct, tile_of(q), layer, &best_v, &best_i, inv_freq, pre, q < nb);
+    consume(bufa, cbeg + (q % nb) * U);
+    if (q % nb == nb - 1) {
+      fold();
+      s_finish_tile<T, EPI, TW>(a, acc, red, ct, tile_of(q), layer, &best_v, &best_i, inv_freq, pre, q < nb);
+    }
     DF_ISSUE(bufa, q + 2);
-    acc = bufb.compute(acc, arow, cbeg + ((q + 1) % nb) * U, cend, clast);
-    if ((q + 1) % nb == nb - 1 && q + 1 < total)
-      s_finish_tile<T, EPI>(a, acc, red, ct, tile_of(q + 1), layer, &best_v, &best_i, inv_freq, pre, q + 1 < nb);
+    consume(bufb, cbeg + ((q + 1) % nb) * U);
+    if ((q + 1) % nb == nb - 1 && q + 1 < total) {
+      fold();
+      s_finish_tile<T, EPI, TW>(a, acc, red, ct, tile_of(q + 1), layer, &best_v, &best_i, inv_freq, pre, q + 1 < nb);
+    }
   }
 #undef DF_ISSUE
 
@@ -499,7 +549,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_portion_kernel(const GemmArgs 
   const int nchunk = a.K / 32;
   const int np = (nchunk + CPP - 1) / CPP;       // portions
   const int clast = nchunk - 1;
-  const T *wrow = W + (size_t)s_weight_row<EPI>(a, t, ln) * a.ldw + 8 * g;
+  const T *wrow = W + (size_t)s_weight_row<EPI, 16>(a, t, ln) * a.ldw + 8 * g;
   const T *arow = reinterpret_cast<const T *>(a_lds + ln * ASTR) + 8 * g;
   // wave w stages row w (row 0 stands in for rows >= M, stored as zeros)
   const bool have_row = wave < a.M;
@@ -510,7 +560,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_portion_kernel(const GemmArgs 
   // free of branches
   auto pfirst = [&](int p) { return p < np ? p * CPP : 0; };
   auto pcount = [&](int p) { return p < np ? min(CPP, nchunk - p * CPP) : 1; };
-  const EpiPre pre = s_epi_pre<EPI>(a, t);
+  const EpiPre pre = s_epi_pre<EPI, 16>(a, t);
 
   Frag<T> wa[U], wb[U];
   uint4 cv[NV];
@@ -564,7 +614,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_portion_kernel(const GemmArgs 
 #undef DF_PORTION_MMA
   float best_v = -INFINITY;
   int best_i = -1;   // set by the first tile
-  s_finish_tile<T, EPI>(a, acc, red, ct, t, layer, &best_v, &best_i, inv_freq, pre, true);
+  s_finish_tile<T, EPI, 16>(a, acc, red, ct, t, layer, &best_v, &best_i, inv_freq, pre, true);
   if constexpr (EPI == EPI_ARGMAX) {
     if (tid < 16 && tid < a.M) {
       a.amax_val[(size_t)(a.row0 + tid) * gridDim.x + blockIdx.x] = best_v;
@@ -576,6 +626,20 @@ __global__ __launch_bounds__(kSThreads) void gemm_portion_kernel(const GemmArgs 
 template <typename T, int EPI>
 static hipError_t launch_s(int am, const GemmArgs &a, dim3 grid, hipStream_t st) {
   const dim3 block(kSThreads);
+  if (am & A_TW8) {   // 8-column tiles: bf16 QKV with RMSNorm staging only
+    if constexpr (sizeof(T) == 2 && qkv_epi(EPI)) {
+      switch (am & ~A_TW8) {
+        case A_NORM: hipLaunchKernelGGL((gemm_stream_kernel<T, EPI, A_NORM, 8>), grid, block, 0, st, a); break;
+        case A_EMBED_NORM:
+          hipLaunchKernelGGL((gemm_stream_kernel<T, EPI, A_EMBED_NORM, 8>), grid, block, 0, st, a);
+          break;
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   switch (am) {
     case A_GLOBAL: hipLaunchKernelGGL((gemm_stream_kernel<T, EPI, A_GLOBAL>), grid, block, 0, st, a); break;
     case A_COPY: hipLaunchKernelGGL((gemm_stream_kernel<T, EPI, A_COPY>), grid, block, 0, st, a); break;

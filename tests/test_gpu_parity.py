@@ -351,6 +351,18 @@ def test_draft_block_single_sequence(ctx, window, blen):
     dr.close()
 
 
+@pytest.mark.parametrize("nq,nkv", [(8, 2), (16, 4)])
+def test_draft_block_qkv_tile_widths(nq, nkv):
+    """Batch 1 x B 16 on the streaming GEMMs with 12 and 24 heads of 128 in the
+    QKV projection: 96 16-column tiles run as 192 8-column tiles (4 RoPE pairs,
+    two k-chunks per weight load), 192 16-column tiles stay 16 wide (8-column
+    tiles would not lower the busiest workgroup's share on 256 compute units);
+    hidden states against the oracle."""
+    cfg = dataclasses.replace(MINI["mini_bf16"], name=f"mini_q{nq}", batch=1, n_q_heads=nq, n_kv_heads=nkv)
+    log(f"draft_block batch 1, {nq} q heads, {nkv} kv heads")
+    run_draft_case(cfg, seed=8)
+
+
 @pytest.mark.parametrize("name,window", [("mini_bf16", 100), ("mini_d64", 50), ("mini_f32", 40)])
 def test_draft_block_sliding_window(name, window):
     """Sliding-window context (ragged contexts above and below the window;
