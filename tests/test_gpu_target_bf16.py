@@ -95,12 +95,29 @@ CASES = [  # (layers, B, lens, block sizes or None)
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("layers,B,lens,blens", CASES)
 def test_target_verify_bf16_qwen3_8b_layers(layers, B, lens, blens):
-    from block_diffusion_drafter_gemm_amd import runtime as R
     lens = np.array(lens, dtype=np.int32)
-    batch = len(lens)
-    cfg = target_cfg(layers, B, batch, int(lens.min()), int(lens.max()))
-    log(f"[{cfg.name}] bf16 target verify, contexts {lens.tolist()}, block sizes {blens}")
+    cfg = target_cfg(layers, B, len(lens), int(lens.min()), int(lens.max()))
     w, w64 = weights(layers)
+    run_verify(cfg, w, w64, lens, blens)
+
+
+def test_target_verify_bf16_qkv_16_column_tiles():
+    """1 sequence x 16 rows at hidden 512 with 16 query and 4 KV heads of 128:
+    192 QKV tiles of 16 columns, which the streaming QKV keeps (the Qwen3-8B
+    layer's 384 run as 768 8-column tiles), with the epilogue that writes the
+    block K/V into the cache; one layer against the oracle, same bars."""
+    cfg = dataclasses.replace(BASE, name="verify_q16", cid=130, hidden=512, n_q_heads=16, n_kv_heads=4, ffn=1024,
+                              vocab=1024, n_layers=1, n_feat_layers=1, block_size=16, batch=1, ctx_min=200,
+                              ctx_max=200)
+    w = S.drafter_weights(cfg, seed=5, random_gain=True)
+    w64 = {k: ([from_storage(x) for x in v] if isinstance(v, list) else from_storage(v)) for k, v in w.items()}
+    run_verify(cfg, w, w64, np.array([200], dtype=np.int32), None)
+
+
+def run_verify(cfg, w, w64, lens, blens):
+    from block_diffusion_drafter_gemm_amd import runtime as R
+    layers, B, batch = cfg.n_layers, cfg.block_size, len(lens)
+    log(f"[{cfg.name}] bf16 target verify, contexts {lens.tolist()}, block sizes {blens}")
     lay = S.paged_layout(cfg, lens, headroom=B, seed=4)
     Kp, Vp = S.ctx_kv_cache(cfg, lay, seed=4)
     rng = np.random.default_rng(int(lens.sum()) + B)
