@@ -5,10 +5,11 @@
 //
 // One 16-wave workgroup runs per compute unit and walks 16-column tiles
 // round-robin (tile = block, block + grid, ...).  For every tile the 16 waves
-// split the k-chunks (32 wide) evenly and their partial tiles are summed
-// through LDS in wave order; the next tile's weight fragments are already in
-// flight while a tile is reduced and its epilogue runs, so the HBM stream does
-// not stop between tiles.
+// split the k-chunk steps evenly and their partial tiles are summed through LDS
+// in wave order; the next tile's weight fragments are already in flight while
+// a tile is reduced and its epilogue runs, so the HBM stream does not stop
+// between tiles.  bf16 weights are read in whole 128-byte lines with the
+// non-temporal hint (see StreamBuf).
 //
 // The activation rows are staged in LDS once per workgroup when all of K fits
 // (K <= 4096 in bf16): as a copy, or as RMSNorm(X) * gain computed from the fp32
@@ -22,12 +23,6 @@
 // Tile width TW = 8 (bf16 QKV with resident rows): a tile is 4 RoPE pairs (8
 // weight rows), so that 6144 QKV columns make 768 tiles, 3 per workgroup on all
 // 256 compute units, where 384 16-column tiles leave a quarter of them idle.
-// One 1 KB weight load then covers 8 rows and two 32-wide k-chunks: lane
-// (l % 16, l / 16) reads row (l % 8) at chunk 2c + (l % 16) / 8.  Two products
-// per load, with the activation fragments of chunk 2c and of chunk 2c + 1,
-// leave x_2c . W_2c in columns 0-7 of the first accumulator and
-// x_2c+1 . W_2c+1 in columns 8-15 of the second; at the end of a tile lane l
-// adds lane (l ^ 8)'s second accumulator to its first.
 #include "dflash_device.h"
 #include "dflash_internal.h"
 
@@ -201,68 +196,122 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
   }
 }
 
-// One batch of U k-chunks: weight fragments (and, when the activations are not
-// resident, activation fragments) for one lane.
+// One batch of weight fragments (and, when the activations are not resident,
+// activation fragments) for one lane: U 1 KB loads per wave.
 //
-// Loads are issued unconditionally: a chunk past the wave's range reads the
-// last valid chunk of the row instead, and its product is masked to zero at
+// bf16: every weight load covers whole 128-byte lines, 8 weight rows at two
+// consecutive 32-wide k-chunks (a chunk step of 64): lane (l % 16, l / 16)
+// reads row r0 + (l % 8) at chunk 2c + (l % 16) / 8, bytes 16 (l / 16) ..  A
+// 16-column tile takes two such loads per step (rows 0-7, rows 8-15), an
+// 8-column tile one.  Two products per load, with the activation fragments of
+// chunk 2c and of chunk 2c + 1, leave the even chunk's dot products in columns
+// 0-7 of one accumulator and the odd chunk's in columns 8-15 of another (fold
+// combines them).  Streamed reads of whole lines with the non-temporal hint
+// measured 6.7 TB/s, half lines 5.6-5.9 TB/s (plain or non-temporal), so the
+// weights take this layout and the hint.  fp32: a 32-wide chunk of a row is
+// already a whole line; one load per chunk step, plain.
+//
+// Loads are issued unconditionally: a step past the wave's range reads the
+// last valid step of the row instead, and its product is masked to zero at
 // compute time.  Branch-free issue lets the compiler count outstanding loads
 // exactly, so consuming one buffer waits only for that buffer's loads while
 // the other buffer's batch stays in flight.  Lanes of rows >= M read row 0;
 // their output rows are never stored.
 template <typename T, int U, bool RES, int TW = 16>
 struct StreamBuf {
-  static_assert(TW == 16 || (RES && sizeof(T) == 2), "8-column tiles: bf16 with resident rows");
-  static constexpr int CE = TW == 16 ? 32 : 64;   // k-elements per chunk step of one load
-  Frag<T> w[U];
-  Frag<T> x[RES ? 1 : U];
+  static constexpr bool WL = sizeof(T) == 2;           // whole-line layout (bf16)
+  static_assert(TW == 16 || WL, "8-column tiles: bf16");
+  static constexpr int NR = WL ? TW / 8 : 1;           // loads per chunk step
+  static constexpr int S = U / NR;                     // chunk steps per batch
+  static constexpr int CE = WL ? 64 : 32;              // k-elements per chunk step
+  static constexpr int NA = WL ? 2 * NR : 1;           // accumulators
+  static_assert(S * NR == U, "whole steps per batch");
+  Frag<T> w[U];                                        // step j, row group r: w[NR * j + r]
+  Frag<T> x[RES ? 1 : (WL ? 2 : 1) * S];
 
   template <int EPI>
   __device__ __forceinline__ void issue(const GemmArgs &a, const T *W, const T *arow, int t, int c0, int clast) {
     const int ln = threadIdx.x & 15, g = (threadIdx.x >> 4) & 3;
-    const T *wp = TW == 16 ? W + (size_t)s_weight_row<EPI, TW>(a, t, ln) * a.ldw + 8 * g
-                           : W + (size_t)s_weight_row<EPI, TW>(a, t, ln & 7) * a.ldw + 8 * g + 32 * (ln >> 3);
+    const T *wp[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+      wp[r] = WL ? W + (size_t)s_weight_row<EPI, TW>(a, t, 8 * r + (ln & 7)) * a.ldw + 8 * g + 32 * (ln >> 3)
+                 : W + (size_t)s_weight_row<EPI, TW>(a, t, ln) * a.ldw + 8 * g;
     __builtin_amdgcn_sched_barrier(0);   // loads issued before the batch stay before it
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
+    for (int j = 0; j < S; ++j) {
       const int c = min(c0 + j, clast);
-      w[j].load(wp + CE * c);
-      if constexpr (!RES) x[j].load(arow + CE * c);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if constexpr (WL) w[NR * j + r].load_stream(wp[r] + CE * c);
+        else w[NR * j + r].load(wp[r] + CE * c);
+      }
+      if constexpr (!RES) {
+        if constexpr (WL) {
+          x[2 * j].load(arow + 64 * c);
+          x[2 * j + 1].load(arow + 64 * c + 32);
+        } else {
+          x[j].load(arow + 32 * c);
+        }
+      }
     }
     // the scheduler would otherwise sink the loads below the products that
     // free their registers, which serialises the stream
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // 8-column tiles: load j carries chunks 2c and 2c + 1 (c = c0 + j)
-  __device__ __forceinline__ void compute2(f32x4 &acc, f32x4 &acc2, const T *arow, int c0, int cend,
-                                           int clast) const {
+  __device__ __forceinline__ void compute(f32x4 (&acc)[NA], const T *arow, int c0, int cend, int clast) const {
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      Frag<T> wj = w[j], a0, a1;
-      if (c0 + j >= cend) wj.zero();
+    for (int j = 0; j < S; ++j) {
+      const bool on = c0 + j < cend;
       const int c = min(c0 + j, clast);
-      a0.load(arow + 64 * c);
-      a1.load(arow + 64 * c + 32);
-      acc = mma(acc, a0, wj);
-      acc2 = mma(acc2, a1, wj);
+      if constexpr (WL) {
+        Frag<T> a0, a1;
+        if constexpr (RES) {
+          a0.load(arow + 64 * c);
+          a1.load(arow + 64 * c + 32);
+        } else {
+          a0 = x[2 * j];
+          a1 = x[2 * j + 1];
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          Frag<T> wj = w[NR * j + r];
+          if (!on) wj.zero();
+          acc[2 * r] = mma(acc[2 * r], a0, wj);
+          acc[2 * r + 1] = mma(acc[2 * r + 1], a1, wj);
+        }
+      } else {
+        Frag<T> wj = w[j], af;
+        if (!on) wj.zero();
+        if constexpr (RES) af.load(arow + 32 * c); else af = x[j];
+        acc[0] = mma(acc[0], af, wj);
+      }
     }
   }
 
-  __device__ __forceinline__ f32x4 compute(f32x4 acc, const T *arow, int c0, int cend, int clast) const {
+  // the tile's 16 x 16 result in the fragment layout of one product (lane:
+  // column l % 16), the accumulators cleared
+  __device__ __forceinline__ static f32x4 fold(f32x4 (&acc)[NA]) {
+    f32x4 o;
+    if constexpr (!WL) {
+      o = acc[0];
+    } else if constexpr (NR == 1) {
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      Frag<T> wj = w[j];
-      if (c0 + j >= cend) wj.zero();
-      if constexpr (RES) {
-        Frag<T> af;
-        af.load(arow + 32 * min(c0 + j, clast));
-        acc = mma(acc, af, wj);
-      } else {
-        acc = mma(acc, x[j], wj);
+      for (int i = 0; i < 4; ++i) o[i] = acc[0][i] + __shfl_xor(acc[1][i], 8);
+    } else {
+      // columns 0-7: rows 0-7 (acc 0 even, acc 1 odd chunks from lane l ^ 8);
+      // columns 8-15: rows 8-15 (acc 3 odd, acc 2 even chunks from lane l ^ 8)
+      const bool lo = (threadIdx.x & 15) < 8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s1 = __shfl_xor(acc[1][i], 8), s2 = __shfl_xor(acc[2][i], 8);
+        o[i] = lo ? acc[0][i] + s1 : acc[3][i] + s2;
       }
     }
-    return acc;
+#pragma unroll
+    for (int k = 0; k < NA; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    return o;
   }
 };
 
@@ -312,9 +361,9 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   constexpr bool RES = AM != A_GLOBAL;
   constexpr int KR = stream_res_k<T>();                        // resident k capacity
   constexpr int ASTR = (RES ? KR : 0) * (int)sizeof(T) + 16;   // bytes per resident row
-  // k-chunks per batch of loads (the double-buffered fragments stay within 64
-  // VGPRs); an 8-column tile has half as many (double-width) chunk steps
+  // 1 KB loads per batch (the double-buffered fragments stay within 64 VGPRs)
   constexpr int U = TW == 8 ? 4 : (RES ? 8 : 4) / (int)(sizeof(T) / 2);
+  using Buf = StreamBuf<T, U, RES, TW>;
   __shared__ __align__(16) unsigned char a_lds[RES ? 16 * ASTR : 16];
   __shared__ float red[kSWaves][256];
   __shared__ float ct[256];
@@ -341,11 +390,11 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   };
   const T *W = (const T *)a0.W[layer];
   const int ntiles = a.n_groups;
-  const int CPT = a.K / StreamBuf<T, U, RES, TW>::CE;          // chunk steps per tile
+  const int CPT = a.K / Buf::CE;                               // chunk steps per tile
   const int CPW = (CPT + kSWaves - 1) / kSWaves;               // chunks per wave
   const int cbeg = min(CPT, wave * CPW), cend = min(CPT, cbeg + CPW);
   const int clast = CPT - 1;                                   // always a valid chunk
-  const int nb = (CPW + U - 1) / U;                            // batches per tile per wave
+  const int nb = (CPW + Buf::S - 1) / Buf::S;                  // batches per tile per wave
   const int my_tiles = blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
   const int total = my_tiles * nb;
   // tile of batch q of this workgroup, clamped to a valid tile
@@ -357,7 +406,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   {                                                                                            \
     const bool live_ = (Q) < total;                                                            \
     const int d_ = min(cbeg, clast); /* the dummy's chunk, valid even for a wave with no chunks */ \
-    BUF.template issue<EPI>(a, W, arow, tile_of(live_ ? (Q) : 0), live_ ? cbeg + ((Q) % nb) * U : d_, \
+    BUF.template issue<EPI>(a, W, arow, tile_of(live_ ? (Q) : 0), live_ ? cbeg + ((Q) % nb) * Buf::S : d_, \
                             live_ ? clast : d_);                                               \
   }
   pre = s_epi_pre<EPI, TW>(a, tile_of(0));
@@ -365,7 +414,7 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   const bool row_ok = ln < a.M;
   const T *arow = RES ? reinterpret_cast<const T *>(a_lds + ln * ASTR) + 8 * g
                       : A + (size_t)(row_ok ? ln : 0) * a.lda + 8 * g;
-  StreamBuf<T, U, RES, TW> bufa, bufb;
+  Buf bufa, bufb;
 
   // ---- resident activation rows ---------------------------------------------
   // Wave w stages row w.  Every load of the row (and of the gain) is issued
@@ -472,20 +521,10 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
 
   float best_v = -INFINITY;
   int best_i = -1;   // set by the first tile
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 acc2 = f32x4{0.f, 0.f, 0.f, 0.f};   // 8-column tiles: the odd chunks' products
-  // 8-column tiles: columns 8-15 of acc2 (lane l ^ 8) complete columns 0-7 of acc
-  auto fold = [&]() {
-    if constexpr (TW == 8) {
+  f32x4 accs[Buf::NA];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc2[i], 8);
-      acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  };
-  auto consume = [&](const StreamBuf<T, U, RES, TW> &b, int c0) {
-    if constexpr (TW == 8) b.compute2(acc, acc2, arow, c0, cend, clast);
-    else acc = b.compute(acc, arow, c0, cend, clast);
-  };
+  for (int k = 0; k < Buf::NA; ++k) accs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc;
   // static ping-pong between two register buffers (dynamic selection would
   // spill the fragments to scratch): the next batch is issued before the
   // current one is consumed.  Every batch is issued whether or not it exists
@@ -497,15 +536,15 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   // consumes a dummy batch and finishes nothing.
   for (int q = 0; q < total; q += 2) {
     DF_ISSUE(bufb, q + 1);
-    consume(bufa, cbeg + (q % nb) * U);
+    bufa.compute(accs, arow, cbeg + (q % nb) * Buf::S, cend, clast);
     if (q % nb == nb - 1) {
-      fold();
+      acc = Buf::fold(accs);
       s_finish_tile<T, EPI, TW>(a, acc, red, ct, tile_of(q), layer, &best_v, &best_i, inv_freq, pre, q < nb);
     }
     DF_ISSUE(bufa, q + 2);
-    consume(bufb, cbeg + ((q + 1) % nb) * U);
+    bufb.compute(accs, arow, cbeg + ((q + 1) % nb) * Buf::S, cend, clast);
     if ((q + 1) % nb == nb - 1 && q + 1 < total) {
-      fold();
+      acc = Buf::fold(accs);
       s_finish_tile<T, EPI, TW>(a, acc, red, ct, tile_of(q + 1), layer, &best_v, &best_i, inv_freq, pre, q + 1 < nb);
     }
   }
