@@ -229,8 +229,11 @@ struct StreamBuf {
   Frag<T> w[U];                                        // step j, row group r: w[NR * j + r]
   Frag<T> x[RES ? 1 : (WL ? 2 : 1) * S];
 
+  // arow: the lane's activation pointer (resident rows: in LDS; bf16 from
+  // global memory: rows 0-7 in the whole-line layout, arow_hi rows 8-15)
   template <int EPI>
-  __device__ __forceinline__ void issue(const GemmArgs &a, const T *W, const T *arow, int t, int c0, int clast) {
+  __device__ __forceinline__ void issue(const GemmArgs &a, const T *W, const T *arow, const T *arow_hi, int t, int c0,
+                                        int clast) {
     const int ln = threadIdx.x & 15, g = (threadIdx.x >> 4) & 3;
     const T *wp[NR];
 #pragma unroll
@@ -249,7 +252,7 @@ struct StreamBuf {
       if constexpr (!RES) {
         if constexpr (WL) {
           x[2 * j].load(arow + 64 * c);
-          x[2 * j + 1].load(arow + 64 * c + 32);
+          x[2 * j + 1].load(arow_hi + 64 * c);
         } else {
           x[j].load(arow + 32 * c);
         }
@@ -271,8 +274,14 @@ struct StreamBuf {
           a0.load(arow + 64 * c);
           a1.load(arow + 64 * c + 32);
         } else {
-          a0 = x[2 * j];
-          a1 = x[2 * j + 1];
+          // whole-line activation loads back to the product layout: lane l
+          // (column l % 16 < 8) holds rows 0-7 at chunk 2c in x[2j] and row
+          // l % 16 at chunk 2c + 1 comes from lane l ^ 8; rows 8-15 the other
+          // way round (x[2j + 1])
+          const bool lo = (threadIdx.x & 15) < 8;
+          const Frag<T> sa = xor8(x[2 * j]), sb = xor8(x[2 * j + 1]);
+          a0 = lo ? x[2 * j] : sb;
+          a1 = lo ? sa : x[2 * j + 1];
         }
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
@@ -288,6 +297,20 @@ struct StreamBuf {
         acc[0] = mma(acc[0], af, wj);
       }
     }
+  }
+
+  // the fragment of lane l ^ 8 (a 16-lane row rotated by 8)
+  __device__ __forceinline__ static Frag<T> xor8(const Frag<T> &f) {
+    Frag<T> o;
+    if constexpr (sizeof(T) == 2) {
+      o.v.x = __builtin_amdgcn_mov_dpp((int)f.v.x, 0x128, 0xF, 0xF, false);
+      o.v.y = __builtin_amdgcn_mov_dpp((int)f.v.y, 0x128, 0xF, 0xF, false);
+      o.v.z = __builtin_amdgcn_mov_dpp((int)f.v.z, 0x128, 0xF, 0xF, false);
+      o.v.w = __builtin_amdgcn_mov_dpp((int)f.v.w, 0x128, 0xF, 0xF, false);
+    } else {
+      o = f;
+    }
+    return o;
   }
 
   // the tile's 16 x 16 result in the fragment layout of one product (lane:
@@ -406,14 +429,24 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   {                                                                                            \
     const bool live_ = (Q) < total;                                                            \
     const int d_ = min(cbeg, clast); /* the dummy's chunk, valid even for a wave with no chunks */ \
-    BUF.template issue<EPI>(a, W, arow, tile_of(live_ ? (Q) : 0), live_ ? cbeg + ((Q) % nb) * Buf::S : d_, \
+    BUF.template issue<EPI>(a, W, arow, arow_hi, tile_of(live_ ? (Q) : 0), live_ ? cbeg + ((Q) % nb) * Buf::S : d_, \
                             live_ ? clast : d_);                                               \
   }
   pre = s_epi_pre<EPI, TW>(a, tile_of(0));
   const T *A = (const T *)a.A;
-  const bool row_ok = ln < a.M;
-  const T *arow = RES ? reinterpret_cast<const T *>(a_lds + ln * ASTR) + 8 * g
-                      : A + (size_t)(row_ok ? ln : 0) * a.lda + 8 * g;
+  // activation pointer of this lane: rows in LDS, or rows in global memory
+  // (bf16: whole lines, rows ln % 8 and 8 + ln % 8 at chunk 2c + ln / 8; rows
+  // >= M read row 0 and are never stored)
+  const T *arow, *arow_hi = nullptr;
+  if constexpr (RES) {
+    arow = reinterpret_cast<const T *>(a_lds + ln * ASTR) + 8 * g;
+  } else if constexpr (Buf::WL) {
+    const int r0 = ln & 7, r1 = 8 + (ln & 7);
+    arow = A + (size_t)(r0 < a.M ? r0 : 0) * a.lda + 8 * g + 32 * (ln >> 3);
+    arow_hi = A + (size_t)(r1 < a.M ? r1 : 0) * a.lda + 8 * g + 32 * (ln >> 3);
+  } else {
+    arow = A + (size_t)(ln < a.M ? ln : 0) * a.lda + 8 * g;
+  }
   Buf bufa, bufb;
 
   // ---- resident activation rows ---------------------------------------------
