@@ -208,7 +208,9 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
 // 0-7 of one accumulator and the odd chunk's in columns 8-15 of another (fold
 // combines them).  Streamed reads of whole lines with the non-temporal hint
 // measured 6.7 TB/s, half lines 5.6-5.9 TB/s (plain or non-temporal), so the
-// weights take this layout and the hint.  fp32: a 32-wide chunk of a row is
+// weights take this layout and the hint.  The QKV projection alone keeps plain
+// loads: with the hint the block attention launched after it ran 1.2 us
+// longer per layer, while QKV itself gained 0.2 us (measured, batch 1).  fp32: a 32-wide chunk of a row is
 // already a whole line; one load per chunk step, plain.
 //
 // Loads are issued unconditionally: a step past the wave's range reads the
@@ -246,7 +248,7 @@ struct StreamBuf {
       const int c = min(c0 + j, clast);
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        if constexpr (WL) w[NR * j + r].load_stream(wp[r] + CE * c);
+        if constexpr (WL && !qkv_epi(EPI)) w[NR * j + r].load_stream(wp[r] + CE * c);
         else w[NR * j + r].load(wp[r] + CE * c);
       }
       if constexpr (!RES) {
