@@ -210,8 +210,9 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
 // measured 6.7 TB/s, half lines 5.6-5.9 TB/s (plain or non-temporal), so the
 // weights take this layout and the hint.  The QKV projection alone keeps plain
 // loads: with the hint the block attention launched after it ran 1.2 us
-// longer per layer, while QKV itself gained 0.2 us (measured, batch 1).  fp32: a 32-wide chunk of a row is
-// already a whole line; one load per chunk step, plain.
+// longer per layer, while QKV itself gained 0.2 us (measured, batch 1).
+// fp32: a 32-wide chunk of a row is already a whole line; one plain load per
+// chunk step.
 //
 // Loads are issued unconditionally: a step past the wave's range reads the
 // last valid step of the row instead, and its product is masked to zero at
@@ -276,10 +277,12 @@ struct StreamBuf {
           a0.load(arow + 64 * c);
           a1.load(arow + 64 * c + 32);
         } else {
-          // whole-line activation loads back to the product layout: lane l
-          // (column l % 16 < 8) holds rows 0-7 at chunk 2c in x[2j] and row
-          // l % 16 at chunk 2c + 1 comes from lane l ^ 8; rows 8-15 the other
-          // way round (x[2j + 1])
+          // whole-line activation loads back to the product layout.  x[2j]
+          // holds rows 0-7 (lane l % 16 < 8: row l % 16, chunk 2c; lane
+          // l % 16 >= 8: row l % 16 - 8, chunk 2c + 1), x[2j + 1] rows 8-15 the
+          // same way.  A lane of row r < 8 keeps its chunk-2c piece and takes
+          // the chunk-2c+1 piece from lane l ^ 8; a lane of row r >= 8 keeps
+          // its chunk-2c+1 piece and takes the chunk-2c piece from lane l ^ 8.
           const bool lo = (threadIdx.x & 15) < 8;
           const Frag<T> sa = xor8(x[2 * j]), sb = xor8(x[2 * j + 1]);
           a0 = lo ? x[2 * j] : sb;
