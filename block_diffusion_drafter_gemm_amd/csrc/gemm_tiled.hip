@@ -948,6 +948,24 @@ hipError_t launch_gemm_tiled(Epilogue epi, GemmArgs &a, int z_slices, int cu, hi
   const long tiles = (long)((a.M + 127) / 128) * a.n_groups * z_slices;
   if (tiles256 >= cu && 2 * ((tiles256 + cu - 1) / cu) <= (tiles + cu - 1) / cu)
     return launch_tiled_bm<256>(epi, a, z_slices, 1, st);
+  // residual projection with a long K (the batched down projection, 512 rows
+  // of K = 12288): 256 x 128 tiles split over K fill the compute units with
+  // half the staged bytes per flop of 128 x 128 ones, when each split keeps at
+  // least 2048 of K (down 79.8 -> 71.9 us with the reduction; the O
+  // projection's 1024-long splits measured slower and keep 128 x 128)
+  if (a.part && z_slices == 1 && epi == EPI_RESID && a.M > 128) {
+    int s2 = 1;
+    while (s2 < 4 && tiles256 * s2 < cu && a.K % (s2 * 2 * kTBK) == 0 && a.K / (s2 * 2) >= 2048 &&
+           (size_t)s2 * 2 * a.M * a.n_groups * kTBN * 4 <= a.part_bytes)
+      s2 *= 2;
+    if (s2 > 1 && tiles256 * s2 >= cu) {
+      a.kper = a.K / s2;
+      hipError_t e = launch_tiled_bm<256>(epi, a, z_slices, s2, st);
+      if (e != hipSuccess) return e;
+      launch_splitk_resid(a, s2, cu, st);
+      return hipGetLastError();
+    }
+  }
   int splits = 1;
   if (a.part && z_slices == 1 && epi == EPI_RESID) {
     while (splits < 4 && tiles * splits * 2 <= cu && a.K % (splits * 2 * kTBK) == 0 && a.K / (splits * 2) >= 1024 &&
