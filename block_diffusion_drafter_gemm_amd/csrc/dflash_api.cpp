@@ -173,10 +173,20 @@ int launch_stream(dflash_handle_s *h, Epilogue epi, int amode, GemmArgs &a, int 
       a.n_groups *= 2;
     }
   }
+  // several weight slices (the inject's per-layer K/V projections): one flat
+  // tile range over all of them, so a workgroup stages its rows once for tiles
+  // of several slices (5 layers x 128 tiles on 256 compute units: 3 tiles per
+  // workgroup in one launch round instead of 640 one-tile workgroups)
+  a.z_flat = 0;
+  if (z > 1 && epi == EPI_INJECT && (amode == AM_COPY || amode == AM_GLOBAL)) {
+    a.z_flat = z;
+    z = 1;
+  }
+  const int tiles = a.n_groups * (a.z_flat > 0 ? a.z_flat : 1);
   // the fewest workgroups that keep the largest per-workgroup tile count (a
   // balanced grid); portions run one tile per workgroup
-  const int per = (a.n_groups + cu - 1) / cu;
-  int grid = (a.n_groups + per - 1) / per;
+  const int per = (tiles + cu - 1) / cu;
+  int grid = (tiles + per - 1) / per;
   if (amode == AM_PORTION) grid = a.n_groups;
   if (grid_out) *grid_out = grid;
   return launch_gemm_stream(h->bf16, epi, amode, a, grid, z, st) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
@@ -190,6 +200,7 @@ int launch_stream(dflash_handle_s *h, Epilogue epi, int amode, GemmArgs &a, int 
 int launch_rows(dflash_handle_s *h, Epilogue epi, GemmArgs &a, hipStream_t st, int *grid_out = nullptr) {
   const int groups = (a.M + 15) / 16;
   a.row_groups = groups;
+  a.z_flat = 0;
   a.m_groups = 1;
   a.n_groups = gemm_tiles(epi, a.N, a.ffn);
   int cu = compute_units(h) / groups / 8 * 8;

@@ -66,6 +66,10 @@ struct GemmArgs {
   // rows): row_groups slices of the grid, one per 16-row group (grid.y); row0
   // is the group's first row, set inside the kernel
   int row_groups, row0;
+  // streaming GEMM over several weight slices in one flat tile range (the
+  // per-layer K/V projections of the context inject): slice = tile / n_groups;
+  // 0 for one slice per grid.y index
+  int z_flat;
 };
 
 // Launch a skinny GEMM; ``z_slices`` = number of weight slices (layers) in the

@@ -378,7 +378,9 @@ __device__ __forceinline__ GemmArgs row_slice(const GemmArgs &a0) {
   return a;
 }
 
-template <typename T, int EPI, int AM, int TW = 16>
+// FLAT: the weight slices of a.z_flat layers form one tile range (the
+// inject's per-layer K/V projections); otherwise grid.y selects the slice.
+template <typename T, int EPI, int AM, int TW = 16, bool FLAT = false>
 __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a0) {
   static_assert(AM != A_COPY_ROWS || EPI == EPI_RESID || EPI == EPI_ARGMAX,
                 "row groups serve the residual projection and the LM head");
@@ -416,8 +418,13 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
       }
     }
   };
-  const T *W = (const T *)a0.W[layer];
-  const int ntiles = a.n_groups;
+  // FLAT: tile t is tile t % n_groups of slice t / n_groups, so a workgroup
+  // stages its rows once for tiles of several slices
+  const T *W0 = (const T *)a0.W[layer];
+  auto slice_of = [&](int t) { return FLAT ? t / a.n_groups : layer; };
+  auto tile_in = [&](int t) { return FLAT ? t - (t / a.n_groups) * a.n_groups : t; };
+  auto w_of = [&](int t) { return FLAT ? (const T *)a0.W[slice_of(t)] : W0; };
+  const int ntiles = FLAT ? a.n_groups * a.z_flat : a.n_groups;
   const int CPT = a.K / Buf::CE;                               // chunk steps per tile
   const int CPW = (CPT + kSWaves - 1) / kSWaves;               // chunks per wave
   const int cbeg = min(CPT, wave * CPW), cend = min(CPT, cbeg + CPW);
@@ -434,10 +441,11 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   {                                                                                            \
     const bool live_ = (Q) < total;                                                            \
     const int d_ = min(cbeg, clast); /* the dummy's chunk, valid even for a wave with no chunks */ \
-    BUF.template issue<EPI>(a, W, arow, arow_hi, tile_of(live_ ? (Q) : 0), live_ ? cbeg + ((Q) % nb) * Buf::S : d_, \
+    const int t_ = tile_of(live_ ? (Q) : 0);                                                      \
+    BUF.template issue<EPI>(a, w_of(t_), arow, arow_hi, tile_in(t_), live_ ? cbeg + ((Q) % nb) * Buf::S : d_, \
                             live_ ? clast : d_);                                               \
   }
-  pre = s_epi_pre<EPI, TW>(a, tile_of(0));
+  pre = s_epi_pre<EPI, TW>(a, tile_in(tile_of(0)));
   const T *A = (const T *)a.A;
   // activation pointer of this lane: rows in LDS, or rows in global memory
   // (bf16: whole lines, rows ln % 8 and 8 + ln % 8 at chunk 2c + ln / 8; rows
@@ -577,13 +585,15 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
     bufa.compute(accs, arow, cbeg + (q % nb) * Buf::S, cend, clast);
     if (q % nb == nb - 1) {
       acc = Buf::fold(accs);
-      s_finish_tile<T, EPI, TW>(a, acc, red, ct, tile_of(q), layer, &best_v, &best_i, inv_freq, pre, q < nb);
+      s_finish_tile<T, EPI, TW>(a, acc, red, ct, tile_in(tile_of(q)), slice_of(tile_of(q)), &best_v, &best_i, inv_freq,
+                                pre, q < nb);
     }
     DF_ISSUE(bufa, q + 2);
     bufb.compute(accs, arow, cbeg + ((q + 1) % nb) * Buf::S, cend, clast);
     if ((q + 1) % nb == nb - 1 && q + 1 < total) {
       acc = Buf::fold(accs);
-      s_finish_tile<T, EPI, TW>(a, acc, red, ct, tile_of(q + 1), layer, &best_v, &best_i, inv_freq, pre, q + 1 < nb);
+      s_finish_tile<T, EPI, TW>(a, acc, red, ct, tile_in(tile_of(q + 1)), slice_of(tile_of(q + 1)), &best_v, &best_i,
+                                inv_freq, pre, q + 1 < nb);
     }
   }
 #undef DF_ISSUE
@@ -703,6 +713,20 @@ __global__ __launch_bounds__(kSThreads) void gemm_portion_kernel(const GemmArgs 
 template <typename T, int EPI>
 static hipError_t launch_s(int am, const GemmArgs &a, dim3 grid, hipStream_t st) {
   const dim3 block(kSThreads);
+  if (a.z_flat > 0) {   // one flat tile range over the layers: the inject's K/V projections
+    if constexpr (EPI == EPI_INJECT) {
+      switch (am) {
+        case A_COPY: hipLaunchKernelGGL((gemm_stream_kernel<T, EPI, A_COPY, 16, true>), grid, block, 0, st, a); break;
+        case A_GLOBAL:
+          hipLaunchKernelGGL((gemm_stream_kernel<T, EPI, A_GLOBAL, 16, true>), grid, block, 0, st, a);
+          break;
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   if (am & A_TW8) {   // 8-column tiles: bf16 QKV with RMSNorm staging only
     if constexpr (sizeof(T) == 2 && qkv_epi(EPI)) {
       switch (am & ~A_TW8) {
