@@ -45,7 +45,7 @@ struct Carve {
 
 // ---- draft_block layout --------------------------------------------------
 struct DraftLayout {
-  size_t X, Y, Q, Kb, Vb, O, Hs, attn_part, attn_stats, gemm_part, gemm_part_bytes, total;
+  size_t X, Y, Q, Kb, Vb, O, Hs, attn_part, attn_stats, gemm_part, gemm_part_bytes, split_part, total;
   int chunk, max_items;
 };
 
@@ -73,6 +73,10 @@ DraftLayout draft_layout(const dflash_handle_s *h, int batch, int max_ctx, int c
   // path: up to 4 fp32 slices of [R, hidden]
   L.gemm_part_bytes = R > 64 ? (size_t)4 * R * c.hidden * 4 : 0;
   L.gemm_part = cv.take(L.gemm_part_bytes);
+  // the two halves' partials of the split residual projection (<= 16 rows);
+  // reserved whenever one sequence's block fits, so that a smaller batch never
+  // needs more workspace than the largest
+  L.split_part = B <= 16 ? cv.take((size_t)2 * 16 * c.hidden * 4) : 0;
   L.total = cv.off;
   return L;
 }
@@ -153,7 +157,10 @@ int compute_units(dflash_handle_s *h) {
   return h->n_cu;
 }
 
-enum { AM_GLOBAL = 0, AM_COPY = 1, AM_NORM = 2, AM_EMBED_NORM = 3, AM_PORTION = 4, AM_COPY_ROWS = 6, AM_TW8 = 16 };
+enum {
+  AM_GLOBAL = 0, AM_COPY = 1, AM_NORM = 2, AM_EMBED_NORM = 3, AM_PORTION = 4, AM_COPY_ROWS = 6, AM_TW8 = 16,
+  AM_SPLIT2 = 32
+};
 
 // Streaming GEMM (M <= 16): one persistent workgroup per compute unit.
 int launch_stream(dflash_handle_s *h, Epilogue epi, int amode, GemmArgs &a, int z, hipStream_t st,
@@ -172,6 +179,18 @@ int launch_stream(dflash_handle_s *h, Epilogue epi, int amode, GemmArgs &a, int 
       amode |= AM_TW8;
       a.n_groups *= 2;
     }
+  }
+  // bf16 residual projection with K past the resident capacity (the down
+  // projection): 32-column tiles in pairs of workgroups, each over half of K,
+  // so a compute unit reads half the activation bytes for the same weight
+  // bytes; the pair's second workgroup to finish adds both halves
+  if (h->bf16 && epi == EPI_RESID && amode == AM_GLOBAL && z == 1 && a.cnt && a.spart &&
+      a.K > stream_res_k(true) && a.K % 128 == 0 && a.N % 256 == 0 && a.N / 16 <= cu) {
+    a.z_flat = 0;
+    const int grid = a.N / 16;   // 2 x the 32-column tiles
+    a.n_groups = grid;
+    if (grid_out) *grid_out = grid;
+    return launch_gemm_stream(true, epi, AM_SPLIT2, a, grid, 1, st) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
   }
   // several weight slices (the inject's per-layer K/V projections): one flat
   // tile range over all of them, so a workgroup stages its rows once for tiles
@@ -610,6 +629,10 @@ static int forward_block(dflash_handle h, const int32_t *anchor_ids, const int32
     dn.ldx = c.hidden;
     dn.part = o.part;
     dn.part_bytes = o.part_bytes;
+    if (L.split_part && R <= 16) {   // arrival counters at the front of the workspace
+      dn.cnt = reinterpret_cast<unsigned *>(w);
+      dn.spart = reinterpret_cast<float *>(w + L.split_part);
+    }
     st = fast ? launch_stream(h, EPI_RESID, c.ffn <= KR ? AM_COPY : AM_GLOBAL, dn, 1, s)
               : launch(h, EPI_RESID, dn, 1, s);
     if (st != DFLASH_OK) return st;

@@ -70,6 +70,11 @@ struct GemmArgs {
   // per-layer K/V projections of the context inject): slice = tile / n_groups;
   // 0 for one slice per grid.y index
   int z_flat;
+  // streaming residual projection split over K in pairs of workgroups: one
+  // arrival counter per 32-column tile (zero between launches) and the two
+  // halves' fp32 partials [2][16][N]; NULL: no split
+  unsigned *cnt;
+  float *spart;
 };
 
 // Launch a skinny GEMM; ``z_slices`` = number of weight slices (layers) in the

@@ -23,6 +23,11 @@
 // Tile width TW = 8 (bf16 QKV with resident rows): a tile is 4 RoPE pairs (8
 // weight rows), so that 6144 QKV columns make 768 tiles, 3 per workgroup on all
 // 256 compute units, where 384 16-column tiles leave a quarter of them idle.
+// TW = 32 (bf16 down projection, K past the resident capacity): a pair of
+// workgroups shares a 32-column tile, each over half of K, so a compute unit
+// reads half the activation fragments for the same weight bytes (down
+// 29.1 -> 25.4 us per layer, Qwen3-8B shape); the pair's second workgroup to
+// finish adds the two halves to the residual.
 #include "dflash_device.h"
 #include "dflash_internal.h"
 
@@ -32,7 +37,7 @@ constexpr int kSWaves = 16;
 constexpr int kSThreads = kSWaves * 64;
 constexpr int kSResBytes = 128 * 1024;   // LDS budget of the resident activation rows
 
-enum AMode { A_GLOBAL = 0, A_COPY = 1, A_NORM = 2, A_EMBED_NORM = 3, A_COPY_ROWS = 6, A_TW8 = 16 };
+enum AMode { A_GLOBAL = 0, A_COPY = 1, A_NORM = 2, A_EMBED_NORM = 3, A_COPY_ROWS = 6, A_TW8 = 16, A_SPLIT2 = 32 };
 
 // the QKV epilogues (with or without the copy into the paged cache)
 constexpr bool qkv_epi(int e) { return e == EPI_QKV || e == EPI_QKV_CACHE; }
@@ -53,7 +58,7 @@ __device__ __forceinline__ int s_weight_row(const GemmArgs &a, int t, int c) {
     const int h = t / tph, j0 = (t - h * tph) * P;
     return h * a.hd + (c < P ? j0 + c : a.hd / 2 + j0 + (c - P));
   } else {
-    return t * 16 + c;
+    return t * TW + c;
   }
 }
 
@@ -72,7 +77,12 @@ template <int EPI, int TW>
 __device__ __forceinline__ EpiPre s_epi_pre(const GemmArgs &a, int t0) {
   EpiPre p{0.f, 0, 0};
   const int tid = threadIdx.x;
-  if constexpr (EPI == EPI_RESID) {
+  if constexpr (EPI == EPI_RESID && TW == 32) {
+    // split pair: thread tid < 512 owns row (tid / 16) % 16, column
+    // 16 (tid / 256) + tid % 16 of the 32-column tile
+    const int r = min((tid >> 4) & 15, a.M - 1), c = 16 * ((tid >> 8) & 1) + (tid & 15);
+    p.x = a.X[(size_t)r * a.ldx + t0 * 32 + c];
+  } else if constexpr (EPI == EPI_RESID) {
     const int r = min(tid >> 4, a.M - 1), c = tid & 15;
     p.x = a.X[(size_t)r * a.ldx + t0 * 16 + c];
   } else if constexpr (qkv_epi(EPI)) {
@@ -223,7 +233,7 @@ __device__ __forceinline__ void s_epilogue(const GemmArgs &a, const float *ct, i
 template <typename T, int U, bool RES, int TW = 16>
 struct StreamBuf {
   static constexpr bool WL = sizeof(T) == 2;           // whole-line layout (bf16)
-  static_assert(TW == 16 || WL, "8-column tiles: bf16");
+  static_assert(TW == 16 || WL, "8- and 32-column tiles: bf16");
   static constexpr int NR = WL ? TW / 8 : 1;           // loads per chunk step
   static constexpr int S = U / NR;                     // chunk steps per batch
   static constexpr int CE = WL ? 64 : 32;              // k-elements per chunk step
@@ -341,6 +351,22 @@ struct StreamBuf {
     for (int k = 0; k < NA; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     return o;
   }
+
+  // 32-column tile (four row groups): columns 16 SUB .. 16 SUB + 15 from
+  // accumulators 4 SUB .. 4 SUB + 3, combined as fold does for two groups;
+  // the accumulators are left as they are
+  template <int SUB>
+  __device__ __forceinline__ static f32x4 fold_sub(const f32x4 (&acc)[NA]) {
+    static_assert(NR == 4 && SUB < 2, "32-column tiles");
+    const bool lo = (threadIdx.x & 15) < 8;
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s1 = __shfl_xor(acc[4 * SUB + 1][i], 8), s2 = __shfl_xor(acc[4 * SUB + 2][i], 8);
+      o[i] = lo ? acc[4 * SUB][i] + s1 : acc[4 * SUB + 3][i] + s2;
+    }
+    return o;
+  }
 };
 
 // Tile finished: sum the 16 waves' partial tiles in wave order, run the epilogue.
@@ -361,6 +387,62 @@ __device__ __forceinline__ void s_finish_tile(const GemmArgs &a, f32x4 &acc, flo
   }
   lds_barrier();
   s_epilogue<T, EPI, TW>(a, ct, t, layer, best_v, best_i, inv_freq, pre, first);
+}
+
+// Split pair (residual projection, 32-column tile, one half of K per
+// workgroup): the waves' partials of the tile's two 16-column halves are summed
+// in wave order into cts[0..511]; the sum goes to this half's slice of
+// a.spart, and the second workgroup of the pair to arrive (counter a.cnt[cg])
+// adds half 0 + half 1, in that order whichever half arrives second, to the
+// residual and clears the counter for the next launch.  The first to arrive
+// only leaves its partial: no workgroup waits for another.  Every value that
+// crosses workgroups (partials, counter) moves through device-scope atomic
+// accesses, each coherent across the XCDs by itself; every wave waits until
+// its partial stores have completed before the barrier that precedes the
+// counter increment, and the second workgroup issues its loads after its
+// increment has returned.  Device-scope release/acquire fences instead write
+// back and invalidate the XCD's whole L2: the projection took 29.7 us with
+// one such pair per workgroup and 73.5 us with one per wave, against 25.4 us
+// (Qwen3-8B shape, K 12288, measured).
+// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt at their maxima, so
+// only vector-memory operations are waited for)
+constexpr int kWaitVmem = 0x0F70;
+
+template <typename T>
+__device__ __forceinline__ void s_finish_split(const GemmArgs &a, const f32x4 (&acc2)[2], float (*red)[256],
+                                               float *cts, int cg, int half, float xpre, int *s_old) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, ln = lane & 15;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][(4 * g + i) * 16 + ln] = f4get(acc2[sub], i);
+    lds_barrier();
+    if (tid < 256) {
+      float sm = 0.f;
+#pragma unroll
+      for (int w = 0; w < kSWaves; ++w) sm += red[w][tid];
+      cts[256 * sub + tid] = sm;
+    }
+    lds_barrier();
+  }
+  const int r = (tid >> 4) & 15, col = cg * 32 + 16 * ((tid >> 8) & 1) + (tid & 15);
+  const bool mine = tid < 512 && r < a.M;
+  const float v = tid < 512 ? cts[tid] : 0.f;
+  if (mine) __hip_atomic_store(a.spart + ((size_t)half * 16 + r) * a.N + col, v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(kWaitVmem);   // this wave's partial stores have completed
+  __syncthreads();
+  if (tid == 0) *s_old = (int)__hip_atomic_fetch_add(a.cnt + cg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (*s_old == 1) {   // second to arrive (uniform)
+    if (mine) {
+      const float o = __hip_atomic_load(a.spart + ((size_t)(1 - half) * 16 + r) * a.N + col, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+      const float p0 = half == 0 ? v : o, p1 = half == 0 ? o : v;
+      a.X[(size_t)r * a.ldx + col] = xpre + (p0 + p1);
+    }
+    if (tid == 0) __hip_atomic_store(a.cnt + cg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // A_COPY_ROWS (residual projection and LM head argmax): grid.y is a 16-row
@@ -384,6 +466,10 @@ template <typename T, int EPI, int AM, int TW = 16, bool FLAT = false>
 __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a0) {
   static_assert(AM != A_COPY_ROWS || EPI == EPI_RESID || EPI == EPI_ARGMAX,
                 "row groups serve the residual projection and the LM head");
+  // TW = 32: the split pair of the residual projection (one workgroup per
+  // pair half, grid = 2 x the 32-column tiles, a multiple of 16)
+  constexpr bool SPLIT = TW == 32;
+  static_assert(!SPLIT || (EPI == EPI_RESID && AM == A_GLOBAL && !FLAT), "split pairs: residual projection");
   // grid.y is the weight slice (layer), or the 16-row group of A_COPY_ROWS
   constexpr bool ROWS = AM == A_COPY_ROWS;
   const int layer = ROWS ? 0 : blockIdx.y;
@@ -396,7 +482,8 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   using Buf = StreamBuf<T, U, RES, TW>;
   __shared__ __align__(16) unsigned char a_lds[RES ? 16 * ASTR : 16];
   __shared__ float red[kSWaves][256];
-  __shared__ float ct[256];
+  __shared__ float ct[SPLIT ? 512 : 256];
+  __shared__ int s_old;
   __shared__ double inv_freq[64];   // RoPE inverse frequencies (head_dim <= 128)
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, ln = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -420,12 +507,21 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   };
   // FLAT: tile t is tile t % n_groups of slice t / n_groups, so a workgroup
   // stages its rows once for tiles of several slices
+  // SPLIT: workgroup u takes half (u / 8) % 2 of K for 32-column tile
+  // (u % 8) + 8 (u / 16), so the two halves of a tile run on one XCD
+  // (workgroups u and u + 8) and share its L2
+  const int KH = SPLIT ? a.K / 2 : a.K;                        // K of one workgroup's range
+  const int half = SPLIT ? ((int)blockIdx.x >> 3) & 1 : 0;
   const T *W0 = (const T *)a0.W[layer];
   auto slice_of = [&](int t) { return FLAT ? t / a.n_groups : layer; };
-  auto tile_in = [&](int t) { return FLAT ? t - (t / a.n_groups) * a.n_groups : t; };
-  auto w_of = [&](int t) { return FLAT ? (const T *)a0.W[slice_of(t)] : W0; };
+  auto tile_in = [&](int t) {
+    return FLAT ? t - (t / a.n_groups) * a.n_groups : SPLIT ? (t & 7) | ((t >> 4) << 3) : t;
+  };
+  auto w_of = [&](int t) {
+    return FLAT ? (const T *)a0.W[slice_of(t)] : SPLIT ? W0 + (size_t)((t >> 3) & 1) * KH : W0;
+  };
   const int ntiles = FLAT ? a.n_groups * a.z_flat : a.n_groups;
-  const int CPT = a.K / Buf::CE;                               // chunk steps per tile
+  const int CPT = KH / Buf::CE;                                // chunk steps per tile
   const int CPW = (CPT + kSWaves - 1) / kSWaves;               // chunks per wave
   const int cbeg = min(CPT, wave * CPW), cend = min(CPT, cbeg + CPW);
   const int clast = CPT - 1;                                   // always a valid chunk
@@ -455,8 +551,8 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
     arow = reinterpret_cast<const T *>(a_lds + ln * ASTR) + 8 * g;
   } else if constexpr (Buf::WL) {
     const int r0 = ln & 7, r1 = 8 + (ln & 7);
-    arow = A + (size_t)(r0 < a.M ? r0 : 0) * a.lda + 8 * g + 32 * (ln >> 3);
-    arow_hi = A + (size_t)(r1 < a.M ? r1 : 0) * a.lda + 8 * g + 32 * (ln >> 3);
+    arow = A + (size_t)(r0 < a.M ? r0 : 0) * a.lda + (size_t)half * KH + 8 * g + 32 * (ln >> 3);
+    arow_hi = A + (size_t)(r1 < a.M ? r1 : 0) * a.lda + (size_t)half * KH + 8 * g + 32 * (ln >> 3);
   } else {
     arow = A + (size_t)(ln < a.M ? ln : 0) * a.lda + 8 * g;
   }
@@ -571,6 +667,16 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
 #pragma unroll
   for (int k = 0; k < Buf::NA; ++k) accs[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 acc;
+  auto finish = [&](int qq, bool first) {
+    const int tf = tile_of(qq);
+    if constexpr (SPLIT) {
+      const f32x4 a2[2] = {Buf::template fold_sub<0>(accs), Buf::template fold_sub<1>(accs)};
+      s_finish_split<T>(a, a2, red, ct, tile_in(tf), half, pre.x, &s_old);
+    } else {
+      acc = Buf::fold(accs);
+      s_finish_tile<T, EPI, TW>(a, acc, red, ct, tile_in(tf), slice_of(tf), &best_v, &best_i, inv_freq, pre, first);
+    }
+  };
   // static ping-pong between two register buffers (dynamic selection would
   // spill the fragments to scratch): the next batch is issued before the
   // current one is consumed.  Every batch is issued whether or not it exists
@@ -583,18 +689,10 @@ __global__ __launch_bounds__(kSThreads) void gemm_stream_kernel(const GemmArgs a
   for (int q = 0; q < total; q += 2) {
     DF_ISSUE(bufb, q + 1);
     bufa.compute(accs, arow, cbeg + (q % nb) * Buf::S, cend, clast);
-    if (q % nb == nb - 1) {
-      acc = Buf::fold(accs);
-      s_finish_tile<T, EPI, TW>(a, acc, red, ct, tile_in(tile_of(q)), slice_of(tile_of(q)), &best_v, &best_i, inv_freq,
-                                pre, q < nb);
-    }
+    if (q % nb == nb - 1) finish(q, q < nb);
     DF_ISSUE(bufa, q + 2);
     bufb.compute(accs, arow, cbeg + ((q + 1) % nb) * Buf::S, cend, clast);
-    if ((q + 1) % nb == nb - 1 && q + 1 < total) {
-      acc = Buf::fold(accs);
-      s_finish_tile<T, EPI, TW>(a, acc, red, ct, tile_in(tile_of(q + 1)), slice_of(tile_of(q + 1)), &best_v, &best_i,
-                                inv_freq, pre, q + 1 < nb);
-    }
+    if ((q + 1) % nb == nb - 1 && q + 1 < total) finish(q + 1, q + 1 < nb);
   }
 #undef DF_ISSUE
 
@@ -722,6 +820,14 @@ static hipError_t launch_s(int am, const GemmArgs &a, dim3 grid, hipStream_t st)
           break;
         default: return hipErrorInvalidValue;
       }
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
+  if (am == A_SPLIT2) {   // split pairs: bf16 residual projection, activations from global memory
+    if constexpr (sizeof(T) == 2 && EPI == EPI_RESID) {
+      hipLaunchKernelGGL((gemm_stream_kernel<T, EPI_RESID, A_GLOBAL, 32>), grid, block, 0, st, a);
       return hipGetLastError();
     } else {
       return hipErrorInvalidValue;

@@ -363,6 +363,20 @@ def test_draft_block_qkv_tile_widths(nq, nkv):
     run_draft_case(cfg, seed=8)
 
 
+@pytest.mark.parametrize("ffn,B", [(4608, 16), (8320, 10)])
+def test_draft_block_split_down_projection(ffn, B):
+    """Batch 1 with an FFN past the 4096 resident columns: the down projection
+    runs as 32-column tiles in pairs of workgroups, each pair half over half
+    of K (2304 of 4608: 36 k-steps, the last four waves idle; 4160 of 8320:
+    65 k-steps), the second half to finish adding both partials to the
+    residual; B = 10 leaves rows 10-15 of each tile unused.  Hidden states and
+    draft ids against the oracle, and two calls bit-identical (the arrival
+    counters are back at zero after each call)."""
+    cfg = dataclasses.replace(MINI["mini_bf16"], name=f"mini_ffn{ffn}", batch=1, ffn=ffn, block_size=B)
+    log(f"draft_block batch 1, FFN {ffn}, B {B} (split down projection)")
+    run_draft_case(cfg, seed=9)
+
+
 @pytest.mark.parametrize("name,window", [("mini_bf16", 100), ("mini_d64", 50), ("mini_f32", 40)])
 def test_draft_block_sliding_window(name, window):
     """Sliding-window context (ragged contexts above and below the window;
