@@ -75,6 +75,11 @@ MINI = {
     "mini_long": mini("mini_long", 111, dtype="bf16", hidden=256, n_q_heads=8, n_kv_heads=2, head_dim=128,
                       ffn=512, vocab=1040, n_layers=1, n_feat_layers=2, block_size=16, batch=8,
                       ctx_min=2000, ctx_max=16384, rope_theta=1e6),
+    # one sequence with an FFN past the 4096 resident columns: the down projection
+    # on split pairs (two workgroups per 32-column tile, half of K each)
+    "mini_ffn_b1": mini("mini_ffn_b1", 112, dtype="bf16", hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                        ffn=4608, vocab=2064, n_layers=2, n_feat_layers=2, block_size=16, batch=1,
+                        ctx_min=150, ctx_max=150, rope_theta=1e6),
     "tiny": S.get_config("tiny"),
 }
 

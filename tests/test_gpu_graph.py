@@ -67,7 +67,7 @@ def capture_and_replay(step, outputs, replays=4, n_fill=None):
     return want
 
 
-@pytest.mark.parametrize("name", ["mini_bf16", "mini_b8", "tiny"])
+@pytest.mark.parametrize("name", ["mini_bf16", "mini_b8", "tiny", "mini_ffn_b1"])
 def test_greedy_step_graph_replays_match_eager(name):
     R, cfg, dr, kv, anchors, y, b, B = setup(name)
     log(f"graph greedy step {name}")

@@ -199,10 +199,11 @@ def test_inject_context(name, n_new):
 
 
 @pytest.mark.parametrize("name,n_new", [("mini_bf16", 5), ("mini_bf16", 300), ("mini_f32", 16), ("mini_f32", 90),
-                                        ("mini_port", 40)])
+                                        ("mini_port", 40), ("mini_port", 3), ("mini_port", 16)])
 def test_inject_context_with_ctx_norm(name, n_new):
     """The optional RMSNorm after the fusion projection (random gain), on the
-    streaming (<= 16 rows), few-rows and LDS-tiled paths."""
+    streaming (<= 16 rows, K-portions for mini_port's K = 17 x 256), few-rows and
+    LDS-tiled paths."""
     run_inject_case(dataclasses.replace(MINI[name], ctx_norm=1), n_new, random_gain=True)
 
 
